@@ -1,0 +1,203 @@
+"""Plain CPU oracle of the speculative-decoding verify sampler (ctypes binding).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()`` and the
+benchmark's CPU-baseline leg may import this package.  The product path (the GPU
+library and its Python binding) never imports, links or calls it, and the two share
+no code.
+
+The C++ source (``specverify_oracle.cpp``) computes everything in double precision;
+this module only builds it with g++, loads it, and marshals numpy arrays.
+Logit arrays are numpy ``uint16`` (raw bf16 bit patterns) or ``float32``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "specverify_oracle.cpp")
+LIB = os.path.join(HERE, "liboracle.so")
+MUTANT_DIR = os.path.join(HERE, "_mutants")
+
+DTYPE_BF16 = 0
+DTYPE_F32 = 1
+
+_CFLAGS = ["-O2", "-std=c++17", "-shared", "-fPIC", "-pthread", "-ffp-contract=off", "-fno-fast-math"]
+
+
+def lib_path(mutant: int | None = None) -> str:
+    if mutant is None:
+        return LIB
+    return os.path.join(MUTANT_DIR, f"liboracle_m{mutant}.so")
+
+
+def build(mutant: int | None = None, force: bool = True) -> str:
+    """Compile the oracle (or a negative-control mutant) with g++; returns the .so path."""
+    out = lib_path(mutant)
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(SRC):
+        return out
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    cmd = ["g++", *_CFLAGS, "-o", out + ".tmp", SRC]
+    if mutant is not None:
+        cmd.insert(1, f"-DORACLE_MUTANT={int(mutant)}")
+    subprocess.run(cmd, check=True, cwd=HERE)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_U32 = ctypes.c_uint32
+_U64 = ctypes.c_uint64
+_D = ctypes.c_double
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(_P)
+
+
+@dataclass
+class VerifyResult:
+    tokens: np.ndarray       # int32 [B, k+1]
+    accept_len: np.ndarray   # int32 [B]
+    logprobs: np.ndarray     # float64 [B, k+1]
+    alpha: np.ndarray        # float64 [B, k]
+    accept_margin: np.ndarray  # float64 [B]
+    gumbel_gap: np.ndarray     # float64 [B]
+    topp_margin: np.ndarray    # float64 [B]
+    residual_mass: np.ndarray  # float64 [B]
+    fallback: np.ndarray       # bool [B]
+    sentinel: np.ndarray       # bool [B]
+    n_accepted: np.ndarray     # int32 [B]
+
+    def margin_rows(self, tol_accept: float = 1e-5, tol_gap: float = 1e-5, tol_topp: float = 1e-5) -> np.ndarray:
+        """Rows whose outcome a different (correct) rounding could change: boolean [B]."""
+        return ((self.accept_margin <= tol_accept) | (self.gumbel_gap <= tol_gap)
+                | (self.topp_margin <= tol_topp) | self.fallback)
+
+
+class Oracle:
+    """Loaded oracle library (optionally a negative-control mutant)."""
+
+    def __init__(self, mutant: int | None = None, rebuild: bool = False):
+        path = lib_path(mutant)
+        if rebuild or not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(SRC):
+            build(mutant)
+        self.mutant = mutant
+        self.lib = ctypes.CDLL(path)
+        L = self.lib
+        L.oracle_philox4x32_10.argtypes = [_P, _P, _P]
+        L.oracle_philox4x32_10.restype = None
+        L.oracle_accept_uniform.argtypes = [_U64, _U32, _U32, _U32]
+        L.oracle_accept_uniform.restype = _D
+        L.oracle_gumbel_uniform.argtypes = [_U64, _U32, _U32, _U32, _U32, _U32]
+        L.oracle_gumbel_uniform.restype = _D
+        L.oracle_row_probs.argtypes = [_P, _I32, _D, _I32, _D, _P, _P]
+        L.oracle_row_probs.restype = ctypes.c_int
+        L.oracle_spec_verify.argtypes = [_P, _P, _I32, _P, _P, _P, _P, _I32, _I32, _I32, _U64, _U64,
+                                         _P, _P, _P, _P, _P, _P, _I32]
+        L.oracle_spec_verify.restype = ctypes.c_int
+        L.oracle_sample.argtypes = [_P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _U64, _U64, _P, _P, _P, _I32]
+        L.oracle_sample.restype = ctypes.c_int
+
+    # -- random streams ---------------------------------------------------------------
+    def philox(self, ctr, key) -> np.ndarray:
+        c = np.ascontiguousarray(np.asarray(ctr, dtype=np.uint32).reshape(4))
+        k = np.ascontiguousarray(np.asarray(key, dtype=np.uint32).reshape(2))
+        out = np.zeros(4, dtype=np.uint32)
+        self.lib.oracle_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+        return out
+
+    def accept_uniform(self, seed: int, b: int, i: int, offset: int) -> float:
+        return self.lib.oracle_accept_uniform(seed, b, i, offset)
+
+    def gumbel_uniform(self, seed: int, tag: int, b: int, j: int, x: int, offset: int) -> float:
+        return self.lib.oracle_gumbel_uniform(seed, tag, b, j, x, offset)
+
+    # -- one row's sampler distribution ---------------------------------------------
+    def row_probs(self, logits, T: float, K: int = 0, P: float = 1.0):
+        l = np.ascontiguousarray(np.asarray(logits, dtype=np.float64))
+        V = l.shape[0]
+        probs = np.zeros(V, dtype=np.float64)
+        info = np.zeros(6, dtype=np.float64)
+        rc = self.lib.oracle_row_probs(_ptr(l), V, float(T), int(K), float(P), _ptr(probs), _ptr(info))
+        if rc != 0:
+            raise ValueError("row has no distribution (all -inf)")
+        return probs, dict(m=info[0], argmax=int(info[1]), Z=info[2], kept=int(info[3]), thr=info[4],
+                           topp_margin=info[5])
+
+    # -- the verify step ------------------------------------------------------------------
+    def spec_verify(self, target, draft, draft_tokens, temperature, top_k, top_p, seed: int = 0,
+                    offset: int = 0, num_threads: int = 0) -> VerifyResult:
+        target = np.ascontiguousarray(target)
+        draft = np.ascontiguousarray(draft)
+        if target.dtype == np.uint16:
+            dtype = DTYPE_BF16
+        elif target.dtype == np.float32:
+            dtype = DTYPE_F32
+        else:
+            raise TypeError("logits must be uint16 (bf16 bits) or float32")
+        if draft.dtype != target.dtype:
+            raise TypeError("target and draft logits must share a dtype")
+        B, k1, V = target.shape
+        k = k1 - 1
+        if draft.shape != (B, k, V):
+            raise ValueError("draft logits must be [B, k, V]")
+        dt = np.ascontiguousarray(np.asarray(draft_tokens, dtype=np.int32).reshape(B, k))
+        T = np.ascontiguousarray(np.asarray(temperature, dtype=np.float32).reshape(B))
+        K = np.ascontiguousarray(np.asarray(top_k, dtype=np.int32).reshape(B))
+        P = np.ascontiguousarray(np.asarray(top_p, dtype=np.float32).reshape(B))
+        tokens = np.zeros((B, k + 1), dtype=np.int32)
+        acc = np.zeros(B, dtype=np.int32)
+        lp = np.zeros((B, k + 1), dtype=np.float64)
+        al = np.zeros((B, k), dtype=np.float64)
+        diag = np.zeros((B, 4), dtype=np.float64)
+        fl = np.zeros(B, dtype=np.int32)
+        rc = self.lib.oracle_spec_verify(_ptr(target), _ptr(draft), dtype, _ptr(dt), _ptr(T), _ptr(K), _ptr(P),
+                                         B, k, V, int(seed), int(offset), _ptr(tokens), _ptr(acc), _ptr(lp),
+                                         _ptr(al), _ptr(diag), _ptr(fl), int(num_threads))
+        if rc != 0:
+            raise ValueError("oracle_spec_verify rejected its scalar arguments")
+        return VerifyResult(tokens, acc, lp, al, diag[:, 0].copy(), diag[:, 1].copy(), diag[:, 2].copy(),
+                            diag[:, 3].copy(), (fl & 1) != 0, (fl & 2) != 0, (fl >> 8).astype(np.int32))
+
+    # -- plain sampler ---------------------------------------------------------------------
+    def sample(self, logits, temperature, top_k, top_p, row_b, row_pos, seed: int = 0, offset: int = 0,
+               num_threads: int = 0):
+        """Sample one token per row of ``logits`` [R, V]; returns (tokens, logprobs, gap)."""
+        logits = np.ascontiguousarray(logits)
+        if logits.dtype == np.uint16:
+            dtype = DTYPE_BF16
+        elif logits.dtype == np.float32:
+            dtype = DTYPE_F32
+        else:
+            raise TypeError("logits must be uint16 (bf16 bits) or float32")
+        R, V = logits.shape
+        T = np.ascontiguousarray(np.asarray(temperature, dtype=np.float32).reshape(R))
+        K = np.ascontiguousarray(np.asarray(top_k, dtype=np.int32).reshape(R))
+        P = np.ascontiguousarray(np.asarray(top_p, dtype=np.float32).reshape(R))
+        rb = np.ascontiguousarray(np.asarray(row_b, dtype=np.int32).reshape(R))
+        rp = np.ascontiguousarray(np.asarray(row_pos, dtype=np.int32).reshape(R))
+        tok = np.zeros(R, dtype=np.int32)
+        lp = np.zeros(R, dtype=np.float64)
+        gap = np.zeros(R, dtype=np.float64)
+        rc = self.lib.oracle_sample(_ptr(logits), dtype, _ptr(T), _ptr(K), _ptr(P), _ptr(rb), _ptr(rp), R, V,
+                                    int(seed), int(offset), _ptr(tok), _ptr(lp), _ptr(gap), int(num_threads))
+        if rc != 0:
+            raise ValueError("oracle_sample rejected its scalar arguments")
+        return tok, lp, gap
+
+
+_default: Oracle | None = None
+
+
+def get() -> Oracle:
+    """The (lazily built and loaded) reference oracle."""
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default

@@ -1,0 +1,542 @@
+// specverify_oracle.cpp -- plain CPU oracle of the speculative-decoding verify sampler.
+//
+// TEST INFRASTRUCTURE ONLY: loaded by the test suite, the smoke check and the benchmark's
+// CPU-baseline leg, never by the product path.  Shares no code with the GPU library.
+//
+// Plain double-precision loops, std::sort as the only library primitive.  No blocking,
+// fusion or reordering beyond what the definitions below state, so every step can be
+// checked by eye against its source:
+//   * AReno PR "feat(engine): MTP training loss and speculative decoding for bailing_v3",
+//     section "What does this PR do?", Phase 2 paragraph: the verify step builds the
+//     sampler-equivalent target distribution and runs exact chain rejection sampling so
+//     that both the sampled distribution and the reported logprobs are those of plain
+//     sampling.
+//   * same page, accept-probability table: alpha = sum_x min(p, q); expected accept length.
+//   * same page, per-step optimisation table: draws are Gumbel-max, without host syncs.
+//   * same page, section "How was it tested?": sampler equivalence with and without
+//     top-k/top-p; distribution preservation; exact under greedy.
+// Where the page is silent, the reading taken is named in the comment (R-numbers refer to
+// the list of readings in the design notes).
+//
+// Negative controls: building with -DORACLE_MUTANT=<n> plants one deliberate mistake
+// (see the MUTANT switch comments); the test suite checks that its pins catch each one.
+
+#include "specverify_oracle.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <limits>
+#include <thread>
+#include <utility>
+#include <vector>
+
+#ifndef ORACLE_MUTANT
+#define ORACLE_MUTANT 0
+#endif
+
+namespace {
+
+const double kInf = std::numeric_limits<double>::infinity();
+const double kNaN = std::numeric_limits<double>::quiet_NaN();
+
+// ---------------------------------------------------------------------------------------
+// Philox-4x32-10 (Salmon et al., SC'11, section 5): two 32x32->64 multiplies per round,
+// the high halves xored with the other counter words and the round key, the key bumped
+// by the Weyl constants between rounds.
+// ---------------------------------------------------------------------------------------
+void philox_round(uint32_t c[4], const uint32_t key[2]) {
+  const uint64_t p0 = (uint64_t)0xD2511F53u * (uint64_t)c[0];
+  const uint64_t p1 = (uint64_t)0xCD9E8D57u * (uint64_t)c[2];
+  const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+  const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+  const uint32_t n0 = hi1 ^ c[1] ^ key[0];
+  const uint32_t n1 = lo1;
+  const uint32_t n2 = hi0 ^ c[3] ^ key[1];
+  const uint32_t n3 = lo0;
+  c[0] = n0; c[1] = n1; c[2] = n2; c[3] = n3;
+}
+
+void philox10(const uint32_t ctr[4], const uint32_t key_in[2], uint32_t out[4]) {
+#if ORACLE_MUTANT == 11
+  const int rounds = 9;  // MUTANT 11: one round short
+#else
+  const int rounds = 10;
+#endif
+  uint32_t c[4] = {ctr[0], ctr[1], ctr[2], ctr[3]};
+  uint32_t key[2] = {key_in[0], key_in[1]};
+  for (int r = 0; r < rounds; ++r) {
+    if (r > 0) {
+      key[0] += 0x9E3779B9u;
+      key[1] += 0xBB67AE85u;
+    }
+    philox_round(c, key);
+  }
+  for (int j = 0; j < 4; ++j) out[j] = c[j];
+}
+
+uint32_t philox_word(uint64_t seed, uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t word) {
+  const uint32_t ctr[4] = {c0, c1, c2, c3};
+  const uint32_t key[2] = {(uint32_t)(seed & 0xffffffffu), (uint32_t)(seed >> 32)};
+  uint32_t out[4];
+  philox10(ctr, key, out);
+  return out[word & 3u];
+}
+
+// Accept uniform u(b, i) in [0, 1): the top 24 bits of the word, exact in float and double (R6).
+double accept_uniform(uint64_t seed, uint32_t b, uint32_t i, uint32_t offset) {
+  const uint32_t w = philox_word(seed, i >> 2, b, 0u, offset, i & 3u);
+  return (double)(w >> 8) * 0x1p-24;
+}
+
+// Gumbel uniform U in (0, 1): the top 23 bits plus one half, exact in float and double (R13).
+double gumbel_uniform(uint64_t seed, uint32_t tag, uint32_t b, uint32_t j, uint32_t x, uint32_t offset) {
+  const uint32_t w = philox_word(seed, x >> 2, b, (tag << 24) | j, offset, x & 3u);
+  return ((double)(w >> 9) + 0.5) * 0x1p-23;
+}
+
+double gumbel(uint64_t seed, uint32_t tag, uint32_t b, uint32_t j, uint32_t x, uint32_t offset) {
+  const double U = gumbel_uniform(seed, tag, b, j, x, offset);
+  return -std::log(-std::log(U));
+}
+
+// ---------------------------------------------------------------------------------------
+// Input conversion: both maps are exact.
+// ---------------------------------------------------------------------------------------
+double bf16_to_double(uint16_t h) {
+  const uint32_t u = (uint32_t)h << 16;
+  float f;
+  std::memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+void load_row(const void* base, int32_t dtype, size_t row, int32_t V, std::vector<double>& out) {
+  out.resize((size_t)V);
+  if (dtype == ORACLE_DTYPE_BF16) {
+    const uint16_t* p = (const uint16_t*)base + row * (size_t)V;
+    for (int32_t x = 0; x < V; ++x) out[(size_t)x] = bf16_to_double(p[x]);
+  } else {
+    const float* p = (const float*)base + row * (size_t)V;
+    for (int32_t x = 0; x < V; ++x) out[(size_t)x] = (double)p[x];
+  }
+}
+
+// A row is unusable if it holds NaN or +inf (R15).  -inf is a legal logit (probability 0).
+bool row_has_nan_or_posinf(const std::vector<double>& l) {
+  for (double v : l)
+    if (std::isnan(v) || v == kInf) return true;
+  return false;
+}
+
+// Sampling parameters are valid when T is finite and >= 0, top_k >= 0, and top_p > 0
+// (top_p >= 1, including +inf, switches top-p off) (R3, R4).
+bool params_valid(float T, int32_t K, float P) {
+  if (std::isnan(T) || std::isinf(T) || T < 0.0f) return false;
+  if (K < 0) return false;
+  if (std::isnan(P) || P <= 0.0f) return false;
+  return true;
+}
+
+// ---------------------------------------------------------------------------------------
+// The sampler distribution of one row: temperature, then top-k, then top-p on the top-k
+// renormalised mass, then renormalise (R1).  Ties at either threshold are kept whole (R2,
+// R3).  T == 0 is greedy: a one-hot at the lowest-index maximum (R4).
+// ---------------------------------------------------------------------------------------
+struct RowDist {
+  std::vector<double> p;  // the distribution
+  double m = -kInf;       // row max
+  int32_t argmax = -1;    // lowest-index maximum
+  double Z = 0.0;         // kept-set normaliser of exp((l - m) / T)
+  int32_t kept = 0;       // number of kept entries
+  double thr = -kInf;     // smallest kept logit
+  double topp_margin = kInf;
+};
+
+bool row_dist(const std::vector<double>& l, double T, int32_t K, double P, RowDist& d) {
+  const int32_t V = (int32_t)l.size();
+  d.p.assign((size_t)V, 0.0);
+  d.m = -kInf;
+  d.argmax = -1;
+  for (int32_t x = 0; x < V; ++x) {
+#if ORACLE_MUTANT == 4
+    if (l[(size_t)x] >= d.m && l[(size_t)x] > -kInf) {  // MUTANT 4: highest index wins ties
+#else
+    if (l[(size_t)x] > d.m) {  // strict: the first (lowest-index) maximum is kept
+#endif
+      d.m = l[(size_t)x];
+      d.argmax = x;
+    }
+  }
+  if (d.argmax < 0) return false;  // every entry is -inf: no distribution
+
+  if (T == 0.0) {  // greedy
+    d.p[(size_t)d.argmax] = 1.0;
+    d.Z = 1.0;
+    d.kept = 1;
+    d.thr = d.m;
+    return true;
+  }
+
+  std::vector<double> e((size_t)V);
+  for (int32_t x = 0; x < V; ++x) {
+#if ORACLE_MUTANT == 9
+    e[(size_t)x] = std::exp((l[(size_t)x] - d.m) * T);  // MUTANT 9: temperature multiplies
+#else
+    e[(size_t)x] = std::exp((l[(size_t)x] - d.m) / T);
+#endif
+  }
+
+  double thr = -kInf;
+  if (K > 0 && K < V) {
+    // K-th largest value, counting multiplicity.
+    std::vector<double> s(l);
+    std::sort(s.begin(), s.end(), [](double a, double b) { return a > b; });
+#if ORACLE_MUTANT == 10
+    thr = s[(size_t)K];  // MUTANT 10: keeps one more than K
+#else
+    thr = s[(size_t)K - 1];
+#endif
+  }
+
+  if (P < 1.0) {
+    // Kept set so far, sorted by value (descending); M(v) = mass of kept entries >= v.
+    std::vector<std::pair<double, double>> kv;  // (logit, e)
+    double ZK = 0.0;
+    for (int32_t x = 0; x < V; ++x) {
+      if (l[(size_t)x] >= thr) {
+        kv.emplace_back(l[(size_t)x], e[(size_t)x]);
+        ZK += e[(size_t)x];
+      }
+    }
+    std::sort(kv.begin(), kv.end(), [](const std::pair<double, double>& a, const std::pair<double, double>& b) {
+      return a.first > b.first;
+    });
+    const double target = P * ZK;
+    double M = 0.0, prevM = -1.0;
+    double chosen = -kInf;
+    size_t i = 0;
+    while (i < kv.size()) {
+      const double v = kv[i].first;
+      while (i < kv.size() && kv[i].first == v) {
+        M += kv[i].second;
+        ++i;
+      }
+#if ORACLE_MUTANT == 3
+      if (M > target) {  // MUTANT 3: strict inequality
+#else
+      if (M >= target) {  // smallest upper set holding at least P of the mass (R3)
+#endif
+        chosen = v;
+        break;
+      }
+      prevM = M;
+    }
+    if (chosen == -kInf && !kv.empty()) chosen = kv.back().first;  // unreachable for P < 1
+    double margin = std::fabs(M / ZK - P);
+    if (prevM >= 0.0) margin = std::min(margin, std::fabs(prevM / ZK - P));
+    d.topp_margin = margin;
+    thr = std::max(thr, chosen);
+  }
+
+  double Z = 0.0;
+  int32_t kept = 0;
+  for (int32_t x = 0; x < V; ++x) {
+#if ORACLE_MUTANT == 5
+    Z += e[(size_t)x];  // MUTANT 5: no renormalisation after truncation
+    if (l[(size_t)x] >= thr) ++kept;
+#else
+    if (l[(size_t)x] >= thr) {
+      Z += e[(size_t)x];
+      ++kept;
+    }
+#endif
+  }
+  for (int32_t x = 0; x < V; ++x)
+    if (l[(size_t)x] >= thr) d.p[(size_t)x] = e[(size_t)x] / Z;
+  d.Z = Z;
+  d.kept = kept;
+  d.thr = thr;
+  return true;
+}
+
+// Gumbel-max over a weight vector w (entries <= 0 are excluded): argmax of ln w(x) + G(x),
+// lowest index on exact key ties (R13).  Returns the index and the top-2 key gap.
+int32_t gumbel_argmax(const std::vector<double>& w, uint64_t seed, uint32_t tag, uint32_t b, uint32_t j,
+                      uint32_t offset, double* gap) {
+  double best = -kInf, second = -kInf;
+  int32_t y = -1;
+  for (size_t x = 0; x < w.size(); ++x) {
+    if (!(w[x] > 0.0)) continue;
+#if ORACLE_MUTANT == 8
+    const double key = std::log(w[x]) - gumbel(seed, tag, b, j, (uint32_t)x, offset);  // MUTANT 8
+#else
+    const double key = std::log(w[x]) + gumbel(seed, tag, b, j, (uint32_t)x, offset);
+#endif
+    if (key > best) {
+      second = best;
+      best = key;
+      y = (int32_t)x;
+    } else if (key > second) {
+      second = key;
+    }
+  }
+  *gap = (second == -kInf) ? kInf : best - second;
+  return y;
+}
+
+// ---------------------------------------------------------------------------------------
+// One batch row of the verify step.
+// ---------------------------------------------------------------------------------------
+struct VerifyArgs {
+  const void* target;
+  const void* draft;
+  int32_t dtype;
+  const int32_t* draft_tokens;
+  const float* temperature;
+  const int32_t* top_k;
+  const float* top_p;
+  int32_t B, k, V;
+  uint64_t seed;
+  uint32_t offset;
+  int32_t* tokens;
+  int32_t* accept_len;
+  double* logprobs;
+  double* alpha;
+  double* diag;
+  int32_t* dflags;
+};
+
+void write_sentinel(const VerifyArgs& a, int32_t b) {
+  const int32_t k = a.k;
+  for (int32_t i = 0; i <= k; ++i) {
+    a.tokens[(size_t)b * (k + 1) + i] = -1;
+    a.logprobs[(size_t)b * (k + 1) + i] = kNaN;
+  }
+  for (int32_t i = 0; i < k; ++i) a.alpha[(size_t)b * k + i] = kNaN;
+  a.accept_len[b] = 0;
+  if (a.diag)
+    for (int j = 0; j < 4; ++j) a.diag[(size_t)b * 4 + j] = kInf;
+  if (a.dflags) a.dflags[b] = 2;
+}
+
+void verify_row(const VerifyArgs& a, int32_t b) {
+  const int32_t k = a.k, V = a.V;
+  const float Tf = a.temperature[b];
+  const int32_t K = a.top_k[b];
+  const float Pf = a.top_p[b];
+  if (!params_valid(Tf, K, Pf)) return write_sentinel(a, b);
+  for (int32_t i = 0; i < k; ++i) {
+    const int32_t x = a.draft_tokens[(size_t)b * k + i];
+    if (x < 0 || x >= V) return write_sentinel(a, b);
+  }
+  const double T = (double)Tf, P = (double)Pf;
+
+  // p_i for target positions i = 0..k, q_i for draft positions i = 0..k-1, each with the
+  // batch row's own (T, top-k, top-p): the draft side is processed exactly like the target.
+  std::vector<RowDist> p((size_t)k + 1), q((size_t)k);
+  std::vector<double> l;
+  double topp_margin = kInf;
+  for (int32_t i = 0; i <= k; ++i) {
+    load_row(a.target, a.dtype, (size_t)b * (k + 1) + i, V, l);
+    if (row_has_nan_or_posinf(l) || !row_dist(l, T, K, P, p[(size_t)i])) return write_sentinel(a, b);
+    topp_margin = std::min(topp_margin, p[(size_t)i].topp_margin);
+  }
+  for (int32_t i = 0; i < k; ++i) {
+    load_row(a.draft, a.dtype, (size_t)b * k + i, V, l);
+    if (row_has_nan_or_posinf(l) || !row_dist(l, T, K, P, q[(size_t)i])) return write_sentinel(a, b);
+    topp_margin = std::min(topp_margin, q[(size_t)i].topp_margin);
+  }
+
+  // Chain rejection: accept draft x_i while the target allows it and u_i < p_i(x_i) / q_i(x_i);
+  // a draft outside q's support is accepted whenever p_i(x_i) > 0 (R5).  Greedy rows reduce to
+  // "accept iff x_i is the target argmax" because p and q are one-hot.
+  int32_t n = k;
+  double accept_margin = kInf;
+  for (int32_t i = 0; i < k; ++i) {
+    const int32_t x = a.draft_tokens[(size_t)b * k + i];
+    const double pt = p[(size_t)i].p[(size_t)x];
+    const double qd = q[(size_t)i].p[(size_t)x];
+    const double u = accept_uniform(a.seed, (uint32_t)b, (uint32_t)i, a.offset);
+#if ORACLE_MUTANT == 1
+    const bool accept = qd > 0.0 && (pt == 0.0 || u < qd / pt);  // MUTANT 1: p and q swapped
+#else
+    const bool accept = pt > 0.0 && (qd == 0.0 || u < pt / qd);
+#endif
+    if (T != 0.0 && pt > 0.0 && qd > 0.0) accept_margin = std::min(accept_margin, std::fabs(u - pt / qd));
+    if (!accept) {
+      n = i;
+      break;
+    }
+  }
+
+  // The committed extra token: residual normalize(max(p_n - q_n, 0)) after a rejection,
+  // the bonus from p_k when every draft is accepted.  Drawn by Gumbel-max (verify stream).
+  int32_t y;
+  double gap = kInf;
+  double resid_mass = -1.0;
+  int32_t flags = 0;
+  if (T == 0.0) {
+    y = p[(size_t)n].argmax;  // greedy: the residual of two one-hots is the target one-hot
+  } else {
+    std::vector<double> w((size_t)V);
+    if (n < k) {
+      resid_mass = 0.0;
+      for (int32_t x = 0; x < V; ++x) {
+#if ORACLE_MUTANT == 13
+        w[(size_t)x] = std::fabs(p[(size_t)n].p[(size_t)x] - q[(size_t)n].p[(size_t)x]);  // MUTANT 13
+#elif ORACLE_MUTANT == 2
+        w[(size_t)x] = p[(size_t)n].p[(size_t)x];  // MUTANT 2: resample from the target
+#else
+        w[(size_t)x] = std::max(p[(size_t)n].p[(size_t)x] - q[(size_t)n].p[(size_t)x], 0.0);
+#endif
+        resid_mass += w[(size_t)x];
+      }
+      if (!(resid_mass > 0.0)) {  // reachable only through rounding: fall back to p_n (R7)
+        w = p[(size_t)n].p;
+        flags |= 1;
+      }
+    } else {
+#if ORACLE_MUTANT == 12
+      w = p[(size_t)k - 1].p;  // MUTANT 12: bonus drawn at the wrong position
+#else
+      w = p[(size_t)k].p;
+#endif
+    }
+    y = gumbel_argmax(w, a.seed, 1u, (uint32_t)b, (uint32_t)n, a.offset, &gap);
+  }
+
+  // Outputs (R8, R9, R10, R11).
+  for (int32_t i = 0; i <= k; ++i) {
+    const size_t o = (size_t)b * (k + 1) + i;
+    if (i < n) {
+      const int32_t x = a.draft_tokens[(size_t)b * k + i];
+      a.tokens[o] = x;
+      a.logprobs[o] = std::log(p[(size_t)i].p[(size_t)x]);
+    } else if (i == n) {
+      a.tokens[o] = y;
+      a.logprobs[o] = std::log(p[(size_t)n].p[(size_t)y]);
+    } else {
+      a.tokens[o] = -1;
+      a.logprobs[o] = 0.0;
+    }
+  }
+#if ORACLE_MUTANT == 6
+  a.accept_len[b] = n;  // MUTANT 6: the extra token is not counted
+#else
+  a.accept_len[b] = n + 1;
+#endif
+  for (int32_t i = 0; i < k; ++i) {
+    double s = 0.0;
+    for (int32_t x = 0; x < V; ++x) {
+#if ORACLE_MUTANT == 7
+      s += std::fabs(p[(size_t)i].p[(size_t)x] - q[(size_t)i].p[(size_t)x]);  // MUTANT 7
+#else
+      s += std::min(p[(size_t)i].p[(size_t)x], q[(size_t)i].p[(size_t)x]);
+#endif
+    }
+#if ORACLE_MUTANT == 7
+    s = 1.0 - s;
+#endif
+    a.alpha[(size_t)b * k + i] = s;
+  }
+  if (a.diag) {
+    a.diag[(size_t)b * 4 + 0] = accept_margin;
+    a.diag[(size_t)b * 4 + 1] = gap;
+    a.diag[(size_t)b * 4 + 2] = topp_margin;
+    a.diag[(size_t)b * 4 + 3] = resid_mass;
+  }
+  if (a.dflags) a.dflags[b] = flags | (n << 8);
+}
+
+template <class F>
+void parallel_rows(int32_t n_rows, int32_t num_threads, F f) {
+  int32_t nt = num_threads > 0 ? num_threads : (int32_t)std::thread::hardware_concurrency();
+  if (nt < 1) nt = 1;
+  if (nt > n_rows) nt = n_rows;
+  if (nt <= 1) {
+    for (int32_t r = 0; r < n_rows; ++r) f(r);
+    return;
+  }
+  std::vector<std::thread> pool;
+  for (int32_t t = 0; t < nt; ++t)
+    pool.emplace_back([=]() {
+      for (int32_t r = t; r < n_rows; r += nt) f(r);
+    });
+  for (auto& th : pool) th.join();
+}
+
+}  // namespace
+
+extern "C" {
+
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) { philox10(ctr, key, out); }
+
+double oracle_accept_uniform(uint64_t seed, uint32_t b, uint32_t i, uint32_t offset) {
+  return accept_uniform(seed, b, i, offset);
+}
+
+double oracle_gumbel_uniform(uint64_t seed, uint32_t tag, uint32_t b, uint32_t j, uint32_t x, uint32_t offset) {
+  return gumbel_uniform(seed, tag, b, j, x, offset);
+}
+
+int oracle_row_probs(const double* logits, int32_t V, double T, int32_t K, double P, double* probs, double* info) {
+  std::vector<double> l(logits, logits + V);
+  RowDist d;
+  if (!row_dist(l, T, K, P, d)) return 1;
+  std::copy(d.p.begin(), d.p.end(), probs);
+  if (info) {
+    info[0] = d.m;
+    info[1] = (double)d.argmax;
+    info[2] = d.Z;
+    info[3] = (double)d.kept;
+    info[4] = d.thr;
+    info[5] = d.topp_margin;
+  }
+  return 0;
+}
+
+int oracle_spec_verify(const void* target_logits, const void* draft_logits, int32_t dtype,
+                       const int32_t* draft_tokens, const float* temperature, const int32_t* top_k,
+                       const float* top_p, int32_t B, int32_t k, int32_t V, uint64_t seed, uint64_t offset,
+                       int32_t* tokens, int32_t* accept_len, double* logprobs, double* alpha, double* diag,
+                       int32_t* dflags, int32_t num_threads) {
+  if (B < 1 || k < 1 || V < 1 || offset >= (1ull << 32)) return 1;
+  if (dtype != ORACLE_DTYPE_BF16 && dtype != ORACLE_DTYPE_F32) return 1;
+  VerifyArgs a{target_logits, draft_logits, dtype, draft_tokens, temperature, top_k, top_p, B, k, V,
+               seed, (uint32_t)offset, tokens, accept_len, logprobs, alpha, diag, dflags};
+  parallel_rows(B, num_threads, [&](int32_t b) { verify_row(a, b); });
+  return 0;
+}
+
+int oracle_sample(const void* logits, int32_t dtype, const float* temperature, const int32_t* top_k,
+                  const float* top_p, const int32_t* row_b, const int32_t* row_pos, int32_t R, int32_t V,
+                  uint64_t seed, uint64_t offset, int32_t* tokens, double* logprobs, double* gap,
+                  int32_t num_threads) {
+  if (R < 1 || V < 1 || offset >= (1ull << 32)) return 1;
+  if (dtype != ORACLE_DTYPE_BF16 && dtype != ORACLE_DTYPE_F32) return 1;
+  parallel_rows(R, num_threads, [&](int32_t r) {
+    std::vector<double> l;
+    load_row(logits, dtype, (size_t)r, V, l);
+    RowDist d;
+    double g = kInf;
+    if (!params_valid(temperature[r], top_k[r], top_p[r]) || row_has_nan_or_posinf(l) ||
+        !row_dist(l, (double)temperature[r], top_k[r], (double)top_p[r], d)) {
+      tokens[r] = -1;
+      logprobs[r] = kNaN;
+      if (gap) gap[r] = kInf;
+      return;
+    }
+    int32_t y;
+    if (temperature[r] == 0.0f) {
+      y = d.argmax;
+    } else {
+      y = gumbel_argmax(d.p, seed, 2u, (uint32_t)row_b[r], (uint32_t)row_pos[r], (uint32_t)offset, &g);
+    }
+    tokens[r] = y;
+    logprobs[r] = std::log(d.p[(size_t)y]);
+    if (gap) gap[r] = g;
+  });
+  return 0;
+}
+
+}  // extern "C"

@@ -1,0 +1,459 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each ``pin_*`` function takes a loaded oracle and raises ``AssertionError`` when the
+oracle disagrees with an independent fact: a published known-answer vector, a value the
+pages print, a library routine (scipy softmax), a textbook sort-based sampler written
+here in numpy, a closed form, or an exact law checked by Monte-Carlo.  None of them
+re-types the oracle's own code.  The same functions run against the planted mutants of
+the oracle (negative controls): every mutant must fail at least one pin.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+from scipy import special, stats
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+CHI2_P_MIN = 1e-3
+
+
+# ---------------------------------------------------------------------------------------
+# independent helpers (numpy / scipy only)
+# ---------------------------------------------------------------------------------------
+
+def softmax_T(l, T):
+    return special.softmax(np.asarray(l, dtype=np.float64) / T)
+
+
+def textbook_topk_topp(l, T, K, P):
+    """Sort-based sampler on a tie-free row: keep the K most likely tokens, then the
+    smallest most-likely prefix holding at least P of the renormalised mass."""
+    l = np.asarray(l, dtype=np.float64)
+    V = l.shape[0]
+    order = np.argsort(-l, kind="stable")
+    keep = np.zeros(V, dtype=bool)
+    n = K if 0 < K < V else V
+    keep[order[:n]] = True
+    if P < 1.0:
+        p = softmax_T(l[order[:n]], T)
+        c = np.cumsum(p)
+        m = int(np.searchsorted(c, P * c[-1], side="left")) + 1
+        keep[:] = False
+        keep[order[:min(m, n)]] = True
+    out = np.zeros(V)
+    out[keep] = softmax_T(l[keep], T)
+    return out
+
+
+def expected_accept_length(alphas):
+    """Closed form of the expected committed tokens per verify step with fresh drafts:
+    1 + sum over depths d of the probability that the first d drafts are all accepted."""
+    total, run = 1.0, 1.0
+    for a in alphas:
+        run *= a
+        total += run
+    return total
+
+
+def chi2_pvalue(counts, probs):
+    counts = np.asarray(counts, dtype=np.float64)
+    probs = np.asarray(probs, dtype=np.float64)
+    n = counts.sum()
+    mask = probs > 0
+    assert np.all(counts[~mask] == 0), "mass observed on a zero-probability outcome"
+    exp = probs[mask] / probs[mask].sum() * n
+    return stats.chisquare(counts[mask], exp).pvalue
+
+
+def f32(x):
+    return np.asarray(x, dtype=np.float32)
+
+
+def _rows(rng, n, V, sigma=2.0):
+    return rng.normal(0.0, sigma, size=(n, V))
+
+
+def read_golden_table(name):
+    out = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                out.append(line)
+    return out
+
+
+def _parse_num(tok):
+    if tok.startswith("ln"):
+        return math.log(float(tok[2:]))
+    return float(tok)
+
+
+# ---------------------------------------------------------------------------------------
+# random streams
+# ---------------------------------------------------------------------------------------
+
+def pin_philox_kat(o):
+    for line in read_golden_table("philox4x32_10_kat.txt"):
+        v = [int(t, 16) for t in line.split()]
+        out = o.philox(v[0:4], v[4:6])
+        assert [int(x) for x in out] == v[6:10], f"Philox KAT mismatch for {line}"
+
+
+def pin_stream_layout(o):
+    """The accept and Gumbel uniforms are the documented words of the documented counters."""
+    seed = (0x1234ABCD << 32) | 0x9E3779B9
+    key = [seed & 0xFFFFFFFF, seed >> 32]
+    for b, i, off in [(0, 0, 0), (5, 3, 7), (1023, 6, 99), (7, 1, 2**32 - 1)]:
+        w = o.philox([i >> 2, b, 0, off], key)[i & 3]
+        assert o.accept_uniform(seed, b, i, off) == float(int(w) >> 8) * 2.0 ** -24
+    for tag in (1, 2):
+        for b, j, x, off in [(0, 0, 0, 0), (3, 2, 157183, 5), (255, 4, 4097, 99)]:
+            w = o.philox([x >> 2, b, (tag << 24) | j, off], key)[x & 3]
+            assert o.gumbel_uniform(seed, tag, b, j, x, off) == ((int(w) >> 9) + 0.5) * 2.0 ** -23
+
+
+def pin_uniform_distribution(o):
+    us = np.array([o.accept_uniform(0, b, i, 0) for b in range(2000) for i in range(4)])
+    assert us.min() >= 0.0 and us.max() < 1.0
+    assert stats.kstest(us, "uniform").pvalue > CHI2_P_MIN
+    gs = np.array([o.gumbel_uniform(3, 1, 2, 1, x, 11) for x in range(8000)])
+    assert gs.min() > 0.0 and gs.max() < 1.0
+    assert stats.kstest(gs, "uniform").pvalue > CHI2_P_MIN
+
+
+# ---------------------------------------------------------------------------------------
+# the sampler distribution
+# ---------------------------------------------------------------------------------------
+
+def pin_softmax_temperature(o):
+    rng = np.random.default_rng(11)
+    for l in _rows(rng, 6, 300, 3.0):
+        for T in (0.37, 1.0, 1.9):
+            p, info = o.row_probs(l, T)
+            np.testing.assert_allclose(p, softmax_T(l, T), rtol=0, atol=1e-14)
+            assert info["argmax"] == int(np.argmax(l))
+
+
+def pin_topk_textbook(o):
+    rng = np.random.default_rng(12)
+    for l in _rows(rng, 6, 500):
+        for K in (1, 2, 17, 50, 499):
+            p, _ = o.row_probs(l, 0.8, K, 1.0)
+            np.testing.assert_allclose(p, textbook_topk_topp(l, 0.8, K, 1.0), rtol=0, atol=1e-14)
+
+
+def pin_topp_textbook(o):
+    rng = np.random.default_rng(13)
+    for l in _rows(rng, 6, 500):
+        for P in (0.05, 0.5, 0.9, 0.95, 0.999):
+            p, _ = o.row_probs(l, 1.3, 0, P)
+            np.testing.assert_allclose(p, textbook_topk_topp(l, 1.3, 0, P), rtol=0, atol=1e-14)
+
+
+def pin_topk_then_topp_textbook(o):
+    rng = np.random.default_rng(14)
+    for l in _rows(rng, 6, 400, 1.5):
+        for K, P in ((50, 0.95), (10, 0.5), (200, 0.9)):
+            p, _ = o.row_probs(l, 0.7, K, P)
+            np.testing.assert_allclose(p, textbook_topk_topp(l, 0.7, K, P), rtol=0, atol=1e-14)
+
+
+def pin_golden_tie_cases(o):
+    for line in read_golden_table("sampler_tie_cases.txt"):
+        name, logits, T, K, P, want = [s.strip() for s in line.split("|")]
+        l = [_parse_num(t) for t in logits.split()]
+        p, _ = o.row_probs(l, float(T), int(K), float(P))
+        np.testing.assert_allclose(p, [float(t) for t in want.split()], rtol=0, atol=1e-12, err_msg=name)
+
+
+def pin_off_switches(o):
+    rng = np.random.default_rng(15)
+    for l in _rows(rng, 4, 64):
+        base, _ = o.row_probs(l, 1.1)
+        for K, P in ((0, 1.0), (64, 1.0), (1000, 1.0), (0, 1.5), (64, float("inf"))):
+            p, _ = o.row_probs(l, 1.1, K, P)
+            np.testing.assert_array_equal(p, base)
+        p1, _ = o.row_probs(l, 1.1, 1, 1.0)   # top-1 on a tie-free row is the greedy one-hot
+        g, _ = o.row_probs(l, 0.0)
+        np.testing.assert_array_equal(p1, g)
+        assert g[int(np.argmax(l))] == 1.0
+
+
+# ---------------------------------------------------------------------------------------
+# verify step
+# ---------------------------------------------------------------------------------------
+
+def _tiny_case(rng, B, k, V, sigma_t=1.0, sigma_n=0.7):
+    t = rng.normal(0.0, sigma_t, size=(k + 1, V)).astype(np.float32)
+    d = (t[:k] + rng.normal(0.0, sigma_n, size=(k, V))).astype(np.float32)
+    return (np.broadcast_to(t, (B, k + 1, V)).copy(), np.broadcast_to(d, (B, k, V)).copy())
+
+
+def _fresh_drafts(o, draft, T, K, P):
+    """Draw every batch row's drafts from its own plain-sampler stream (independent trials)."""
+    B, k, V = draft.shape
+    tok, _, _ = o.sample(draft.reshape(B * k, V), np.repeat(T, k), np.repeat(K, k), np.repeat(P, k),
+                         np.repeat(np.arange(B), k), np.tile(np.arange(k), B), seed=7, offset=3)
+    return tok.reshape(B, k)
+
+
+def _params(B, T=1.0, K=0, P=1.0):
+    return f32(np.full(B, T)), np.full(B, K, dtype=np.int32), f32(np.full(B, P))
+
+
+def pin_alpha_identities(o):
+    rng = np.random.default_rng(21)
+    B, k, V = 3, 3, 64
+    t, d = _tiny_case(rng, B, k, V)
+    for T, K, P in ((1.0, 0, 1.0), (0.6, 10, 1.0), (1.3, 0, 0.8), (0.9, 20, 0.9)):
+        Ta, Ka, Pa = _params(B, T, K, P)
+        drafts = np.zeros((B, k), dtype=np.int32)
+        r = o.spec_verify(t, d, drafts, Ta, Ka, Pa, seed=1)
+        for i in range(k):
+            p = textbook_topk_topp(t[0, i].astype(np.float64), T, K, P)
+            q = textbook_topk_topp(d[0, i].astype(np.float64), T, K, P)
+            tv_alpha = 1.0 - 0.5 * np.abs(p - q).sum()   # total-variation identity
+            np.testing.assert_allclose(r.alpha[:, i], tv_alpha, atol=1e-12)
+    # identical rows: alpha = 1; disjoint one-hot supports (top-1, different argmax): alpha = 0
+    Ta, Ka, Pa = _params(B, 1.0, 0, 1.0)
+    r = o.spec_verify(t, t[:, :k].copy(), np.zeros((B, k), np.int32), Ta, Ka, Pa)
+    np.testing.assert_allclose(r.alpha, 1.0, atol=1e-12)
+    t2 = np.zeros((1, 2, 8), np.float32)
+    d2 = np.zeros((1, 1, 8), np.float32)
+    t2[0, 0, 2] = 5.0
+    d2[0, 0, 6] = 5.0
+    r = o.spec_verify(t2, d2, np.array([[6]]), *_params(1, 1.0, 1, 1.0))
+    assert r.alpha[0, 0] == 0.0
+    assert r.tokens[0, 0] == 2 and r.accept_len[0] == 1   # rejected; residual is the target one-hot
+    assert np.all((r.alpha >= 0) & (r.alpha <= 1))
+
+
+def pin_identity_accepts_all(o):
+    """Bit-identical draft and target rows: every draft is accepted (p/q = 1 > u)."""
+    rng = np.random.default_rng(22)
+    B, k, V = 200, 3, 50
+    t, _ = _tiny_case(rng, B, k, V)
+    for T, K, P in ((1.0, 0, 1.0), (0.7, 5, 0.9)):
+        Ta, Ka, Pa = _params(B, T, K, P)
+        d = t[:, :k].copy()
+        drafts = _fresh_drafts(o, d, Ta, Ka, Pa)
+        r = o.spec_verify(t, d, drafts, Ta, Ka, Pa, seed=5)
+        assert np.all(r.accept_len == k + 1)
+        np.testing.assert_array_equal(r.tokens[:, :k], drafts)
+
+
+def pin_greedy_chain(o):
+    """Greedy (T = 0): accept while the draft is the target argmax; the extra token is the
+    target argmax at the first mismatch (lowest index on exact ties)."""
+    rng = np.random.default_rng(23)
+    B, k, V = 64, 3, 40
+    t = rng.integers(-4, 5, size=(B, k + 1, V)).astype(np.float32)   # many exact ties
+    d = rng.integers(-4, 5, size=(B, k, V)).astype(np.float32)
+    drafts = rng.integers(0, V, size=(B, k)).astype(np.int32)
+    am = np.argmax(t, axis=2)   # numpy argmax returns the first maximum
+    hit = rng.random((B, k)) < 0.6
+    drafts = np.where(hit, am[:, :k], drafts).astype(np.int32)
+    r = o.spec_verify(t, d, drafts, *_params(B, 0.0, 7, 0.5))
+    for b in range(B):
+        n = 0
+        while n < k and drafts[b, n] == am[b, n]:
+            n += 1
+        want = list(drafts[b, :n]) + [am[b, n]] + [-1] * (k - n)
+        assert list(r.tokens[b]) == want, (b, list(r.tokens[b]), want)
+        assert r.accept_len[b] == n + 1
+        np.testing.assert_array_equal(r.logprobs[b], 0.0)
+        np.testing.assert_array_equal(r.alpha[b], (am[b, :k] == np.argmax(d[b], axis=1)).astype(float))
+
+
+def pin_marginal_k1(o):
+    """Committed first token ~ p_0 (chi-square over 1e5 independent trials, V = 8)."""
+    rng = np.random.default_rng(31)
+    B, k, V = 100_000, 1, 8
+    t, d = _tiny_case(rng, B, k, V, 1.0, 0.9)
+    T, K, P = _params(B, 1.0)
+    r = o.spec_verify(t, d, _fresh_drafts(o, d, T, K, P), T, K, P, seed=9, offset=1)
+    counts = np.bincount(r.tokens[:, 0], minlength=V)
+    assert chi2_pvalue(counts, softmax_T(t[0, 0], 1.0)) > CHI2_P_MIN
+
+
+def pin_marginal_k2(o):
+    """k = 2, truncated sampler: token 0 ~ p_0; token 1 given that draft 0 was accepted ~ p_1."""
+    rng = np.random.default_rng(32)
+    B, k, V = 100_000, 2, 16
+    t, d = _tiny_case(rng, B, k, V, 1.2, 0.8)
+    T, K, P = _params(B, 0.9, 12, 0.95)
+    r = o.spec_verify(t, d, _fresh_drafts(o, d, T, K, P), T, K, P, seed=4, offset=2)
+    p0 = textbook_topk_topp(t[0, 0].astype(np.float64), 0.9, 12, 0.95)
+    p1 = textbook_topk_topp(t[0, 1].astype(np.float64), 0.9, 12, 0.95)
+    assert chi2_pvalue(np.bincount(r.tokens[:, 0], minlength=V), p0) > CHI2_P_MIN
+    sel = r.accept_len >= 2
+    assert chi2_pvalue(np.bincount(r.tokens[sel, 1], minlength=V), p1) > CHI2_P_MIN
+
+
+def pin_marginal_bonus(o):
+    """With drafts equal to targets except the last target row, every draft is accepted and
+    the bonus token ~ p_k."""
+    rng = np.random.default_rng(33)
+    B, k, V = 100_000, 2, 8
+    t, _ = _tiny_case(rng, B, k, V, 1.0)
+    d = t[:, :k].copy()
+    T, K, P = _params(B, 1.0)
+    r = o.spec_verify(t, d, _fresh_drafts(o, d, T, K, P), T, K, P, seed=6)
+    assert np.all(r.accept_len == k + 1)
+    assert chi2_pvalue(np.bincount(r.tokens[:, k], minlength=V), softmax_T(t[0, k], 1.0)) > CHI2_P_MIN
+
+
+def pin_joint_law_v3(o):
+    """V = 3, k = 2, fixed drafts: the law of (accepted count n, extra token y) is
+    P(n=j, y) = prod_{i<j} a_i * (1 - a_j) * r_j(y) for j < k and prod a_i * p_k(y) for j = k,
+    with a_i = min(1, p_i(x_i)/q_i(x_i)) and r_j the normalised positive part of p_j - q_j."""
+    B, k, V = 100_000, 2, 3
+    tl = np.array([[0.2, 1.0, -0.5], [0.9, -0.3, 0.4], [-0.2, 0.6, 0.1]], np.float32)
+    dl = np.array([[1.1, 0.1, -0.2], [0.1, 0.5, 0.3]], np.float32)
+    x = np.array([0, 1], np.int32)
+    t = np.broadcast_to(tl, (B, k + 1, V)).copy()
+    d = np.broadcast_to(dl, (B, k, V)).copy()
+    r = o.spec_verify(t, d, np.broadcast_to(x, (B, k)).copy(), *_params(B, 1.0), seed=12, offset=4)
+    p = [softmax_T(tl[i], 1.0) for i in range(k + 1)]
+    q = [softmax_T(dl[i], 1.0) for i in range(k)]
+    a = [min(1.0, p[i][x[i]] / q[i][x[i]]) for i in range(k)]
+    law = np.zeros((k + 1, V))
+    run = 1.0
+    for j in range(k):
+        res = np.maximum(p[j] - q[j], 0.0)
+        law[j] = run * (1.0 - a[j]) * res / res.sum()
+        run *= a[j]
+    law[k] = run * p[k]
+    n = r.accept_len - 1
+    y = r.tokens[np.arange(B), n]
+    counts = np.zeros((k + 1, V))
+    np.add.at(counts, (n, y), 1)
+    assert chi2_pvalue(counts.ravel(), law.ravel()) > CHI2_P_MIN
+
+
+def pin_expected_accept_length(o):
+    """Mean committed tokens with fresh drafts = 1 + a_0 + a_0 a_1 (closed form from the alphas)."""
+    rng = np.random.default_rng(41)
+    B, k, V = 100_000, 2, 12
+    t, d = _tiny_case(rng, B, k, V, 1.0, 0.6)
+    T, K, P = _params(B, 1.0)
+    r = o.spec_verify(t, d, _fresh_drafts(o, d, T, K, P), T, K, P, seed=3, offset=8)
+    alphas = [np.minimum(softmax_T(t[0, i], 1.0), softmax_T(d[0, i], 1.0)).sum() for i in range(k)]
+    want = expected_accept_length(alphas)
+    se = r.accept_len.std() / math.sqrt(B)
+    assert abs(r.accept_len.mean() - want) < 4.5 * se, (r.accept_len.mean(), want, se)
+
+
+def pin_expected_accept_length_given_drafts(o):
+    """Fixed drafts, randomness over u only: E[accept_len] = 1 + sum_d prod_{j<d} min(1, p_j/q_j)."""
+    rng = np.random.default_rng(42)
+    B, k, V = 100_000, 3, 10
+    t, d = _tiny_case(rng, B, k, V, 1.0, 0.8)
+    x = np.array([1, 4, 7], np.int32)
+    r = o.spec_verify(t, d, np.broadcast_to(x, (B, k)).copy(), *_params(B, 1.0), seed=17, offset=5)
+    a = [min(1.0, softmax_T(t[0, i], 1.0)[x[i]] / softmax_T(d[0, i], 1.0)[x[i]]) for i in range(k)]
+    want = expected_accept_length(a)
+    se = r.accept_len.std() / math.sqrt(B)
+    assert abs(r.accept_len.mean() - want) < 4.5 * se, (r.accept_len.mean(), want, se)
+
+
+def pin_pages_accept_length(o):
+    """The closed form reproduces the pages' printed expected accept lengths from their alphas."""
+    vals = dict(line.split() for line in read_golden_table("accept_length_table.txt"))
+    a1, a2 = float(vals["alpha_depth1"]), float(vals["alpha_depth2_given_1"])
+    assert round(expected_accept_length([a1]), 2) == float(vals["expected_accept_length_k1"])
+    assert round(expected_accept_length([a1, a2]), 2) == float(vals["expected_accept_length_k2"])
+
+
+def pin_logprobs(o):
+    """Reported logprobs are ln p_i(token_i) under the processed target distribution."""
+    rng = np.random.default_rng(51)
+    B, k, V = 50, 2, 30
+    t, d = _tiny_case(rng, B, k, V, 1.5, 0.9)
+    for T, K, P in ((1.0, 0, 1.0), (0.8, 10, 0.9)):
+        Ta, Ka, Pa = _params(B, T, K, P)
+        r = o.spec_verify(t, d, _fresh_drafts(o, d, Ta, Ka, Pa), Ta, Ka, Pa, seed=2)
+        with np.errstate(divide="ignore"):
+            _check_logprobs(r, t, B, k, T, K, P)
+
+
+def _check_logprobs(r, t, B, k, T, K, P):
+    for b in range(B):
+        for i in range(k + 1):
+            if i < r.accept_len[b]:
+                p = textbook_topk_topp(t[b, i].astype(np.float64), T, K, P)
+                np.testing.assert_allclose(r.logprobs[b, i], np.log(p[r.tokens[b, i]]), atol=1e-12)
+            else:
+                assert r.tokens[b, i] == -1 and r.logprobs[b, i] == 0.0
+
+
+def pin_residual_mass(o):
+    """At a rejection, the residual mass equals 1 - alpha at that position."""
+    rng = np.random.default_rng(52)
+    B, k, V = 400, 2, 20
+    t, d = _tiny_case(rng, B, k, V, 1.0, 1.0)
+    T, K, P = _params(B, 1.0)
+    r = o.spec_verify(t, d, _fresh_drafts(o, d, T, K, P), T, K, P, seed=8)
+    n = r.accept_len - 1
+    rej = n < k
+    assert rej.any()
+    np.testing.assert_allclose(r.residual_mass[rej], 1.0 - r.alpha[np.arange(B)[rej], n[rej]], atol=1e-12)
+
+
+def pin_invalid_rows(o):
+    """Rows with unusable inputs come back as sentinels; the other rows are untouched."""
+    rng = np.random.default_rng(53)
+    B, k, V = 8, 2, 16
+    t, d = _tiny_case(rng, B, k, V)
+    T, K, P = _params(B, 1.0)
+    drafts = np.zeros((B, k), np.int32)
+    t[1, 0, 3] = np.nan
+    d[2, 1, 5] = np.inf
+    t[3, 2, :] = -np.inf
+    T[4] = -1.0
+    K[5] = -3
+    P[6] = 0.0
+    drafts[7, 1] = V
+    r = o.spec_verify(t, d, drafts, T, K, P)
+    bad = [1, 2, 3, 4, 5, 6, 7]
+    assert np.all(r.accept_len[bad] == 0) and np.all(r.tokens[bad] == -1)
+    assert np.all(np.isnan(r.logprobs[bad])) and np.all(np.isnan(r.alpha[bad]))
+    assert r.accept_len[0] >= 1 and np.all(np.isfinite(r.alpha[0]))
+    # -inf entries are legal (probability zero)
+    t2, d2 = _tiny_case(rng, 1, 1, 16)
+    t2[0, :, ::2] = -np.inf
+    r2 = o.spec_verify(t2, d2, np.array([[1]]), *_params(1, 1.0))
+    assert r2.accept_len[0] >= 1 and r2.tokens[0, r2.accept_len[0] - 1] % 2 == 1
+
+
+def pin_determinism(o):
+    rng = np.random.default_rng(54)
+    B, k, V = 300, 2, 32
+    t, d = _tiny_case(rng, B, k, V)
+    T, K, P = _params(B, 1.0)
+    drafts = _fresh_drafts(o, d, T, K, P)
+    r1 = o.spec_verify(t, d, drafts, T, K, P, seed=77, offset=4, num_threads=1)
+    r2 = o.spec_verify(t, d, drafts, T, K, P, seed=77, offset=4, num_threads=5)
+    np.testing.assert_array_equal(r1.tokens, r2.tokens)
+    np.testing.assert_array_equal(r1.logprobs, r2.logprobs)
+    r3 = o.spec_verify(t, d, drafts, T, K, P, seed=77, offset=5)
+    assert not np.array_equal(r1.tokens, r3.tokens)
+
+
+def pin_plain_sampler_marginal(o):
+    """The plain sampler draws from the processed distribution (it produces the drafts)."""
+    rng = np.random.default_rng(61)
+    R, V = 100_000, 10
+    l = rng.normal(0.0, 1.3, size=V).astype(np.float32)
+    T, K, P = 0.8, 7, 0.9
+    tok, lp, _ = o.sample(np.broadcast_to(l, (R, V)).copy(), np.full(R, T), np.full(R, K), np.full(R, P),
+                          np.arange(R), np.zeros(R), seed=5, offset=6)
+    p = textbook_topk_topp(l.astype(np.float64), T, K, P)
+    assert chi2_pvalue(np.bincount(tok, minlength=V), p) > CHI2_P_MIN
+    np.testing.assert_allclose(lp, np.log(p[tok]), atol=1e-12)
+
+
+ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_") and callable(v)]

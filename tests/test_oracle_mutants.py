@@ -1,0 +1,26 @@
+"""Negative controls: every planted mistake in the oracle must fail at least one pin.
+
+Each mutant is the oracle built with -DORACLE_MUTANT=<n>, which changes one step
+(swapped p/q in the accept test, resampling from p instead of the residual, strict top-p
+inequality, highest-index ties, no renormalisation after top-k, accept length without
+the extra token, wrong alpha, wrong Gumbel sign, temperature multiplying, top-k off by
+one, Philox one round short, bonus at the wrong position, residual without the clamp).
+"""
+import pytest
+
+import oracle
+import oracle_pins
+
+MUTANTS = list(range(1, 14))
+
+
+@pytest.mark.parametrize("mutant", MUTANTS)
+def test_mutant_is_caught(mutant):
+    o = oracle.Oracle(mutant=mutant, rebuild=True)
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(o)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"mutant {mutant} passed every pin"
