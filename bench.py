@@ -1,0 +1,196 @@
+"""Benchmark of libspecverify on one MI355X: verified rows/s and logit bandwidth vs the HBM roofline.
+
+One step = one spec_verify() call over one batch of synthetic inputs already resident in HBM
+(default workload: B=64, k=2, V=157184, bf16, mixed temperature / top-k / top-p per row).
+Input sets are rotated so that the working set exceeds the 256 MB Infinity Cache.
+
+Prints one JSON line.  Besides the throughput it reports
+  roofline:     algorithmic logit bytes per launch / average kernel duration (HIP events around
+                each launch in a separate pass), against the 8 TB/s HBM peak;
+  cpu_baseline: the CPU oracle timed on this host on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified rows/s + logits HBM GB/s (% peak), B=64 k=2 V=157184 bf16"
+HBM_PEAK_GBPS = 8000.0
+ROTATE_BYTES = 1 << 30
+KERNEL_SRC = [os.path.join(ROOT, "rejection_sampling_verify_16_amd", "csrc", f)
+              for f in ("specverify.hip", "sv_common.h")]
+
+
+def kernel_digest() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SRC:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(config: str):
+    """HBM traffic per launch from the committed PMC summary, if it was taken on this kernel."""
+    path = os.path.join(ROOT, "profiles", f"traffic_config{config}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_digest") != kernel_digest():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--config", default="3", help="workload: 1, 2, 3, 4a, 4b, 5")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+    import rejection_sampling_verify_16_amd as sv
+    from rejection_sampling_verify_16_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.CONFIGS[args.config]()
+    B, k, V = w.B, w.k, w.V
+    bf16 = w.dtype == "bf16"
+
+    def to_dev(a):
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if bf16 else torch.from_numpy(a)
+        return t.to(dev)
+
+    tgt0, drf0 = to_dev(w.target), to_dev(w.draft)
+    T = torch.from_numpy(w.temperature).to(dev)
+    K = torch.from_numpy(w.top_k).to(dev)
+    P = torch.from_numpy(w.top_p).to(dev)
+
+    # drafts sampled from the processed q by the library's plain sampler
+    rows, Tr, Kr, Pr, rb, rp = w.draft_sampling_inputs()
+    tt = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).to(dev)
+    dtok, _ = sv.spec_sample(drf0.reshape(B * k, V), tt(Tr, np.float32), tt(Kr, np.int32), tt(Pr, np.float32),
+                             tt(rb, np.int32), tt(rp, np.int32), seed=w.draft_seed, offset=w.draft_offset)
+    drafts = dtok.reshape(B, k).contiguous()
+    for b, i, t in w.draft_overrides:
+        drafts[b, i] = t
+
+    n_sets = max(2, math.ceil(ROTATE_BYTES / w.logit_bytes))
+    sets = [(tgt0, drf0)] + [(tgt0.clone(), drf0.clone()) for _ in range(n_sets - 1)]
+    out = sv.alloc_outputs(B, k, dev)
+    ws = sv.make_workspace(B, k, V, sv.SPEC_DTYPE_BF16 if bf16 else sv.SPEC_DTYPE_F32, dev)
+    stream = torch.cuda.current_stream(dev)
+    offsets = w.offsets
+
+    def step(i):
+        t_, d_ = sets[i % n_sets]
+        sv.spec_verify(t_, d_, drafts, T, K, P, seed=w.seed, offset=offsets[i % len(offsets)], out=out,
+                       workspace=ws, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` calls ----
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1)
+    ms_per_step = ms / args.steps
+
+    # ---- per-launch kernel duration (event pair around each launch) ----
+    n_prof = min(args.steps, 200)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_prof)]
+    for i in range(n_prof):
+        evs[i][0].record(stream)
+        step(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    durs = np.array([a.elapsed_time(b) for a, b in evs])
+    kern_ms = float(np.median(durs))
+    kern_mean_ms = float(durs.mean())
+
+    logit_bytes = w.logit_bytes
+    achieved_gbps = logit_bytes / (kern_mean_ms * 1e-3) / 1e9
+    rows_per_s = B / (ms_per_step * 1e-3)
+    traffic = load_traffic(args.config)
+
+    result = {
+        "metric": METRIC,
+        "value": rows_per_s,
+        "unit": "verified rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "k": k, "V": V, "logit_bytes_per_step": logit_bytes,
+                   "rotating_input_sets": n_sets},
+        "logits_GBps": logit_bytes / (ms_per_step * 1e-3) / 1e9,
+        "pct_hbm_peak": 100.0 * logit_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "wall_s": wall,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved_gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved_gbps / HBM_PEAK_GBPS,
+            "traffic": traffic,
+            "kernel": "verify_kernel",
+            "kernel_ms_mean": kern_mean_ms,
+            "kernel_ms_median": kern_ms,
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, drafts.cpu().numpy(), args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, drafts, seconds):
+    """The CPU oracle, as it stands, on whole calls of the same workload until ~`seconds` pass."""
+    import oracle
+    o = oracle.get()
+    threads = min(os.cpu_count() or 1, 16)
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        o.spec_verify(w.target, w.draft, drafts, w.temperature, w.top_k, w.top_p, seed=w.seed,
+                      offset=w.offsets[calls % len(w.offsets)], num_threads=threads)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or calls >= 1000:
+            break
+    return {"value": w.B * calls / el, "unit": "verified rows/s", "cores": threads, "kind": "oracle",
+            "sample": f"{calls} full calls of the benchmark workload ({w.B} batch rows each), {el:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

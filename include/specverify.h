@@ -1,0 +1,119 @@
+/*
+ * specverify.h -- C ABI of libspecverify, the MI355X (gfx950) speculative-decoding verify sampler.
+ *
+ * What the library computes (AReno pull request "feat(engine): MTP training loss and speculative
+ * decoding for bailing_v3", section "What does this PR do?", Phase 2 paragraph; its accept-probability
+ * table; its per-step optimisation table):
+ *
+ *   For every batch row b, the k+1 target logit rows and the k draft logit rows are turned into the
+ *   distributions plain sampling would draw from (temperature, then top-k, then top-p on the top-k
+ *   renormalised mass, ties at a threshold kept whole; temperature 0 = greedy one-hot at the
+ *   lowest-index maximum): p_0..p_k (target) and q_0..q_{k-1} (draft).  Draft x_i is accepted while
+ *   p_i(x_i) > 0 and (q_i(x_i) == 0 or u_i < p_i(x_i) / q_i(x_i)); at the first rejection n one token
+ *   is drawn from normalize(max(p_n - q_n, 0)), and when all k are accepted a bonus token is drawn
+ *   from p_k.  Draws are Gumbel-max (argmax of ln w(x) + G(x), lowest index on exact ties) on a
+ *   Philox-4x32-10 stream.  Reported are the committed tokens, their count, ln p_i of each committed
+ *   token, and alpha_i = sum_x min(p_i(x), q_i(x)) for every draft position.
+ *
+ * Random stream (Philox-4x32-10 of Salmon et al., SC'11; key = (seed & 0xffffffff, seed >> 32)):
+ *   accept uniform u(b,i):        counter (i>>2, b, 0, offset), word i&3, u = (w>>8) * 2^-24
+ *   verify Gumbel U(b,j,x):       counter (x>>2, b, (1<<24)|j, offset), word x&3, U = ((w>>9)+0.5) * 2^-23
+ *   plain-sampler Gumbel U(b,i,x): counter (x>>2, b, (2<<24)|i, offset), word x&3, same map
+ * b is the batch row index within the call.  Replaying a call with the same (seed, offset) reproduces
+ * its outputs bit for bit; callers advance `offset` between calls.
+ *
+ * Memory and streams.  Every pointer except `stream` is a device pointer owned by the caller.  The
+ * library allocates nothing per call and keeps no per-call state outside the caller's workspace.  A
+ * call only enqueues work on `stream` (a hipStream_t; NULL = the default stream) and returns without
+ * synchronising, so it can be captured in a HIP graph.  Outputs are valid once the stream reaches the
+ * enqueued work.  Calls that share one workspace must be ordered on one stream.
+ *
+ * Errors.  Scalar, pointer and size problems detectable on the host return a status and enqueue
+ * nothing.  Problems found in the data (a draft token outside [0, V), a NaN or +inf logit in any of
+ * a batch row's 2k+1 rows, a row that is entirely -inf, a temperature that is NaN, negative or
+ * infinite, top_k < 0, top_p <= 0 or NaN) turn that batch row into a sentinel row: accept_len 0,
+ * tokens -1, logprobs NaN, alpha NaN.  -inf logits are legal and mean probability 0.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SPEC_DTYPE_BF16 = 0, SPEC_DTYPE_F32 = 1 } spec_dtype_t;
+
+typedef enum {
+  SPEC_OK = 0,
+  SPEC_ERR_INVALID_ARGUMENT = 1,   /* bad scalar, null or misaligned pointer, offset >= 2^32 */
+  SPEC_ERR_WORKSPACE = 2,          /* workspace null or smaller than spec_verify_workspace_size() */
+  SPEC_ERR_UNSUPPORTED_DEVICE = 3, /* the current device is not a gfx950 */
+  SPEC_ERR_LAUNCH = 4              /* the HIP runtime refused the launch */
+} spec_status_t;
+
+/*
+ * Bytes of device workspace spec_verify() needs for these sizes (0 if the sizes are invalid).
+ * The workspace must be zero-filled once before its first use (e.g. hipMemset); every completed
+ * call leaves the bytes the next call relies on at zero again, so it can be reused without clearing.
+ */
+size_t spec_verify_workspace_size(int32_t B, int32_t k, int32_t V, spec_dtype_t dtype);
+
+/*
+ * The verify step (see the top of this file for the method).
+ *
+ *   target_logits  [B, k+1, V] row-major, contiguous, dtype; 16-byte aligned
+ *   draft_logits   [B, k,   V] row-major, contiguous, dtype; 16-byte aligned
+ *   dtype          SPEC_DTYPE_BF16 (V % 8 == 0) or SPEC_DTYPE_F32 (V % 4 == 0)
+ *   draft_tokens   int32 [B, k]
+ *   temperature    float [B]   0 = greedy (top_k/top_p ignored)
+ *   top_k          int32 [B]   0 or >= V = off
+ *   top_p          float [B]   >= 1 (including +inf) = off
+ *   B, k, V        1 <= B <= 2^20, 1 <= k <= 8, 8 <= V <= 2^20
+ *   seed, offset   Philox key and counter word 3; offset < 2^32
+ *   tokens         out int32 [B, k+1]  x_0..x_{n-1}, the drawn token, then -1
+ *   accept_len     out int32 [B]       n + 1 (committed tokens, 1..k+1), 0 for a sentinel row
+ *   logprobs       out float [B, k+1]  ln p_i(tokens[b,i]) for i <= n, 0 after
+ *   alpha          out float [B, k]    sum_x min(p_i(x), q_i(x)) for every i < k
+ *   workspace      device scratch of at least spec_verify_workspace_size() bytes (see there)
+ *   stream         hipStream_t or NULL
+ * Every output element is written by every successful call.
+ */
+spec_status_t spec_verify(const void* target_logits, const void* draft_logits, spec_dtype_t dtype,
+                          const int32_t* draft_tokens, const float* temperature, const int32_t* top_k,
+                          const float* top_p, int32_t B, int32_t k, int32_t V, uint64_t seed, uint64_t offset,
+                          int32_t* tokens, int32_t* accept_len, float* logprobs, float* alpha, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * Plain (non-speculative) sampler: one token per logit row from the same sampler distribution
+ * (temperature, top-k, top-p as above) by Gumbel-max on the plain-sampler stream.  This is the step
+ * either side of verify: it draws the draft tokens from q, and it is what "sampler-equivalent" refers
+ * to (AReno pull request above, section "How was it tested?": sampler equivalence with and without
+ * top-k/top-p).
+ *
+ *   logits        [R, V] row-major, contiguous, dtype; 16-byte aligned
+ *   temperature   float [R]; top_k int32 [R]; top_p float [R] (meaning as in spec_verify)
+ *   row_b, row_pos  int32 [R] stream coordinates (b, i) of each row; NULL = (row index, 0)
+ *   R, V          1 <= R <= 2^20, 8 <= V <= 2^20 (V % 8 == 0 for bf16, V % 4 == 0 for fp32)
+ *   tokens        out int32 [R]   the drawn token (-1 for a row with unusable inputs)
+ *   logprobs      out float [R]   ln of its sampler probability (0 for greedy rows, NaN if unusable)
+ *   workspace     at least spec_sample_workspace_size(R, V, dtype) bytes, same rules as spec_verify
+ */
+size_t spec_sample_workspace_size(int32_t R, int32_t V, spec_dtype_t dtype);
+
+spec_status_t spec_sample(const void* logits, spec_dtype_t dtype, const float* temperature, const int32_t* top_k,
+                          const float* top_p, const int32_t* row_b, const int32_t* row_pos, int32_t R, int32_t V,
+                          uint64_t seed, uint64_t offset, int32_t* tokens, float* logprobs, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* A static, human-readable name of a status code. */
+const char* spec_verify_status_string(spec_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

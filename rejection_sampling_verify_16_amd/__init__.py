@@ -1,1 +1,140 @@
-"""MI355X-native speculative-decoding verify sampler (libspecverify) and its inputs."""
+"""MI355X-native speculative-decoding verify sampler: Python binding of libspecverify.
+
+The binding only marshals arguments: torch tensors (device memory and streams) are turned
+into raw pointers and passed to the C ABI declared in ``include/specverify.h``.  Every step
+of the verify method runs in the library's HIP kernels.  If the library has not been built
+the calls raise; there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libspecverify.so")
+
+SPEC_DTYPE_BF16 = 0
+SPEC_DTYPE_F32 = 1
+STATUS = {0: "SPEC_OK", 1: "SPEC_ERR_INVALID_ARGUMENT", 2: "SPEC_ERR_WORKSPACE",
+          3: "SPEC_ERR_UNSUPPORTED_DEVICE", 4: "SPEC_ERR_LAUNCH"}
+
+_lib = None
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status: int, what: str = "spec_verify"):
+        super().__init__(f"{what} failed: {STATUS.get(status, status)}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, U64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t
+        L.spec_verify_workspace_size.argtypes = [I32, I32, I32, ctypes.c_int]
+        L.spec_verify_workspace_size.restype = SZ
+        L.spec_verify.argtypes = [P, P, ctypes.c_int, P, P, P, P, I32, I32, I32, U64, U64, P, P, P, P, P, SZ, P]
+        L.spec_verify.restype = ctypes.c_int
+        L.spec_sample_workspace_size.argtypes = [I32, I32, ctypes.c_int]
+        L.spec_sample_workspace_size.restype = SZ
+        L.spec_sample.argtypes = [P, ctypes.c_int, P, P, P, P, P, I32, I32, U64, U64, P, P, P, SZ, P]
+        L.spec_sample.restype = ctypes.c_int
+        L.spec_verify_status_string.argtypes = [ctypes.c_int]
+        L.spec_verify_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return SPEC_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return SPEC_DTYPE_F32
+    raise TypeError("logits must be torch.bfloat16 or torch.float32")
+
+
+def workspace_size(B: int, k: int, V: int, dtype: int = SPEC_DTYPE_BF16) -> int:
+    return int(lib().spec_verify_workspace_size(B, k, V, dtype))
+
+
+def make_workspace(B: int, k: int, V: int, dtype: int = SPEC_DTYPE_BF16, device="cuda"):
+    """A zero-filled device workspace for spec_verify (reusable across calls on one stream)."""
+    import torch
+    n = workspace_size(B, k, V, dtype)
+    if n == 0:
+        raise ValueError("invalid sizes for spec_verify")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def alloc_outputs(B: int, k: int, device="cuda"):
+    import torch
+    return dict(tokens=torch.empty((B, k + 1), dtype=torch.int32, device=device),
+                accept_len=torch.empty((B,), dtype=torch.int32, device=device),
+                logprobs=torch.empty((B, k + 1), dtype=torch.float32, device=device),
+                alpha=torch.empty((B, k), dtype=torch.float32, device=device))
+
+
+def spec_verify(target_logits, draft_logits, draft_tokens, temperature, top_k, top_p, seed: int = 0,
+                offset: int = 0, out=None, workspace=None, stream=None):
+    """Run the verify step on device tensors; returns a dict of output tensors.
+
+    target_logits [B, k+1, V] and draft_logits [B, k, V] (bf16 or fp32, contiguous, same device),
+    draft_tokens int32 [B, k], temperature float32 [B], top_k int32 [B], top_p float32 [B].
+    ``out`` (from alloc_outputs) and ``workspace`` (from make_workspace) may be passed in to
+    avoid allocations; ``stream`` defaults to torch's current stream.
+    """
+    import torch
+    B, k1, V = target_logits.shape
+    k = k1 - 1
+    dt = _dtype_code(target_logits)
+    for t in (target_logits, draft_logits, draft_tokens, temperature, top_k, top_p):
+        if not t.is_contiguous():
+            raise ValueError("all inputs must be contiguous")
+    if out is None:
+        out = alloc_outputs(B, k, target_logits.device)
+    if workspace is None:
+        workspace = make_workspace(B, k, V, dt, target_logits.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(target_logits.device)
+    st = lib().spec_verify(target_logits.data_ptr(), draft_logits.data_ptr(), dt, draft_tokens.data_ptr(),
+                           temperature.data_ptr(), top_k.data_ptr(), top_p.data_ptr(), B, k, V, int(seed),
+                           int(offset), out["tokens"].data_ptr(), out["accept_len"].data_ptr(),
+                           out["logprobs"].data_ptr(), out["alpha"].data_ptr(), workspace.data_ptr(),
+                           workspace.numel(), ctypes.c_void_p(stream.cuda_stream))
+    if st != 0:
+        raise SpecVerifyError(st)
+    return out
+
+
+def spec_sample(logits, temperature, top_k, top_p, row_b=None, row_pos=None, seed: int = 0, offset: int = 0,
+                out=None, workspace=None, stream=None):
+    """Plain sampler on device tensors: one token per row of ``logits`` [R, V].
+
+    Returns (tokens int32 [R], logprobs float32 [R]).  ``row_b``/``row_pos`` (int32 [R]) are the
+    stream coordinates of each row (default: row index, 0)."""
+    import torch
+    R, V = logits.shape
+    dt = _dtype_code(logits)
+    if out is None:
+        out = (torch.empty(R, dtype=torch.int32, device=logits.device),
+               torch.empty(R, dtype=torch.float32, device=logits.device))
+    if workspace is None:
+        n = int(lib().spec_sample_workspace_size(R, V, dt))
+        if n == 0:
+            raise ValueError("invalid sizes for spec_sample")
+        workspace = torch.zeros(n, dtype=torch.uint8, device=logits.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(logits.device)
+    st = lib().spec_sample(logits.data_ptr(), dt, temperature.data_ptr(), top_k.data_ptr(), top_p.data_ptr(),
+                           row_b.data_ptr() if row_b is not None else None,
+                           row_pos.data_ptr() if row_pos is not None else None, R, V, int(seed), int(offset),
+                           out[0].data_ptr(), out[1].data_ptr(), workspace.data_ptr(), workspace.numel(),
+                           ctypes.c_void_p(stream.cuda_stream))
+    if st != 0:
+        raise SpecVerifyError(st, "spec_sample")
+    return out

@@ -1,0 +1,139 @@
+// sv_common.h -- device helpers of libspecverify (gfx950): element access, keys, Philox, reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int NT = 256;          // threads per workgroup (4 wave64s)
+constexpr int NWAVE = NT / 64;
+constexpr int MAXK = 8;          // largest number of drafts per batch row
+constexpr int MAXROWS = 2 * MAXK + 1;
+
+// ---------------------------------------------------------------------------------------------
+// Element types.  A 16-byte vector holds 8 bf16 or 4 fp32 logits.
+// ---------------------------------------------------------------------------------------------
+struct BF16 {
+  static constexpr int EPV = 8;       // elements per 16-byte vector
+  static constexpr int KEYBITS = 16;  // bits of the order-preserving key
+  __device__ static inline float get(const uint4& v, int e) {
+    const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
+    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+  __device__ static inline float load1(const void* row, int x) {
+    return __uint_as_float((uint32_t)((const uint16_t*)row)[x] << 16);
+  }
+};
+
+struct F32 {
+  static constexpr int EPV = 4;
+  static constexpr int KEYBITS = 32;
+  __device__ static inline float get(const uint4& v, int e) {
+    return __uint_as_float(e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w);
+  }
+  __device__ static inline float load1(const void* row, int x) { return ((const float*)row)[x]; }
+};
+
+// Order-preserving unsigned key of a float (-0 canonicalised to +0); bf16 values use the top 16 bits.
+__device__ inline uint32_t key32(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+template <class E>
+__device__ inline uint32_t key_of(float f) {
+  return E::KEYBITS == 16 ? (key32(f) >> 16) : key32(f);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11).  The multiplies map to v_mad_u64_u32.
+// ---------------------------------------------------------------------------------------------
+__device__ inline uint4 philox10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c.y ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c.w ^ k1;
+    c.y = (uint32_t)p1;
+    c.w = (uint32_t)p0;
+    c.x = n0;
+    c.z = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+__device__ inline float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Accept uniform: top 24 bits, exact in fp32.
+__device__ inline float u24(uint32_t w) { return (float)(w >> 8) * 0x1p-24f; }
+
+// Exponential variate of the Gumbel draw, in base-2 units: E2 = -log2(U), U = ((w>>9)+0.5) 2^-23.
+// The Gumbel key ln w + G equals ln(w / E) with E = -ln U; E2 = E / ln 2 only rescales every key
+// by the same factor, so argmax_x w(x) / E2(x) is the Gumbel-max draw.
+__device__ inline float exp_race_E2(uint32_t w) {
+  const float U = ((float)(w >> 9) + 0.5f) * 0x1p-23f;
+  return -__builtin_amdgcn_logf(U);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Wave / workgroup reductions (fixed order: deterministic).
+// ---------------------------------------------------------------------------------------------
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ inline uint32_t wave_or(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, 64);
+  return v;
+}
+
+// (max, lowest argmax) of a value; idx = INT32_MAX means "none".
+__device__ inline void maxarg_combine(float& m, int& a, float m2, int a2) {
+  if (m2 > m || (m2 == m && a2 < a)) {
+    m = m2;
+    a = a2;
+  }
+}
+__device__ inline void wave_maxarg(float& m, int& a) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, 64);
+    const int a2 = __shfl_xor(a, o, 64);
+    maxarg_combine(m, a, m2, a2);
+  }
+}
+
+// Combine two (max, sum of exp2((l - max) c)) pairs.
+__device__ inline void lse_combine(float& m, float& s, float m2, float s2, float c) {
+  if (m2 > m) {
+    s = s2 + (m == -INFINITY ? 0.0f : s * fexp2((m - m2) * c));
+    m = m2;
+  } else if (m2 != -INFINITY) {
+    s = s + s2 * fexp2((m2 - m) * c);
+  }
+}
+
+// Inclusive scan over the workgroup in thread order (NT threads), 32-bit and 64-bit.
+template <class T>
+__device__ inline T block_inclusive_scan(T v, T* lds_tmp /* >= NWAVE */) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const T n = __shfl_up(v, o, 64);
+    if (lane >= o) v += n;
+  }
+  if (lane == 63) lds_tmp[wave] = v;
+  __syncthreads();
+  T add = 0;
+  for (int w = 0; w < wave; ++w) add += lds_tmp[w];
+  __syncthreads();
+  return v + add;
+}
+
+}  // namespace sv

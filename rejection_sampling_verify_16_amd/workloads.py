@@ -151,6 +151,7 @@ def make(B: int, k: int, V: int, *, dtype: str = "bf16", seed: int = 1000, targe
         n_d = math.ceil(tie_fraction * B * k)
         t_rows = rng.choice(B * (k + 1), size=n_t, replace=False)
         d_rows = rng.choice(B * k, size=n_d, replace=False)
+        with_draft = 0
         for c, r in enumerate(t_rows):
             b, i = divmod(int(r), k + 1)
             res = _inject_tie(tgt[b, i], rng, above=(c % 2 == 1))
@@ -158,10 +159,12 @@ def make(B: int, k: int, V: int, *, dtype: str = "bf16", seed: int = 1000, targe
                 continue
             w.tie_rows_target.append((b, i))
             a, j = res
-            # half of the tied target rows get the higher-index tied token as their draft:
-            # the lowest index is the argmax, so that draft must be rejected.
-            if i < k and (c // 2) % 2 == 0:
-                w.draft_overrides.append((b, i, max(a, j)))
+            # half of the tied target rows that have a draft get the higher-index tied token as
+            # their draft: the lowest index is the argmax, so that draft must be rejected.
+            if i < k:
+                if with_draft % 2 == 0:
+                    w.draft_overrides.append((b, i, max(a, j)))
+                with_draft += 1
         for c, r in enumerate(d_rows):
             b, i = divmod(int(r), k)
             if _inject_tie(drf[b, i], rng, above=(c % 2 == 1)) is not None:
