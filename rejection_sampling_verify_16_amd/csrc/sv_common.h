@@ -119,6 +119,24 @@ __device__ inline void lse_combine(float& m, float& s, float m2, float s2, float
   }
 }
 
+// Inclusive scan over the 64 lanes of a wave (lane order).
+template <class T>
+__device__ inline T wave_incl_scan(T v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const T n = __shfl_up(v, o, 64);
+    if (lane >= o) v += n;
+  }
+  return v;
+}
+
+// Lowest lane whose predicate holds (64 if none).
+__device__ inline int first_lane(bool pred) {
+  const unsigned long long m = __ballot(pred);
+  return m ? __ffsll((long long)m) - 1 : 64;
+}
+
 // Inclusive scan over the workgroup in thread order (NT threads), 32-bit and 64-bit.
 template <class T>
 __device__ inline T block_inclusive_scan(T v, T* lds_tmp /* >= NWAVE */) {
