@@ -112,6 +112,23 @@ spec_status_t spec_sample(const void* logits, spec_dtype_t dtype, const float* t
 /* A static, human-readable name of a status code. */
 const char* spec_verify_status_string(spec_status_t status);
 
+/*
+ * Benchmark hook: per-kernel timing of later calls.  Each spec_verify / spec_sample call enqueues
+ * SPEC_NUM_KERNELS kernels: 0 = row statistics and kept thresholds (reads every logit once),
+ * 1 = accept chain, alpha and draws (re-reads the draft-position rows).
+ *
+ *   events  NULL (turns the hook off; count ignored) or 2 * SPEC_NUM_KERNELS hipEvent_t handles,
+ *           created by the caller with timing enabled and owned by the caller
+ *   count   2 * SPEC_NUM_KERNELS
+ * While set, every call records events[2j] on its stream just before launching kernel j and
+ * events[2j+1] just after it, so hipEventElapsedTime(events[2j], events[2j+1]) is kernel j's duration
+ * in the most recent call.  The setting is process-wide and not synchronised: set it from the thread
+ * that makes the calls, and turn it off (NULL) before the events are destroyed.
+ * Returns SPEC_ERR_INVALID_ARGUMENT if count is wrong.
+ */
+#define SPEC_NUM_KERNELS 2
+spec_status_t spec_set_kernel_events(void* const* events, int32_t count);
+
 #ifdef __cplusplus
 }
 #endif

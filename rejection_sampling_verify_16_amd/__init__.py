@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 
 SPEC_DTYPE_BF16 = 0
 SPEC_DTYPE_F32 = 1
+SPEC_NUM_KERNELS = 2  # kernels per call: 0 = row statistics / thresholds, 1 = accept chain / alpha / draws
 STATUS = {0: "SPEC_OK", 1: "SPEC_ERR_INVALID_ARGUMENT", 2: "SPEC_ERR_WORKSPACE",
           3: "SPEC_ERR_UNSUPPORTED_DEVICE", 4: "SPEC_ERR_LAUNCH"}
 
@@ -45,6 +46,8 @@ def lib() -> ctypes.CDLL:
         L.spec_sample.restype = ctypes.c_int
         L.spec_verify_status_string.argtypes = [ctypes.c_int]
         L.spec_verify_status_string.restype = ctypes.c_char_p
+        L.spec_set_kernel_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), I32]
+        L.spec_set_kernel_events.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -138,3 +141,16 @@ def spec_sample(logits, temperature, top_k, top_p, row_b=None, row_pos=None, see
     if st != 0:
         raise SpecVerifyError(st, "spec_sample")
     return out
+
+
+def set_kernel_events(events):
+    """Benchmark hook: ``events`` is None (off) or 2 * SPEC_NUM_KERNELS raw hipEvent_t handles (ints).
+
+    While set, every later call records events[2j] / events[2j+1] around its j-th kernel on its stream."""
+    if events is None:
+        st = lib().spec_set_kernel_events(None, 0)
+    else:
+        arr = (ctypes.c_void_p * len(events))(*events)
+        st = lib().spec_set_kernel_events(arr, len(events))
+    if st != 0:
+        raise SpecVerifyError(st, "spec_set_kernel_events")

@@ -6,29 +6,32 @@
 // rejection sampling, unchanged logprobs), its accept-probability table (alpha = sum min(p, q)), and
 // its per-step optimisation table (Gumbel-max draws, no host synchronisation).
 //
-// One call enqueues three kernels on the caller's stream; no workgroup ever waits for another.  A
-// merge across workgroups is done by the last one to arrive at a per-row counter (agent-scope
-// atomics; partials travel through agent-scope atomic stores and loads, coherent across the XCDs'
-// L2s without cache-wide write-back or invalidation).
+// One call enqueues two kernels on the caller's stream; no workgroup ever waits for another.
+// A merge across workgroups is done by the last one to arrive at a per-row counter (agent-scope
+// atomics; partials travel through agent-scope atomic stores and loads, coherent across the XCDs' L2s
+// without cache-wide write-back or invalidation).  Workgroup ids map to (row, slice) so that all
+// slices of one row run on one XCD and consecutive rows' merges run on different XCDs.
 //
-//   K1 stats   grid (slices, logit rows).  Streams every logit once (16-byte loads): slice max,
-//              lowest argmax, sum of exp2((l - max) * log2(e) / T), NaN/+inf flags; for rows with
-//              top-k / top-p (bf16) also a count histogram of the 512 order-preserving codes below the
-//              slice max and a 128-bin histogram of log2 value (counts, and masses relative to each
-//              bin's top).  The last slice of a row merges: row max / argmax / normaliser, and the
-//              exact kept threshold when it lies among the row's top 512 codes (per-code counts merged
-//              exactly, masses = count x 2^40 fixed-point exp2 of the code's value: integer sums).
-//              Otherwise it picks, from the merged log2-value histogram, a window of codes that must
-//              hold the threshold.
-//   K3 fine    grid (slices, logit rows), only rows with a pending window: exact per-code counts in
-//              the window and the exact fixed-point mass above it; the last slice merges and sets the
-//              threshold.  Rows this cannot settle (fp32 keys, a window too wide, a threshold outside
-//              the window) take an exact whole-row MSD radix select instead.
-//   K5 verify  grid (slices, batch rows).  Every slice evaluates the accept chain (p_i(x_i), q_i(x_i)
-//              from the row statistics and two gathered logits, Philox accept uniforms), then re-reads
-//              its slice of the draft-position rows: alpha partial sums for every position and the
-//              Gumbel-max race candidate at the first rejected position (residual max(p - q, 0)) or at
-//              position k (bonus from p_k).  The last slice of a batch row writes the outputs.
+//   K1 stats   items (logit row, slice).  Streams every logit once with 16-byte loads and keeps only
+//              what the row needs: NaN-propagating max (lowest argmax for greedy rows); the sum of
+//              exp2((l - max) * log2(e) / T) for rows whose normaliser is the whole row; for bf16 rows
+//              with top-k / top-p, exact per-code counts of the 512 order-preserving codes below the
+//              slice max (keys of two logits at a time, packed 16-bit operations), and for top-p-only
+//              rows also counts in 1/8-log2-unit weight bins.  The last slice of a row merges (one round
+//              trip for all its partials): row max / argmax / normaliser and, for truncated rows, the
+//              kept threshold.  Among the row's top 512 codes the threshold is exact (merged per-code
+//              counts, masses = count x 2^40 fixed-point weight, integer sums).  Otherwise the weight
+//              bins bound the cumulative mass, which gives a code window that must hold the threshold;
+//              the merging workgroup counts that window exactly over the whole row.  Anything this
+//              cannot settle (fp32 keys, a window too wide, a failed self-check) takes an exact MSD
+//              radix select.
+//   K5 verify  items (batch row, slice).  Each evaluates the accept chain (p_i(x_i), q_i(x_i) from the
+//              row statistics and two gathered logits, Philox accept uniforms), then re-reads its slice
+//              of the draft-position rows (the next position's loads in flight while one is computed):
+//              alpha partial sums for every position and the Gumbel-max race candidate at the first
+//              rejected position (residual max(p - q, 0)) or at position k (bonus from p_k).  Logits
+//              below a row's kept threshold are skipped a wave at a time.  The last slice of a batch row
+//              writes the outputs.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -46,46 +49,47 @@ constexpr int MODE_VERIFY = 0;
 constexpr int MODE_SAMPLE = 1;  // plain sampler: k = 0, one logit row per batch row, stream tag 2
 constexpr int MAXDEV = 64;
 constexpr int VPT1 = 8;         // K1: 16-byte vectors per thread per slice
-constexpr int VPT3 = 8;         // K3
-constexpr int VPT5 = 4;         // K5
-constexpr int WTOP = 512;       // K1: per-code window below the slice max
-constexpr int NB = 128;         // K1: log2-value bins (2 per log2 unit)
-constexpr float BR = 2.0f;      // bins per log2 unit
-constexpr int WF = 2048;        // K3: widest per-code window
+constexpr int VPT5 = 2;         // K5
+constexpr int OCC1 = 8;         // K1 workgroups per CU (register budget of its launch bounds)
+constexpr int OCC5 = 4;         // K5 workgroups per CU
+constexpr int FVPT = 2;         // whole-row passes of one workgroup: vectors per thread per step
+constexpr int WTOP = 512;       // K1: exact per-code window below the slice max
+constexpr int NBC = 256;        // K1: weight bins of top-p-only rows
+constexpr float BRC = 8.0f;     // weight bins per log2 unit
+constexpr int WF = 2048;        // widest exact code window of the whole-row pass
+constexpr int MAXS1 = 64;       // slices per bf16 row at the largest V
+constexpr int MB = 8;           // merge: slices whose histogram words are loaded in one round trip
+constexpr int HCW = NBC / 2 + 1;  // words per slice of packed bin counts + the slice's base bin
+constexpr int NKERN = 2;        // kernels per call
 
-// RowInfo.state bits
-constexpr uint32_t ST_BAD = 1u;      // NaN / +inf entries, or every entry -inf
-constexpr uint32_t ST_FINE = 2u;     // threshold pending: fine pass over [clo, chi]
-constexpr uint32_t ST_RADIX = 4u;    // threshold pending: whole-row radix select
+constexpr uint32_t ST_BAD = 1u;  // NaN / +inf entries, or every entry -inf
 
 struct StatPart {  // K1, per (logit row, slice)
-  float m;         // slice max
-  int32_t arg;     // lowest index of the slice max (INT_MAX if none)
-  float s;         // sum of exp2((l - m) * c) over the slice
+  float m;         // slice max (NaN if the slice holds a NaN, for non-greedy rows)
+  int32_t arg;     // lowest index of the slice max (greedy rows; INT_MAX otherwise)
+  float s;         // sum of exp2((l - m) c) over the slice (rows that need the whole-row normaliser)
   uint32_t flags;  // bit 0: NaN or +inf seen
+  float g;         // the row's logit at its draft token, if the token falls in this slice
+  uint32_t pad[3];
 };
 
 struct RowInfo {    // per logit row
   float m;          // row max
-  int32_t arg;      // lowest argmax
-  float Z;          // normaliser of the kept set: sum of exp2((l - m) * c) over kept entries
-  uint32_t thr;     // smallest kept order-preserving key (0: everything kept)
-  uint32_t state;   // ST_* bits
-  uint32_t clo, chi;  // K3 window of keys [clo, chi]
-  float Ztot;       // normaliser of the whole row
-};
-
-struct FinePart {  // K3, per (logit row, slice): count and fixed-point mass of the entries above chi
-  unsigned long long above_mass;
-  uint32_t above_cnt;
-  uint32_t pad;
+  int32_t arg;      // lowest argmax (greedy rows)
+  float Z;          // normaliser of the kept set: sum of exp2((l - m) c) over kept entries
+  float lz;         // log2(Z)
+  float fthr;       // smallest kept value (-inf: every entry kept)
+  uint32_t state;   // ST_BAD
+  float Ztot;       // whole-row normaliser (rows that needed it)
+  float gath;       // logit at the draft token of this position (draft-position rows of a valid token)
 };
 
 struct FinalPart {  // K5, per (batch row, slice)
   float alpha[MAXK];
   float key;        // best Gumbel race key w / E2 (0 = no candidate)
   int32_t idx;      // its vocabulary index (INT_MAX = none)
-  uint32_t pad[2];
+  float val;        // its logit
+  uint32_t pad;
 };
 
 struct Params {
@@ -96,7 +100,7 @@ struct Params {
   const int32_t* top_k;
   const float* top_p;
   int32_t B, k, V, rows, R;  // rows = 2k + 1 logit rows per batch row, R = B * rows
-  int32_t S1, S3, S5, L1, L3, L5;
+  int32_t S1, S5, L1, L5;
   int32_t mode;              // MODE_VERIFY or MODE_SAMPLE
   const int32_t* row_b;      // plain sampler: stream coordinate b of each row (NULL = row index)
   const int32_t* row_pos;    // plain sampler: stream coordinate i of each row (NULL = 0)
@@ -106,29 +110,34 @@ struct Params {
   float* logprobs;
   float* alpha;
   uint32_t* cnt1;     // [R] K1 arrivals
-  uint32_t* cnt3;     // [R] K3 arrivals
   uint32_t* cnt5;     // [B] K5 arrivals
   StatPart* st1;      // [R][S1]
   uint32_t* hw1;      // [R][S1][WTOP/2] packed 16-bit code counts
-  uint32_t* hb1;      // [R][S1][NB/2 + NB + 1] packed 16-bit bin counts, bin masses, slice base bin
+  uint32_t* hc1;      // [R][S1][HCW] packed 16-bit bin counts, then the slice's base bin (float)
   RowInfo* rinfo;     // [R]
-  FinePart* fp3;      // [R][S3]
-  uint32_t* fc3;      // [R][S3][WF/2] packed 16-bit code counts
   FinalPart* fin5;    // [B][S5]
-  unsigned long long* trace;  // K1 phase timestamps per (row, slice), instrumented builds only
+  unsigned long long* trace;   // K1 phase timestamps per item: instrumented builds only
+  unsigned long long* trace5;  // K5 phase timestamps per item: instrumented builds only
 };
 
 // Phase timestamps of instrumented builds (compiled with -DSV_TRACE); no-ops otherwise.
 #ifdef SV_TRACE
 constexpr int TRACE_SLOTS = 8;
-#define SV_TRACE_AT(idx, slot)                                                   \
-  do {                                                                           \
-    if (threadIdx.x == 0 && p.trace) p.trace[(size_t)(idx)*TRACE_SLOTS + (slot)] = wall_clock64(); \
+#define SV_TRACE_AT(p, item, slot)                                                                  \
+  do {                                                                                             \
+    if (threadIdx.x == 0 && (p).trace) (p).trace[(size_t)(item)*TRACE_SLOTS + (slot)] = wall_clock64(); \
+  } while (0)
+#define SV_TRACE5_AT(p, item, slot)                                                                 \
+  do {                                                                                             \
+    if (threadIdx.x == 0 && (p).trace5) (p).trace5[(size_t)(item)*TRACE_SLOTS + (slot)] = wall_clock64(); \
   } while (0)
 #else
 constexpr int TRACE_SLOTS = 0;
-#define SV_TRACE_AT(idx, slot) \
-  do {                         \
+#define SV_TRACE_AT(p, item, slot) \
+  do {                             \
+  } while (0)
+#define SV_TRACE5_AT(p, item, slot) \
+  do {                              \
   } while (0)
 #endif
 
@@ -139,29 +148,32 @@ __device__ inline const uint8_t* row_ptr(const Params& p, int b, int r, int esiz
   return p.draft + ((size_t)b * p.k + (r - p.k - 1)) * V * esize;
 }
 
-__device__ inline unsigned long long fixmass(float e) {  // e in [0, 1] -> 2^40 fixed point
-  return __float2ull_rn(e * 0x1p40f);
+// Work item g -> (row r, slice s) for R rows of S slices.  Rows go in groups of 8, slice-major within
+// a group: with a grid that is a multiple of 8 (workgroups are dealt to the 8 XCDs round robin) every
+// slice of row 8q + x runs on XCD x.  Rows past the last full group map row-major.
+__device__ inline void item_rs(int g, int R, int S, int& r, int& s) {
+  const int full = (R & ~7) * S;
+  if (g < full) {
+    const int grp = g / (8 * S), rem = g - grp * 8 * S;
+    s = rem >> 3;
+    r = grp * 8 + (rem & 7);
+  } else {
+    const int h = g - full, q = h / S;
+    r = (R & ~7) + q;
+    s = h - q * S;
+  }
 }
 
-// bf16 value of a 16-bit order-preserving key (inverse of key32(f) >> 16)
-__device__ inline float key16_value(uint32_t k16) {
-  const uint32_t k32 = k16 << 16;
-  const uint32_t u = (k32 & 0x80000000u) ? (k32 & 0x7fffffffu) : ~k32;
-  return __uint_as_float(u & 0xffff0000u);
+__device__ inline unsigned long long fixmass(float e) {  // e in [0, 1] -> 2^40 fixed point
+  return __float2ull_rn(e * 0x1p40f);
 }
 
 __device__ inline void st32(void* p, uint32_t v) {
   __hip_atomic_store((uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ inline void st64(void* p, unsigned long long v) {
-  __hip_atomic_store((unsigned long long*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ inline void stf(void* p, float v) { st32(p, __float_as_uint(v)); }
 __device__ inline uint32_t ld32(const void* p) {
   return __hip_atomic_load((const uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline unsigned long long ld64(const void* p) {
-  return __hip_atomic_load((const unsigned long long*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ inline float ldf(const void* p) { return __uint_as_float(ld32(p)); }
 // Wait until this thread's outstanding memory operations (stores and atomics included) are done.
@@ -184,7 +196,7 @@ __device__ inline bool arrive_last(uint32_t* counter, uint32_t total, int* flag)
 struct RowParams {
   float T, P, c;
   int K;
-  bool ok, greedy, trunc;
+  bool ok, greedy, trunc, useK, useP;
 };
 __device__ inline RowParams row_params(const Params& p, int b) {
   RowParams q;
@@ -195,7 +207,9 @@ __device__ inline RowParams row_params(const Params& p, int b) {
          !(__builtin_isnan(q.P) || q.P <= 0.0f);
   q.greedy = q.T == 0.0f;
   q.c = q.greedy ? 0.0f : 1.4426950408889634f / q.T;
-  q.trunc = q.ok && !q.greedy && ((q.K > 0 && q.K < p.V) || q.P < 1.0f);
+  q.useK = q.ok && !q.greedy && q.K > 0 && q.K < p.V;
+  q.useP = q.ok && !q.greedy && q.P < 1.0f;
+  q.trunc = q.useK || q.useP;
   return q;
 }
 
@@ -221,6 +235,7 @@ struct RedSmem {
   uint32_t u[NWAVE];
   unsigned long long scan64[NWAVE];
   uint32_t scan32[NWAVE];
+  double scand[NWAVE];
   int32_t flag;
 };
 
@@ -249,14 +264,15 @@ __device__ void block_stats(RedSmem& rs, float& m, int& a, float& s, uint32_t& f
   __syncthreads();
 }
 
-__device__ float block_max(RedSmem& rs, float m) {
+// Workgroup NaN-propagating max into every thread.
+__device__ float block_nan_max(RedSmem& rs, float m) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  for (int o = 32; o > 0; o >>= 1) m = nan_max(m, __shfl_xor(m, o, 64));
   if (lane == 0) rs.f[wave] = m;
   __syncthreads();
   m = rs.f[0];
-  for (int w = 1; w < NWAVE; ++w) m = fmaxf(m, rs.f[w]);
+  for (int w = 1; w < NWAVE; ++w) m = nan_max(m, rs.f[w]);
   __syncthreads();
   return m;
 }
@@ -275,6 +291,18 @@ __device__ void block_maxarg(RedSmem& rs, float& m, int& a) {
   __syncthreads();
 }
 
+// Lowest thread index whose predicate holds, into every thread (NT if none).
+__device__ int block_first(RedSmem& rs, bool pred) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int fl = first_lane(pred);
+  if (lane == 0) rs.i[wave] = fl < 64 ? wave * 64 + fl : NT;
+  __syncthreads();
+  int r = NT;
+  for (int w = 0; w < NWAVE; ++w) r = min(r, rs.i[w]);
+  __syncthreads();
+  return r;
+}
+
 // ---------------------------------------------------------------------------------------------
 // Exact kept threshold of one whole row (top-k, then top-p on the top-k mass), by one workgroup.
 // MSD radix select over order-preserving keys, 8-bit digits; per-digit LDS histograms of counts
@@ -286,6 +314,38 @@ struct RadixSmem {
   uint32_t sel, sel_excl;
   unsigned long long sel_mexcl, sel_m;
 };
+
+// One digit histogram of the entries whose key is >= thr and matches `prefix` above the digit.
+template <class E, bool COUNTS>
+__device__ void radix_hist(RadixSmem& sm, const uint4* src, int nvec, int lev, uint32_t prefix, uint32_t thr,
+                           float m, float c) {
+  const int tid = threadIdx.x;
+  const int shift = E::KEYBITS - 8 * (lev + 1);
+  for (int j0 = 0; j0 < nvec; j0 += NT * FVPT) {
+    uint4 v[FVPT];
+#pragma unroll
+    for (int u = 0; u < FVPT; ++u) {
+      const int j = j0 + tid + u * NT;
+      if (j < nvec) v[u] = src[j];
+    }
+#pragma unroll
+    for (int u = 0; u < FVPT; ++u) {
+      const int j = j0 + tid + u * NT;
+      if (j < nvec) {
+#pragma unroll
+        for (int e = 0; e < E::EPV; ++e) {
+          const float f = E::get(v[u], e);
+          const uint32_t key = key_of<E>(f);
+          if (key >= thr && (lev == 0 || (key >> (shift + 8)) == prefix)) {
+            const uint32_t d = (key >> shift) & 255u;
+            if (COUNTS) atomicAdd(&sm.hcnt[d], 1u);
+            atomicAdd(&sm.hmass[d], fixmass(fexp2((f - m) * c)));
+          }
+        }
+      }
+    }
+  }
+}
 
 template <class E>
 __device__ void row_cutoff(RadixSmem& sm, RedSmem& rs, const uint8_t* row, int V, float m, float c, int K, float P,
@@ -302,23 +362,10 @@ __device__ void row_cutoff(RadixSmem& sm, RedSmem& rs, const uint8_t* row, int V
     uint32_t prefix = 0, need = (uint32_t)K;
     unsigned long long mabove = 0;
     for (int lev = 0; lev < LEVELS; ++lev) {
-      const int shift = E::KEYBITS - 8 * (lev + 1);
       sm.hcnt[tid] = 0;
       sm.hmass[tid] = 0;
       __syncthreads();
-      for (int j = tid; j < nvec; j += NT) {
-        const uint4 v = src[j];
-#pragma unroll
-        for (int e = 0; e < E::EPV; ++e) {
-          const float f = E::get(v, e);
-          const uint32_t key = key_of<E>(f);
-          if (lev == 0 || (key >> (shift + 8)) == prefix) {
-            const uint32_t d = (key >> shift) & 255u;
-            atomicAdd(&sm.hcnt[d], 1u);
-            atomicAdd(&sm.hmass[d], fixmass(fexp2((f - m) * c)));
-          }
-        }
-      }
+      radix_hist<E, true>(sm, src, nvec, lev, prefix, 0u, m, c);
       __syncthreads();
       const int d = 255 - tid;  // thread t scans bins in descending key order
       const uint32_t cnt = sm.hcnt[d];
@@ -348,19 +395,9 @@ __device__ void row_cutoff(RadixSmem& sm, RedSmem& rs, const uint8_t* row, int V
     unsigned long long mabove = 0;
     double target = 0.0;
     for (int lev = 0; lev < LEVELS; ++lev) {
-      const int shift = E::KEYBITS - 8 * (lev + 1);
       sm.hmass[tid] = 0;
       __syncthreads();
-      for (int j = tid; j < nvec; j += NT) {
-        const uint4 v = src[j];
-#pragma unroll
-        for (int e = 0; e < E::EPV; ++e) {
-          const float f = E::get(v, e);
-          const uint32_t key = key_of<E>(f);
-          if (key >= thr && (lev == 0 || (key >> (shift + 8)) == prefix))
-            atomicAdd(&sm.hmass[(key >> shift) & 255u], fixmass(fexp2((f - m) * c)));
-        }
-      }
+      radix_hist<E, false>(sm, src, nvec, lev, prefix, thr, m, c);
       __syncthreads();
       const int d = 255 - tid;
       const unsigned long long ms = sm.hmass[d];
@@ -393,23 +430,25 @@ __device__ void row_cutoff(RadixSmem& sm, RedSmem& rs, const uint8_t* row, int V
 }
 
 // ---------------------------------------------------------------------------------------------
-// Threshold search over a descending run of per-code (count, mass) entries, 2 per thread:
-// the first entry where the running count reaches K (top-k) and, within the kept prefix, the first
-// where the running mass reaches P * Z_K (top-p).  Entries are indexed 0..n-1 from the top.
+// Threshold search over a descending run of bf16 codes: cnt[i] (LDS) counts code ktop - i, whose mass
+// is cnt x 2^40-fixed-point exp2((value - m) c).  Finds the first entry where the running count reaches
+// K (top-k) and, within the kept prefix, the first where the running mass reaches P * Z_K (top-p).
+// base_cnt / base_mass are the totals above entry 0; ztot_fixed is the whole row's mass (used when
+// top-k is off).  Returns false if a threshold lies outside the run: the caller then looks elsewhere.
 // ---------------------------------------------------------------------------------------------
 struct SelState {
   int32_t sel_k, sel_p;
   unsigned long long zk, zp;
 };
 
-// cnt/mass[0..n) hold the entries (LDS); base_cnt / base_mass are the totals above entry 0; ztot_fixed is
-// the whole row's mass (used when top-k is off).  Returns false if a threshold lies beyond the run.
-__device__ bool select_run(const uint32_t* cnt, const unsigned long long* mass, SelState& ss, RedSmem& rs, int n,
-                           uint32_t base_cnt, unsigned long long base_mass, double ztot_fixed, int K, float P, int V,
-                           int& sel, unsigned long long& zsel) {
+__device__ inline unsigned long long code_mass(uint32_t cnt, uint32_t code, float m, float c) {
+  return cnt ? (unsigned long long)cnt * fixmass(fexp2((key16_value(code) - m) * c)) : 0ull;
+}
+
+__device__ bool select_run(const uint32_t* cnt, int n, uint32_t ktop, float m, float c, SelState& ss, RedSmem& rs,
+                           uint32_t base_cnt, unsigned long long base_mass, double ztot_fixed, bool useK, int K,
+                           bool useP, float P, int& sel, unsigned long long& zsel) {
   const int tid = threadIdx.x;
-  const bool useK = K > 0 && K < V;
-  const bool useP = P < 1.0f;
   if (tid == 0) {
     ss.sel_k = -1;
     ss.sel_p = -1;
@@ -424,7 +463,7 @@ __device__ bool select_run(const uint32_t* cnt, const unsigned long long* mass, 
     for (int c0 = 0; c0 < n; c0 += 2 * NT) {
       const int i0 = c0 + 2 * tid, i1 = i0 + 1;
       const uint32_t a0 = i0 < n ? cnt[i0] : 0u, a1 = i1 < n ? cnt[i1] : 0u;
-      const unsigned long long b0 = i0 < n ? mass[i0] : 0ull, b1 = i1 < n ? mass[i1] : 0ull;
+      const unsigned long long b0 = code_mass(a0, ktop - i0, m, c), b1 = code_mass(a1, ktop - i1, m, c);
       const uint32_t ic = block_inclusive_scan<uint32_t>(a0 + a1, rs.scan32) + ccarry;
       const unsigned long long im = block_inclusive_scan<unsigned long long>(b0 + b1, rs.scan64) + mcarry;
       const uint32_t e0 = ic - a0 - a1;
@@ -459,7 +498,8 @@ __device__ bool select_run(const uint32_t* cnt, const unsigned long long* mass, 
     mcarry = base_mass;
     for (int c0 = 0; c0 <= last; c0 += 2 * NT) {
       const int i0 = c0 + 2 * tid, i1 = i0 + 1;
-      const unsigned long long b0 = i0 <= last ? mass[i0] : 0ull, b1 = i1 <= last ? mass[i1] : 0ull;
+      const uint32_t a0 = i0 <= last ? cnt[i0] : 0u, a1 = i1 <= last ? cnt[i1] : 0u;
+      const unsigned long long b0 = code_mass(a0, ktop - i0, m, c), b1 = code_mass(a1, ktop - i1, m, c);
       const unsigned long long im = block_inclusive_scan<unsigned long long>(b0 + b1, rs.scan64) + mcarry;
       const unsigned long long f0 = im - b0 - b1;
       if (i0 <= last && (double)f0 < target && (double)(f0 + b0) >= target) {
@@ -490,206 +530,290 @@ __device__ bool select_run(const uint32_t* cnt, const unsigned long long* mass, 
 // ---------------------------------------------------------------------------------------------
 struct K1Smem {
   RedSmem rs;
-  uint32_t hw[WTOP];   // per-code counts below the slice max
-  uint32_t hbc[NB];    // log2-value bin counts
-  float hbm[NB];       // bin masses relative to each bin's top
-  uint4 st[64];        // staged slice statistics (merge), chunks of 64 slices
-  uint32_t keyms[64];  // slice max keys (merge; bf16 rows have at most 64 slices)
-  uint32_t scnt[WTOP];
-  unsigned long long smass[WTOP];
   SelState ss;
-  float bm[NB];        // merged bin masses relative to the row max
-  uint32_t bc[NB];     // merged bin counts
   uint32_t win[4];
+  union {
+    struct {                    // streaming phase; entries past WTOP / NBC absorb out-of-range
+      uint32_t hw[WTOP + 64];   // logits, one per lane, so the atomics need no branch
+      uint32_t hc[NBC + 64];
+    } st;
+    struct {               // merge phase
+      uint32_t keyms[MAXS1];  // slice max keys
+      float cbs[MAXS1];       // slice base bins
+      uint32_t bc[NBC];       // merged weight-bin counts (row-relative)
+      uint32_t cnt[WF];       // merged per-code counts: the top codes, later the exact window
+    } mg;
+    RadixSmem rad;
+  } u;
 };
 
+// Code window [klo, khi] that must hold the top-p threshold of a top-p-only row, from the merged
+// weight-bin counts: bin j holds the entries with floor(-l c BRC) = A_m + j, A_m = floor(-m c BRC),
+// so its weights exp2((l - m) c) lie in (2^(hi_j - 1/BRC), 2^hi_j], hi_j = -(A_m + j)/BRC - m c.
+// With these bounds and Z (the row normaliser) the threshold bin lies between the first bin whose
+// upper-bound cumulative mass can reach P Z and the first whose lower-bound cumulative mass must.
+__device__ bool coarse_window(K1Smem& sm, float m, float c, float P, float Ztot, int V, uint32_t keym, uint32_t& klo,
+                              uint32_t& khi) {
+  const int tid = threadIdx.x;  // NT == NBC: thread t owns bin t
+  const float Am = floorf(-m * (c * BRC));
+  const double mc = (double)m * (double)c;
+  const double hi = -((double)Am + tid) / BRC - mc;
+  const double wmax = exp2(fmin(hi, 0.0)), wmin = exp2(hi - 1.0 / BRC);
+  const uint32_t n = sm.u.mg.bc[tid];
+  const uint32_t nin = block_inclusive_scan<uint32_t>(n, sm.rs.scan32);
+  const double U = block_inclusive_scan<double>((double)n * wmax, sm.rs.scand);
+  const double L = block_inclusive_scan<double>((double)n * wmin, sm.rs.scand);
+  if (tid == NT - 1) {
+    sm.rs.scand[0] = U;
+    sm.rs.u[0] = nin;
+  }
+  __syncthreads();
+  const double Utot = sm.rs.scand[0];
+  const uint32_t ntot = sm.rs.u[0];
+  __syncthreads();
+  const double wunder = exp2(fmin(-((double)Am + NBC) / BRC - mc, 0.0));
+  const double Ubelow = Utot - U + (double)((uint32_t)V - ntot) * wunder;
+  const double t = (double)P * (double)Ztot;
+  const double slack = 1e-4;
+  const int jlo = block_first(sm.rs, U >= t * (1.0 - slack));
+  const int jhi = block_first(sm.rs, fmax(L, (double)Ztot * (1.0 - slack) - Ubelow) >= t * (1.0 + slack));
+  if (jhi >= NBC || !(fabsf(Am) <= 0x1p22f)) return false;
+  // one bin of slack either side (bin edges are computed in fp32), then the codes of those values
+  const float vhi = -(Am + (float)(jlo - 1)) / (BRC * c);
+  const float vlo = -(Am + (float)(jhi + 2)) / (BRC * c);
+  const uint32_t kh = key32(vhi) >> 16, kl = key32(vlo) >> 16;  // within one code of key16 of those values
+  khi = min(kh + 2u, keym);
+  klo = kl > 2u ? kl - 2u : 0u;
+  return khi >= klo && khi - klo + 1u <= (uint32_t)WF;
+}
+
+// Exact per-code counts of [klo, khi] over the whole row by this workgroup (entry i counts code khi - i),
+// plus the exact count and fixed-point mass above khi; then the threshold search over the window.
+__device__ bool window_pass(K1Smem& sm, const uint8_t* row, int V, float m, float c, uint32_t klo, uint32_t khi,
+                            bool useK, int K, bool useP, float P, double ztot_fixed, uint32_t& thr, float& Z) {
+  const int tid = threadIdx.x;
+  const int width = (int)(khi - klo + 1);
+  uint32_t* h = sm.u.mg.cnt;
+  for (int j = tid; j < width; j += NT) h[j] = 0;
+  __syncthreads();
+  const uint4* src = (const uint4*)row;
+  const int nvec = V / BF16::EPV;
+  uint32_t acnt = 0;
+  unsigned long long amass = 0;
+  for (int j0 = 0; j0 < nvec; j0 += NT * FVPT) {
+    uint4 v[FVPT];
+#pragma unroll
+    for (int u = 0; u < FVPT; ++u) {
+      const int j = j0 + tid + u * NT;
+      if (j < nvec) v[u] = src[j];
+    }
+#pragma unroll
+    for (int u = 0; u < FVPT; ++u) {
+      const int j = j0 + tid + u * NT;
+      if (j < nvec) {
+#pragma unroll
+        for (int e = 0; e < BF16::EPV; ++e) {
+          const float f = BF16::get(v[u], e);
+          const uint32_t key = key16f(f);
+          if (key > khi) {
+            ++acnt;
+            amass += fixmass(fexp2((f - m) * c));
+          } else if (key >= klo) {
+            atomicAdd(&h[khi - key], 1u);  // descending: entry i is code khi - i
+          }
+        }
+      }
+    }
+  }
+  const uint32_t tc = block_inclusive_scan<uint32_t>(acnt, sm.rs.scan32);
+  const unsigned long long tm = block_inclusive_scan<unsigned long long>(amass, sm.rs.scan64);
+  if (tid == NT - 1) {
+    sm.win[0] = tc;
+    sm.rs.scan64[0] = tm;
+  }
+  __syncthreads();
+  const uint32_t above_c = sm.win[0];
+  const unsigned long long above_m = sm.rs.scan64[0];
+  __syncthreads();
+  int sel = -1;
+  unsigned long long zsel = 0;
+  if (!select_run(h, width, khi, m, c, sm.ss, sm.rs, above_c, above_m, ztot_fixed, useK, K, useP, P, sel, zsel))
+    return false;
+  thr = khi - (uint32_t)sel;
+  Z = (float)((double)zsel * 0x1p-40);
+  return true;
+}
+
+// Merge of one row by the last of its slices to arrive.  The slice statistics and, for histogram rows,
+// thread t's word of each slice's packed code counts are all loaded before any is used, so they cost
+// one round trip for up to MB slices; the weight-bin counts are loaded only when the top codes do not
+// hold the threshold.
 template <class E>
-__device__ void k1_merge(const Params& p, K1Smem& sm, int r, const RowParams& q) {
+__device__ void k1_merge(const Params& p, K1Smem& sm, int r, int b, int i, const RowParams& q) {
   constexpr bool BF = E::KEYBITS == 16;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int esize = 16 / E::EPV;
+  const int tid = threadIdx.x;
   const int S = p.S1;
-  RowInfo* ri = p.rinfo + r;
-  // row statistics: slice partials combined in slice order by wave 0
+  const bool hist = BF && q.trunc;
+  const bool coarse = hist && !q.useK;
   float m = -INFINITY, sum = 0.0f;
   int a = INT_MAX;
   uint32_t fl = 0;
-  for (int s0 = 0; s0 < S; s0 += 64) {
-    if (tid < 64 && s0 + tid < S) {
-      const StatPart* sp = p.st1 + (size_t)r * S + s0 + tid;
-      sm.st[tid] = make_uint4(ld32(&sp->m), ld32(&sp->arg), ld32(&sp->s), ld32(&sp->flags));
-      if (s0 == 0) sm.keyms[tid] = key32(__uint_as_float(sm.st[tid].x)) >> 16;
-    }
-    __syncthreads();
-    if (wave == 0 && s0 + lane < S) {
-      const uint4 v = sm.st[lane];
-      float mm = m, ss = sum;
-      lse_combine(mm, ss, __uint_as_float(v.x), __uint_as_float(v.z), q.c);
-      maxarg_combine(m, a, __uint_as_float(v.x), (int)v.y);
-      sum = ss;
-      fl |= v.w;
-    }
-    __syncthreads();
+  // slice holding this row's draft token (-1: none or out of range)
+  int sg = -1;
+  if (p.mode == MODE_VERIFY && i != p.k) {
+    const int xg = p.draft_tokens[(size_t)b * p.k + (i < p.k ? i : i - p.k - 1)];
+    if (xg >= 0 && xg < p.V) sg = xg / p.L1;
   }
-  if (wave == 0) wave_stats(m, a, sum, fl, q.c);
-  if (tid == 0) {
-    sm.rs.f[0] = m;
-    sm.rs.i[0] = a;
-    sm.rs.g[0] = sum;
-    sm.rs.u[0] = fl;
+  if (tid < S) {
+    const StatPart* sp = p.st1 + (size_t)r * S + tid;
+    m = ldf(&sp->m);
+    a = (int)ld32(&sp->arg);
+    sum = ldf(&sp->s);
+    fl = ld32(&sp->flags);
+    if (tid == sg) sm.win[1] = ld32(&sp->g);
   }
-  __syncthreads();
-  m = sm.rs.f[0];
-  a = sm.rs.i[0];
-  sum = sm.rs.g[0];
-  fl = sm.rs.u[0];
-  __syncthreads();
-  const bool bad = fl != 0 || m == -INFINITY;
-  uint32_t state = bad ? ST_BAD : 0u, thr = 0, clo = 0, chi = 0;
-  float Zk = sum;
-  if (!bad && q.trunc && !BF) state |= ST_RADIX;
-  if (!bad && q.trunc && BF) {
-    const uint32_t keym = key32(m) >> 16;
-    // merged per-code counts of the row's top WTOP codes (exact: every slice's window reaches them)
-    for (int co = tid; co < WTOP; co += NT) {
-      uint32_t cnt = 0;
-      for (int s = 0; s < S; ++s) {
-        const int d = co - (int)(keym - sm.keyms[s]);
-        if (d >= 0 && d < WTOP) {
-          const uint32_t w = ld32(&p.hw1[((size_t)r * S + s) * (WTOP / 2) + (d >> 1)]);
-          cnt += (d & 1) ? (w >> 16) : (w & 0xffffu);
-        }
-      }
-      sm.scnt[co] = cnt;
-      const float e = (cnt != 0 && (uint32_t)co <= keym) ? fexp2((key16_value(keym - (uint32_t)co) - m) * q.c) : 0.0f;
-      sm.smass[co] = (unsigned long long)cnt * fixmass(e);
-    }
-    __syncthreads();
-    int sel = -1;
-    unsigned long long zsel = 0;
+  uint32_t hwv[MB];
+  if (hist) {
+#pragma unroll
+    for (int t = 0; t < MB; ++t) hwv[t] = t < S ? ld32(&p.hw1[((size_t)r * S + t) * (WTOP / 2) + tid]) : 0u;
+    sm.u.mg.cnt[tid] = 0;
+    sm.u.mg.cnt[tid + NT] = 0;
+  }
+  if (coarse) {
+    if (tid < S) sm.u.mg.cbs[tid] = ldf(&p.hc1[((size_t)r * S + tid) * HCW + NBC / 2]);
+    sm.u.mg.bc[tid] = 0;
+  }
+  if (hist && tid < S) sm.u.mg.keyms[tid] = key16f(m);
+  block_stats(sm.rs, m, a, sum, fl, q.c);  // its barriers publish keyms / cbs and the cleared counts
+  const bool bad = fl != 0 || !(m > -INFINITY) || m == INFINITY;
+  uint32_t thr = 0;
+  float Z = sum;
+  if (!bad && q.trunc) {
+    bool done = false;
     const double ztot = (double)sum * 0x1p40;
-    if (select_run(sm.scnt, sm.smass, sm.ss, sm.rs, WTOP, 0u, 0ull, ztot, q.K, q.P, p.V, sel, zsel)) {
-      thr = keym - (uint32_t)sel;
-      Zk = (float)((double)zsel * 0x1p-40);
-    } else {
-      // The threshold lies below the top codes: merge the log2-value bins and pick a key window.
-      const float base_row = floorf(-m * q.c * BR);
-      for (int j = tid; j < NB; j += NT) {
-        sm.bc[j] = 0;
-        sm.bm[j] = 0.0f;
-      }
-      __syncthreads();
-      if (wave == 0) {
-        for (int s = 0; s < S; ++s) {
-          const uint32_t* hb = p.hb1 + ((size_t)r * S + s) * (NB / 2 + NB + 1);
-          const float base_s = ldf(&hb[NB / 2 + NB]);
-          for (int j = lane; j < NB; j += 64) {
-            const float jrf = base_s + (float)j - base_row;  // row-relative bin
-            if (jrf >= 0.0f && jrf < (float)NB) {
-              const int jr = (int)jrf;
-              const uint32_t w = ld32(&hb[j >> 1]);
-              const uint32_t cnt = (j & 1) ? (w >> 16) : (w & 0xffffu);
-              const float ms = ldf(&hb[NB / 2 + j]);
-              sm.bc[jr] += cnt;
-              // masses relative to the bin top 2^(-(base_s + j) / BR) -> relative to the row max
-              sm.bm[jr] += ms * fexp2(-(base_s + (float)j) / BR - m * q.c);
-            }
+    if (BF) {
+      const uint32_t keym = key16f(m);
+      // merged counts of the row's top WTOP codes: entry co is code keym - co.  Slice s's word tid holds
+      // its codes keyms[s] - 2 tid and keyms[s] - 2 tid - 1, i.e. entries off + 2 tid (+1) with
+      // off = keym - keyms[s] >= 0.
+      uint32_t* cnt = sm.u.mg.cnt;
+      for (int s0 = 0; s0 < S; s0 += MB) {
+        if (s0 > 0) {
+#pragma unroll
+          for (int t = 0; t < MB; ++t)
+            hwv[t] = s0 + t < S ? ld32(&p.hw1[((size_t)r * S + s0 + t) * (WTOP / 2) + tid]) : 0u;
+        }
+#pragma unroll
+        for (int t = 0; t < MB; ++t) {
+          const uint32_t w = hwv[t];
+          if (w != 0) {
+            const uint32_t co = (keym - sm.u.mg.keyms[s0 + t]) + 2u * tid;
+            if (co < (uint32_t)WTOP && (w & 0xffffu)) atomicAdd(&cnt[co], w & 0xffffu);
+            if (co + 1u < (uint32_t)WTOP && (w >> 16)) atomicAdd(&cnt[co + 1u], w >> 16);
           }
         }
       }
       __syncthreads();
-      if (tid == 0) {
-        const bool useK = q.K > 0 && q.K < p.V;
-        const bool useP = q.P < 1.0f;
-        int jk = NB - 1, jlo, jhi;
-        double zk_lo = 0.0, zk_hi = 0.0, ztot_est = 0.0;
-        for (int j = 0; j < NB; ++j) ztot_est += sm.bm[j];
-        if (useK) {
-          uint32_t cc = 0;
-          double mm = 0.0;
-          for (int j = 0; j < NB; ++j) {
-            if (cc + sm.bc[j] >= (uint32_t)q.K) {
-              jk = j;
-              zk_lo = mm;
-              zk_hi = mm + sm.bm[j];
-              break;
-            }
-            cc += sm.bc[j];
-            mm += sm.bm[j];
-          }
-        }
-        if (useP) {
-          const double tlo = (double)q.P * (useK ? zk_lo : ztot_est), thi = (double)q.P * (useK ? zk_hi : ztot_est);
-          double mm = 0.0;
-          int plo = NB - 1, phi = NB - 1;
-          bool got = false;
-          for (int j = 0; j < NB; ++j) {
-            mm += sm.bm[j];
-            if (!got && mm >= tlo * 0.999) {
-              plo = j;
-              got = true;
-            }
-            if (mm >= thi * 1.001 || j == NB - 1) {
-              phi = j;
-              break;
+      int sel = -1;
+      unsigned long long zsel = 0;
+      if (select_run(cnt, WTOP, keym, m, q.c, sm.ss, sm.rs, 0u, 0ull, ztot, q.useK, q.K, q.useP, q.P, sel, zsel)) {
+        thr = keym - (uint32_t)sel;
+        Z = (float)((double)zsel * 0x1p-40);
+        done = true;
+      } else if (coarse) {
+        // merged weight bins, row-relative: slice bin j is row bin cbs[s] + j - A_m
+        const float Am = floorf(-m * (q.c * BRC));
+        for (int s0 = 0; s0 < S; s0 += MB) {
+          uint32_t hcv[MB];
+#pragma unroll
+          for (int t = 0; t < MB; ++t)
+            hcv[t] = (s0 + t < S && tid < NBC / 2) ? ld32(&p.hc1[((size_t)r * S + s0 + t) * HCW + tid]) : 0u;
+#pragma unroll
+          for (int t = 0; t < MB; ++t) {
+            const uint32_t w = hcv[t];
+            if (w != 0) {
+              const float jr = sm.u.mg.cbs[s0 + t] + (float)(2 * tid) - Am;
+              if (jr >= 0.0f && jr < (float)NBC && (w & 0xffffu)) atomicAdd(&sm.u.mg.bc[(int)jr], w & 0xffffu);
+              if (jr + 1.0f >= 0.0f && jr + 1.0f < (float)NBC && (w >> 16))
+                atomicAdd(&sm.u.mg.bc[(int)jr + 1], w >> 16);
             }
           }
-          jlo = plo;
-          jhi = useK ? jk : phi;
-        } else {
-          jlo = jk;
-          jhi = jk;
         }
-        // widen by two bins either side against bin-edge rounding and the estimated masses
-        jlo = max(jlo - 2, 0);
-        jhi = min(jhi + 2, NB - 1);
-        // keys of the window: bins hold -l * c * BR in [base_row + j, base_row + j + 1)
-        const float vhi = -(base_row + (float)jlo) / (BR * q.c);
-        const float vlo = -(base_row + (float)(jhi + 1)) / (BR * q.c);
-        uint32_t khi = key32(vhi) >> 16, klo = key32(vlo) >> 16;
-        khi = min(khi + 2u, keym);
-        klo = klo > 2u ? klo - 2u : 0u;
-        if (jhi >= NB - 1 || khi < klo || khi - klo + 1 > (uint32_t)WF) {
-          sm.win[0] = ST_RADIX;
-        } else {
-          sm.win[0] = ST_FINE;
-          sm.win[1] = klo;
-          sm.win[2] = khi;
-        }
+        __syncthreads();
+        uint32_t klo = 0, khi = 0;
+        if (coarse_window(sm, m, q.c, q.P, sum, p.V, keym, klo, khi))
+          done = window_pass(sm, row_ptr(p, b, i, esize), p.V, m, q.c, klo, khi, q.useK, q.K, q.useP, q.P, ztot,
+                             thr, Z);
       }
+    }
+    if (!done) {
       __syncthreads();
-      state |= sm.win[0];
-      clo = sm.win[1];
-      chi = sm.win[2];
+      row_cutoff<E>(sm.u.rad, sm.rs, row_ptr(p, b, i, esize), p.V, m, q.c, q.K, q.P, thr, Z);
     }
   }
   if (tid == 0) {
-    stf(&ri->m, m);
-    st32(&ri->arg, (uint32_t)a);
-    stf(&ri->Z, Zk);
-    st32(&ri->thr, thr);
-    st32(&ri->state, state);
-    st32(&ri->clo, clo);
-    st32(&ri->chi, chi);
-    stf(&ri->Ztot, sum);
+    RowInfo* ri = p.rinfo + r;
+    ri->m = m;
+    ri->arg = a;
+    ri->Z = Z;
+    ri->lz = __builtin_amdgcn_logf(Z);
+    ri->fthr = thr == 0 ? -INFINITY : key_value<E>(thr);
+    ri->state = bad ? ST_BAD : 0u;
+    ri->Ztot = sum;
+    ri->gath = sg >= 0 ? __uint_as_float(sm.win[1]) : 0.0f;
     atomicExch(&p.cnt1[r], 0u);
   }
 }
 
+// Histogram pass of a truncated bf16 slice (values held in registers), relative to the slice max ms:
+// per-code counts of the WTOP codes below ms; top-p-only rows also add the normaliser sum and the
+// weight-bin counts (bin floor(-l c BRC) - cbase).  Out-of-range entries go to a per-lane spare bin.
+template <int VPT, bool TOPP_ONLY>
+__device__ void k1_hist(K1Smem& sm, const uint4 (&v)[VPT], int nv, float ms, float c, float cbase, float& sum) {
+  const int tid = threadIdx.x;
+  const uint32_t lane = tid & 63;
+  const uint32_t keyms2 = key16f(ms) * 0x10001u;
+  const uint32_t spare2 = (WTOP + lane) * 0x10001u;
+  const uint32_t spare_c = NBC + lane;
+  const float cb = c * BRC;
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) {
+    const int j = tid + u * NT;
+    if (j < nv) {
+      const uint32_t wv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t d2 = min16x2(sub16x2(keyms2, key16x2(wv[q])), spare2);
+        atomicAdd(&sm.u.st.hw[d2 & 0xffffu], 1u);
+        atomicAdd(&sm.u.st.hw[d2 >> 16], 1u);
+        if (TOPP_ONLY) {
+          const float f0 = __uint_as_float(wv[q] << 16), f1 = __uint_as_float(wv[q] & 0xffff0000u);
+          sum += fexp2((f0 - ms) * c);
+          sum += fexp2((f1 - ms) * c);
+          const uint32_t j0 = min(__float2uint_rz(fmaf(f0, -cb, -cbase)), spare_c);
+          const uint32_t j1 = min(__float2uint_rz(fmaf(f1, -cb, -cbase)), spare_c);
+          atomicAdd(&sm.u.st.hc[j0], 1u);
+          atomicAdd(&sm.u.st.hc[j1], 1u);
+        }
+      }
+    }
+  }
+}
+
+// One K1 work item: slice s of logit row r.
 template <class E, int VPT>
-__global__ __launch_bounds__(NT) void k1_stats(Params p) {
+__device__ void k1_item(const Params& p, K1Smem& sm, int item, int r, int s) {
   constexpr int EPV = E::EPV;
   constexpr int esize = 16 / EPV;
   constexpr bool BF = E::KEYBITS == 16;
-  __shared__ K1Smem sm;
   const int tid = threadIdx.x;
-  const int r = blockIdx.x / p.S1, s = blockIdx.x - r * p.S1;
   const int b = r / p.rows, i = r - b * p.rows;
   const RowParams q = row_params(p, b);
   const int x0 = s * p.L1;
-  const int x1 = min(x0 + p.L1, p.V);
-  const int nv = x0 < x1 ? (x1 - x0) / EPV : 0;
+  const int nv = min(p.L1, p.V - x0) / EPV;
   const uint4* src = (const uint4*)(row_ptr(p, b, i, esize) + (size_t)x0 * esize);
-  SV_TRACE_AT(blockIdx.x, 0);
+  SV_TRACE_AT(p, item, 0);
 
   uint4 v[VPT];
 #pragma unroll
@@ -697,229 +821,106 @@ __global__ __launch_bounds__(NT) void k1_stats(Params p) {
     const int j = tid + u * NT;
     if (j < nv) v[u] = src[j];
   }
+  // draft-position rows also record their logit at the draft token (used by the accept chain)
+  float gval = 0.0f;
+  if (p.mode == MODE_VERIFY && i != p.k) {
+    const int xg = p.draft_tokens[(size_t)b * p.k + (i < p.k ? i : i - p.k - 1)];
+    if (tid == 0 && xg >= x0 && xg < x0 + nv * EPV) gval = E::load1(row_ptr(p, b, i, esize), xg);
+  }
   float m = -INFINITY, sum = 0.0f;
   int a = INT_MAX;
   uint32_t fl = 0;
-#pragma unroll
-  for (int u = 0; u < VPT; ++u) {
-    const int j = tid + u * NT;
-    if (j < nv) {
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        const float f = E::get(v[u], e);
-        fl |= (__builtin_isnan(f) || f == INFINITY) ? 1u : 0u;
-        if (f > m) {
-          m = f;
-          a = x0 + j * EPV + e;
-        }
-      }
-    }
-  }
-  const bool hist = BF && q.trunc;
-  float base_s = 0.0f;
-  if (hist) {
-    // histograms are relative to the slice max
-    const float ms = block_max(sm.rs, m);
-    for (int j = tid; j < WTOP; j += NT) sm.hw[j] = 0;
-    for (int j = tid; j < NB; j += NT) {
-      sm.hbc[j] = 0;
-      sm.hbm[j] = 0.0f;
-    }
-    __syncthreads();
-    if (ms != -INFINITY) {
-      const uint32_t keyms = key32(ms) >> 16;
-      base_s = floorf(-ms * q.c * BR);
-#pragma unroll
-      for (int u = 0; u < VPT; ++u) {
-        const int j = tid + u * NT;
-        if (j < nv) {
-#pragma unroll
-          for (int e = 0; e < EPV; ++e) {
-            const float f = E::get(v[u], e);
-            if (f == -INFINITY) continue;
-            sum += fexp2((f - ms) * q.c);
-            const uint32_t d = keyms - key_of<E>(f);
-            if (d < (uint32_t)WTOP) atomicAdd(&sm.hw[d], 1u);
-            const float ta = f * q.c;
-            const float bin = floorf(-ta * BR);
-            const float jb = bin - base_s;
-            if (jb >= 0.0f && jb < (float)NB) {
-              atomicAdd(&sm.hbc[(int)jb], 1u);
-              atomicAdd(&sm.hbm[(int)jb], fexp2(ta + bin / BR));
-            }
-          }
-        }
-      }
-    }
-    m = ms;  // the sums above are relative to the slice max
-  } else if (!q.greedy && m != -INFINITY) {
+  if (q.greedy) {
+    // lowest argmax; NaN never compares greater, so it is flagged separately
+    bool nan = false;
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
       const int j = tid + u * NT;
       if (j < nv) {
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) sum += fexp2((E::get(v[u], e) - m) * q.c);
+        for (int e = 0; e < EPV; ++e) {
+          const float f = E::get(v[u], e);
+          nan = nan || (f != f);
+          if (f > m) {
+            m = f;
+            a = x0 + j * EPV + e;
+          }
+        }
       }
     }
+    fl = (nan || m == INFINITY) ? 1u : 0u;
+  } else {
+    // NaN-propagating max: a NaN or +inf anywhere shows in the row max
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int j = tid + u * NT;
+      if (j < nv) {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) m = nan_max(m, E::get(v[u], e));
+      }
+    }
+    SV_TRACE_AT(p, item, 1);
+    if (!(BF && q.trunc)) {
+      // the whole-row normaliser, unless top-k fixes the kept set (fp32 truncated rows: radix select)
+      if (!q.useK && m > -INFINITY) {
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+          const int j = tid + u * NT;
+          if (j < nv) {
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) sum += fexp2((E::get(v[u], e) - m) * q.c);
+          }
+        }
+      }
+    } else if constexpr (BF) {
+      // histograms relative to the slice max
+      const bool topp_only = !q.useK;
+      sm.u.st.hw[tid] = 0;
+      sm.u.st.hw[tid + NT] = 0;
+      if (topp_only) sm.u.st.hc[tid] = 0;
+      const float ms = block_nan_max(sm.rs, m);
+      const float cbase = floorf(-ms * (q.c * BRC));
+      if (ms > -INFINITY && ms < INFINITY) {  // not NaN, +inf or an all -inf slice
+        if (topp_only)
+          k1_hist<VPT, true>(sm, v, nv, ms, q.c, cbase, sum);
+        else
+          k1_hist<VPT, false>(sm, v, nv, ms, q.c, cbase, sum);
+      }
+      m = ms;  // the sums above are relative to the slice max
+      __syncthreads();
+      uint32_t* hw = p.hw1 + ((size_t)r * p.S1 + s) * (WTOP / 2);
+      st32(&hw[tid], sm.u.st.hw[2 * tid] | (sm.u.st.hw[2 * tid + 1] << 16));  // WTOP / 2 == NT
+      if (topp_only) {
+        uint32_t* hc = p.hc1 + ((size_t)r * p.S1 + s) * HCW;
+        if (tid < NBC / 2) st32(&hc[tid], sm.u.st.hc[2 * tid] | (sm.u.st.hc[2 * tid + 1] << 16));
+        if (tid == 0) stf(&hc[NBC / 2], cbase);
+      }
+    }
+    if (!(m == m) || m == INFINITY) fl = 1u;
   }
-  SV_TRACE_AT(blockIdx.x, 1);
   block_stats(sm.rs, m, a, sum, fl, q.c);
-  StatPart* sp = p.st1 + (size_t)r * p.S1 + s;
   if (tid == 0) {
+    StatPart* sp = p.st1 + (size_t)r * p.S1 + s;
     stf(&sp->m, m);
     st32(&sp->arg, (uint32_t)a);
     stf(&sp->s, sum);
     st32(&sp->flags, fl);
+    stf(&sp->g, gval);
   }
-  if (hist) {
-    uint32_t* hw = p.hw1 + ((size_t)r * p.S1 + s) * (WTOP / 2);
-    for (int j = tid; j < WTOP / 2; j += NT) st32(&hw[j], sm.hw[2 * j] | (sm.hw[2 * j + 1] << 16));
-    uint32_t* hb = p.hb1 + ((size_t)r * p.S1 + s) * (NB / 2 + NB + 1);
-    for (int j = tid; j < NB / 2; j += NT) st32(&hb[j], sm.hbc[2 * j] | (sm.hbc[2 * j + 1] << 16));
-    for (int j = tid; j < NB; j += NT) stf(&hb[NB / 2 + j], sm.hbm[j]);
-    if (tid == 0) stf(&hb[NB / 2 + NB], base_s);
-  }
-  SV_TRACE_AT(blockIdx.x, 2);
+  SV_TRACE_AT(p, item, 2);
   if (arrive_last(&p.cnt1[r], (uint32_t)p.S1, &sm.rs.flag)) {
-    SV_TRACE_AT(blockIdx.x, 3);
-    k1_merge<E>(p, sm, r, q);
-    SV_TRACE_AT(blockIdx.x, 4);
+    SV_TRACE_AT(p, item, 3);
+    k1_merge<E>(p, sm, r, b, i, q);
+    SV_TRACE_AT(p, item, 7);
   }
 }
 
-// ---------------------------------------------------------------------------------------------
-// K3: exact per-code window (rows whose threshold lies below the top codes), or the radix select.
-// ---------------------------------------------------------------------------------------------
-struct K3Smem {
-  RedSmem rs;
-  uint32_t h[WF];
-  uint32_t scnt[WF];
-  unsigned long long smass[WF];
-  SelState ss;
-  RadixSmem rad;
-  uint32_t state, clo, chi;
-  float m, Ztot;
-};
-
 template <class E, int VPT>
-__global__ __launch_bounds__(NT) void k3_fine(Params p) {
-  constexpr int EPV = E::EPV;
-  constexpr int esize = 16 / EPV;
-  __shared__ K3Smem sm;
-  const int tid = threadIdx.x;
-  const int r = blockIdx.x / p.S3, s = blockIdx.x - r * p.S3;
-  RowInfo* ri = p.rinfo + r;
-  if (tid == 0) {
-    sm.state = ri->state;
-    sm.clo = ri->clo;
-    sm.chi = ri->chi;
-    sm.m = ri->m;
-    sm.Ztot = ri->Ztot;
-  }
-  __syncthreads();
-  const uint32_t state = sm.state;
-  if (state & ST_BAD) return;
-  if (!(state & (ST_FINE | ST_RADIX))) return;
-  const int b = r / p.rows, i = r - b * p.rows;
-  const RowParams q = row_params(p, b);
-  const float m = sm.m;
-  const uint8_t* row = row_ptr(p, b, i, esize);
-  if (state & ST_RADIX) {
-    if (s != 0) return;
-    uint32_t thr;
-    float Z;
-    row_cutoff<E>(sm.rad, sm.rs, row, p.V, m, q.c, q.K, q.P, thr, Z);
-    if (tid == 0) {
-      ri->thr = thr;
-      ri->Z = Z;
-      ri->state = state & ~ST_RADIX;
-    }
-    return;
-  }
-  const uint32_t clo = sm.clo, chi = sm.chi;
-  const int width = (int)(chi - clo + 1);
-  for (int j = tid; j < width; j += NT) sm.h[j] = 0;
-  __syncthreads();
-  const int x0 = s * p.L3;
-  const int x1 = min(x0 + p.L3, p.V);
-  const int nv = x0 < x1 ? (x1 - x0) / EPV : 0;
-  const uint4* src = (const uint4*)(row + (size_t)x0 * esize);
-  uint4 v[VPT];
-#pragma unroll
-  for (int u = 0; u < VPT; ++u) {
-    const int j = tid + u * NT;
-    if (j < nv) v[u] = src[j];
-  }
-  uint32_t acnt = 0;
-  unsigned long long amass = 0;
-#pragma unroll
-  for (int u = 0; u < VPT; ++u) {
-    const int j = tid + u * NT;
-    if (j < nv) {
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        const float f = E::get(v[u], e);
-        const uint32_t key = key_of<E>(f);
-        if (key > chi) {
-          ++acnt;
-          amass += fixmass(fexp2((f - m) * q.c));
-        } else if (key >= clo) {
-          atomicAdd(&sm.h[key - clo], 1u);
-        }
-      }
-    }
-  }
-  // workgroup sums of the entries above the window
-  const uint32_t tc = block_inclusive_scan<uint32_t>(acnt, sm.rs.scan32);
-  const unsigned long long tm = block_inclusive_scan<unsigned long long>(amass, sm.rs.scan64);
-  FinePart* fp = p.fp3 + (size_t)r * p.S3 + s;
-  if (tid == NT - 1) {
-    st64(&fp->above_mass, tm);
-    st32(&fp->above_cnt, tc);
-  }
-  uint32_t* fc = p.fc3 + ((size_t)r * p.S3 + s) * (WF / 2);
-  for (int j = tid; j < (width + 1) / 2; j += NT) {
-    const uint32_t lo = sm.h[2 * j], hi = (2 * j + 1 < width) ? sm.h[2 * j + 1] : 0u;
-    st32(&fc[j], lo | (hi << 16));
-  }
-  if (!arrive_last(&p.cnt3[r], (uint32_t)p.S3, &sm.rs.flag)) return;
-  // merge: entries from the top of the window (key chi) downwards
-  uint32_t above_c = 0;
-  unsigned long long above_m = 0;
-  for (int t = 0; t < p.S3; ++t) {
-    above_c += ld32(&p.fp3[(size_t)r * p.S3 + t].above_cnt);
-    above_m += ld64(&p.fp3[(size_t)r * p.S3 + t].above_mass);
-  }
-  for (int co = tid; co < width; co += NT) {
-    const uint32_t key = chi - (uint32_t)co;
-    const uint32_t d = key - clo;
-    uint32_t cnt = 0;
-    for (int t = 0; t < p.S3; ++t) {
-      const uint32_t w = ld32(&p.fc3[((size_t)r * p.S3 + t) * (WF / 2) + (d >> 1)]);
-      cnt += (d & 1) ? (w >> 16) : (w & 0xffffu);
-    }
-    sm.scnt[co] = cnt;
-    sm.smass[co] = cnt ? (unsigned long long)cnt * fixmass(fexp2((key16_value(key) - m) * q.c)) : 0ull;
-  }
-  __syncthreads();
-  int sel = -1;
-  unsigned long long zsel = 0;
-  const bool good = select_run(sm.scnt, sm.smass, sm.ss, sm.rs, width, above_c, above_m, (double)sm.Ztot * 0x1p40,
-                               q.K, q.P, p.V, sel, zsel);
-  uint32_t thr = 0;
-  float Z = 0.0f;
-  if (good) {
-    thr = chi - (uint32_t)sel;
-    Z = (float)((double)zsel * 0x1p-40);
-  } else {
-    row_cutoff<E>(sm.rad, sm.rs, row, p.V, m, q.c, q.K, q.P, thr, Z);
-  }
-  if (tid == 0) {
-    ri->thr = thr;
-    ri->Z = Z;
-    ri->state = state & ~ST_FINE;
-    atomicExch(&p.cnt3[r], 0u);
-  }
+__global__ __launch_bounds__(NT, OCC1) void k1_stats(Params p) {
+  __shared__ K1Smem sm;
+  int r, s;
+  item_rs(blockIdx.x, p.R, p.S1, r, s);
+  k1_item<E, VPT>(p, sm, blockIdx.x, r, s);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -927,34 +928,79 @@ __global__ __launch_bounds__(NT) void k3_fine(Params p) {
 // ---------------------------------------------------------------------------------------------
 struct K5Smem {
   RedSmem rs;
-  float m[MAXROWS], Z[MAXROWS], invZ[MAXROWS];
+  float m[MAXROWS], Z[MAXROWS], lz[MAXROWS], fthr[MAXROWS], gath[MAXROWS];
   int32_t arg[MAXROWS];
-  uint32_t thr[MAXROWS], state[MAXROWS];
-  float gath[2 * MAXK];
+  uint32_t state[MAXROWS];
+  int32_t tok[MAXK];
   float u[MAXK];
   float wacc[MAXK][NWAVE];
-  float stage[64 * (MAXK + 2)];
-  int32_t n, pick;
+  int32_t n;
 };
 
-// Gumbel-max over w(x) = exp2((l - m) c) on the kept entries of one row (stream tag, b, position j).
+// p(x) = exp2((l - m) c - log2 Z) on the kept entries, 0 below the kept threshold.
+__device__ inline float kept_p(float f, float m, float c, float lz, float fthr) {
+  return f >= fthr ? fexp2(fmaf(f - m, c, -lz)) : 0.0f;
+}
+
+// Exponential-race key w / E2 with E2 = -log2 U (see exp_race_E2): a reciprocal and a product; keys
+// are only compared with each other.
+__device__ inline float race_key(float w, uint32_t word) { return w * __builtin_amdgcn_rcpf(exp_race_E2(word)); }
+
+// Race candidate update: larger key wins, the lower index on an exact tie.
+__device__ inline void race_take(float& best, int& bidx, float& bval, float key, int idx, float val) {
+  if (key > best || (key == best && idx < bidx)) {
+    best = key;
+    bidx = idx;
+    bval = val;
+  }
+}
+
+// Workgroup race winner (key, index, logit) into every thread.
+__device__ void block_race(RedSmem& rs, float& best, int& bidx, float& bval) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float k2 = __shfl_xor(best, o, 64);
+    const int i2 = __shfl_xor(bidx, o, 64);
+    const float v2 = __shfl_xor(bval, o, 64);
+    race_take(best, bidx, bval, k2, i2, v2);
+  }
+  if (lane == 0) {
+    rs.f[wave] = best;
+    rs.i[wave] = bidx;
+    rs.g[wave] = bval;
+  }
+  __syncthreads();
+  best = rs.f[0];
+  bidx = rs.i[0];
+  bval = rs.g[0];
+  for (int w = 1; w < NWAVE; ++w) race_take(best, bidx, bval, rs.f[w], rs.i[w], rs.g[w]);
+  __syncthreads();
+}
+
+// Gumbel-max candidates over w(x) = exp2((l - m) c) on the kept entries of one 16-byte vector
+// (stream tag, b, position j).  Groups of four entries with no kept entry draw nothing.
 template <class E>
-__device__ void gumbel_row_partial(const uint4& v, int xbase, float m, float c, uint32_t thr, uint32_t tag,
-                                   uint32_t b, uint32_t j, const Params& p, float& best, int& bidx) {
+__device__ void gumbel_vec(const uint4& v, int xbase, float m, float c, float fthr, uint32_t tag, uint32_t b,
+                           uint32_t j, const Params& p, float& best, int& bidx, float& bval) {
 #pragma unroll
   for (int g = 0; g < E::EPV; g += 4) {
-    const int x = xbase + g;
-    const uint4 w4 = philox10(make_uint4((uint32_t)x >> 2, b, (tag << 24) | j, p.offset), p.key0, p.key1);
+    float w[4];
+    bool any = false;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float f = E::get(v, g + e);
-      const float w = key_of<E>(f) >= thr ? fexp2((f - m) * c) : 0.0f;
-      if (w > 0.0f) {
-        const uint32_t word = e == 0 ? w4.x : e == 1 ? w4.y : e == 2 ? w4.z : w4.w;
-        const float key = w / exp_race_E2(word);
-        if (key > best) {
-          best = key;
-          bidx = x + e;
+      w[e] = f >= fthr ? fexp2((f - m) * c) : 0.0f;
+      any = any || w[e] > 0.0f;
+    }
+    if (any) {
+      const int x = xbase + g;
+      const uint4 w4 = philox10(make_uint4((uint32_t)x >> 2, b, (tag << 24) | j, p.offset), p.key0, p.key1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (w[e] > 0.0f) {
+          const uint32_t word = e == 0 ? w4.x : e == 1 ? w4.y : e == 2 ? w4.z : w4.w;
+          race_take(best, bidx, bval, race_key(w[e], word), x + e, E::get(v, g + e));
         }
       }
     }
@@ -994,14 +1040,14 @@ __device__ void k5_finalize(const Params& p, K5Smem& sm, int b, bool ok, const R
     }
     int n = k;
     for (int i = 0; i < k; ++i)
-      if (p.draft_tokens[(size_t)b * k + i] != sm.arg[i]) {
+      if (sm.tok[i] != sm.arg[i]) {
         n = i;
         break;
       }
     const int y = sm.arg[n];
     if (tid < k) p.alpha[(size_t)b * k + tid] = (sm.arg[tid] == sm.arg[k + 1 + tid]) ? 1.0f : 0.0f;
     if (tid <= k) {
-      const int t = tid < n ? p.draft_tokens[(size_t)b * k + tid] : (tid == n ? y : -1);
+      const int t = tid < n ? sm.tok[tid] : (tid == n ? y : -1);
       p.tokens[(size_t)b * (k + 1) + tid] = t;
       p.logprobs[(size_t)b * (k + 1) + tid] = 0.0f;
     }
@@ -1009,52 +1055,51 @@ __device__ void k5_finalize(const Params& p, K5Smem& sm, int b, bool ok, const R
     return;
   }
   const int n = sm.n;
-  const int W = k + 2;
-  float asum = 0.0f;  // thread t < k: alpha_t summed in slice order
-  float best = 0.0f;
+  const int lane = tid & 63, wave = tid >> 6;
+  // slice partials: thread t reads slices t, t + NT, ... (one round of loads when S <= NT)
+  float best = 0.0f, bval = 0.0f;
   int bidx = INT_MAX;
-  for (int s0 = 0; s0 < S; s0 += 64) {
-    const int cnt = min(64, S - s0);
-    for (int e = tid; e < cnt * W; e += NT) {
-      const int sl = e / W, f = e - sl * W;
-      const FinalPart* fp = p.fin5 + (size_t)b * S + s0 + sl;
-      sm.stage[e] = f < k ? ldf(&fp->alpha[f]) : (f == k ? ldf(&fp->key) : __uint_as_float(ld32(&fp->idx)));
-    }
-    __syncthreads();
-    if (tid < k)
-      for (int sl = 0; sl < cnt; ++sl) asum += sm.stage[sl * W + tid];
-    if (tid == 0)
-      for (int sl = 0; sl < cnt; ++sl) {
-        const float key = sm.stage[sl * W + k];
-        if (key > best) {
-          best = key;
-          bidx = (int)__float_as_uint(sm.stage[sl * W + k + 1]);
-        }
-      }
-    __syncthreads();
+  float al[MAXK];
+#pragma unroll
+  for (int i = 0; i < MAXK; ++i) al[i] = 0.0f;
+  for (int sl = tid; sl < S; sl += NT) {
+    const FinalPart* fp = p.fin5 + (size_t)b * S + sl;
+    race_take(best, bidx, bval, ldf(&fp->key), (int)ld32(&fp->idx), ldf(&fp->val));
+#pragma unroll
+    for (int i = 0; i < MAXK; ++i)
+      if (i < k) al[i] += ldf(&fp->alpha[i]);
   }
-  if (tid < k) p.alpha[(size_t)b * k + tid] = asum;
-  if (tid == 0) sm.pick = bidx;
-  __syncthreads();
-  int y = sm.pick;
-  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < MAXK; ++i) {
+    if (i < k) {
+      const float v = wave_sum(al[i]);
+      if (lane == 0) sm.wacc[i][wave] = v;
+    }
+  }
+  block_race(sm.rs, best, bidx, bval);  // also orders the wacc writes before the reads below
+  if (tid < k) {
+    float v = 0.0f;
+    for (int w = 0; w < NWAVE; ++w) v += sm.wacc[tid][w];
+    p.alpha[(size_t)b * k + tid] = v;
+  }
+  int y = bidx;
+  float yv = bval;
   if (y == INT_MAX && n < k) {
     // The residual mass vanished in fp32 (rounding only): draw from p_n over the whole row.
-    const uint8_t* row = row_ptr(p, b, n, esize);
-    float bb = 0.0f;
+    const uint4* row = (const uint4*)row_ptr(p, b, n, esize);
+    float bb = 0.0f, bv = 0.0f;
     int bi = INT_MAX;
     for (int j = tid; j < p.V / E::EPV; j += NT)
-      gumbel_row_partial<E>(((const uint4*)row)[j], j * E::EPV, sm.m[n], q.c, sm.thr[n], 1u, (uint32_t)b, (uint32_t)n,
-                            p, bb, bi);
-    block_maxarg(sm.rs, bb, bi);
+      gumbel_vec<E>(row[j], j * E::EPV, sm.m[n], q.c, sm.fthr[n], 1u, (uint32_t)b, (uint32_t)n, p, bb, bi, bv);
+    block_race(sm.rs, bb, bi, bv);
     y = bi;
+    yv = bv;
   }
   if (y < 0 || y >= p.V) return write_sentinel(p, b);  // no candidate: not reachable for a valid row
   if (p.mode == MODE_SAMPLE) {
     if (tid == 0) {
-      const float l = E::load1(row_ptr(p, b, 0, esize), y);
       p.tokens[b] = y;
-      p.logprobs[b] = (l - sm.m[0]) / q.T - logf(sm.Z[0]);
+      p.logprobs[b] = (yv - sm.m[0]) / q.T - logf(sm.Z[0]);
     }
     return;
   }
@@ -1062,8 +1107,8 @@ __device__ void k5_finalize(const Params& p, K5Smem& sm, int b, bool ok, const R
     int t = -1;
     float lp = 0.0f;
     if (tid <= n) {
-      t = tid < n ? p.draft_tokens[(size_t)b * k + tid] : y;
-      const float l = tid < n ? sm.gath[tid] : E::load1(row_ptr(p, b, tid, esize), t);
+      t = tid < n ? sm.tok[tid] : y;
+      const float l = tid < n ? sm.gath[tid] : yv;
       lp = (l - sm.m[tid]) / q.T - logf(sm.Z[tid]);
     }
     p.tokens[(size_t)b * (k + 1) + tid] = t;
@@ -1073,136 +1118,226 @@ __device__ void k5_finalize(const Params& p, K5Smem& sm, int b, bool ok, const R
 }
 
 template <class E, int VPT>
-__global__ __launch_bounds__(NT) void k5_verify(Params p) {
+__device__ inline void load_slice(const uint8_t* row, int x0, int nv, uint4 (&v)[VPT]) {
+  constexpr int esize = 16 / E::EPV;
+  const uint4* src = (const uint4*)(row + (size_t)x0 * esize);
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) {
+    const int j = threadIdx.x + u * NT;
+    if (j < nv) v[u] = src[j];
+  }
+}
+
+// 16-byte vector u (runtime index) of a per-thread slice held in registers.
+template <int VPT>
+__device__ inline uint4 pick_vec(const uint4 (&v)[VPT], int u) {
+  uint4 r = v[0];
+#pragma unroll
+  for (int t = 1; t < VPT; ++t)
+    if (u == t) r = v[t];
+  return r;
+}
+
+// Gumbel-max race over the 4-entry groups of a slice held in registers, one vector at a time (the
+// Philox rounds of different groups are not interleaved, which keeps register use flat).  Weights:
+// RESID: r(x) = max(p(x) - q(x), 0) of a target / draft pair; otherwise w(x) = exp2((l - m) c) on the
+// kept entries of one row.  Either is 0 wherever the (target) logit is below the kept threshold tt, so
+// a vector with no entry >= tt is skipped before any exp2.  Stream (tag, b, position j).  The winner's
+// (target) logit rides along.
+template <class E, int VPT, bool RESID>
+__device__ void race_slice(const Params& p, const uint4 (&va)[VPT], const uint4 (&vb)[VPT], int x0, int nv, float c,
+                           float mt, float lt, float tt, float md, float ld, float td, uint32_t tag, uint32_t sb,
+                           uint32_t sj, float& best, int& bidx, float& bval) {
+  constexpr int EPV = E::EPV;
+  const int tid = threadIdx.x;
+#pragma unroll 1
+  for (int u = 0; u < VPT; ++u) {
+    const int j = tid + u * NT;
+    if (j >= nv) continue;
+    const uint4 a = pick_vec<VPT>(va, u);
+    bool kept = false;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) kept = kept || E::get(a, e) >= tt;
+    if (!kept) continue;
+    const uint4 bv = RESID ? pick_vec<VPT>(vb, u) : a;
+#pragma unroll 1
+    for (int g = 0; g < EPV; g += 4) {
+      float w[4];
+      bool any = false;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float ft = E::get(a, g + e);
+        if (RESID) {
+          const float fd = E::get(bv, g + e);
+          w[e] = kept_p(ft, mt, c, lt, tt) - kept_p(fd, md, c, ld, td);
+        } else {
+          w[e] = ft >= tt ? fexp2((ft - mt) * c) : 0.0f;
+        }
+        any = any || w[e] > 0.0f;
+      }
+      if (!any) continue;
+      const int x = x0 + j * EPV + g;
+      const uint4 w4 = philox10(make_uint4((uint32_t)x >> 2, sb, (tag << 24) | sj, p.offset), p.key0, p.key1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (w[e] > 0.0f) {
+          const uint32_t word = e == 0 ? w4.x : e == 1 ? w4.y : e == 2 ? w4.z : w4.w;
+          race_take(best, bidx, bval, race_key(w[e], word), x + e, E::get(a, g + e));
+        }
+      }
+    }
+  }
+}
+
+// Alpha partial sum of draft position i over this slice (va / vb: its target / draft slices), and the
+// residual race if i is the first rejected position.  min(p, q) is taken on the log2 weights, so it
+// costs one exp2.  TRUNC: the batch row is truncated (some entries have p = 0); then a vector without
+// a kept target entry adds nothing and is skipped.
+template <class E, int VPT, bool TRUNC>
+__device__ void k5_position(const Params& p, K5Smem& sm, int b, int i, int n, int x0, int nv, float c,
+                            const uint4 (&va)[VPT], const uint4 (&vb)[VPT], float& best, int& bidx, float& bval) {
+  constexpr int EPV = E::EPV;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int k = p.k;
+  const float mt = sm.m[i], md = sm.m[k + 1 + i];
+  const float lt = sm.lz[i], ld = sm.lz[k + 1 + i];
+  const float tt = sm.fthr[i], td = sm.fthr[k + 1 + i];
+  float acc = 0.0f;
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) {
+    const int j = tid + u * NT;
+    bool live = j < nv;
+    if (TRUNC) {
+      bool any = false;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) any = any || E::get(va[u], e) >= tt;
+      live = live && any;
+    }
+    if (live) {
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        const float ft = E::get(va[u], e), fd = E::get(vb[u], e);
+        float lp = fmaf(ft - mt, c, -lt), lq = fmaf(fd - md, c, -ld);  // log2 p, log2 q
+        if (TRUNC) {
+          lp = ft >= tt ? lp : -INFINITY;
+          lq = fd >= td ? lq : -INFINITY;
+        }
+        acc += fexp2(fminf(lp, lq));
+      }
+    }
+  }
+  if (i == n)
+    race_slice<E, VPT, true>(p, va, vb, x0, nv, c, mt, lt, tt, md, ld, td, 1u, (uint32_t)b, (uint32_t)n, best, bidx,
+                             bval);
+  acc = wave_sum(acc);
+  if (lane == 0) sm.wacc[i][wave] = acc;
+}
+
+// Every draft position of this slice, two positions' slices in flight: (a0, b0) and (a1, b1) hold
+// positions 0 and 1 on entry; position i + 2 is loaded into the pair that position i has just used.
+template <class E, int VPT, bool TRUNC>
+__device__ void k5_positions(const Params& p, K5Smem& sm, int b, int n, int x0, int nv, float c, uint4 (&a0)[VPT],
+                             uint4 (&b0)[VPT], uint4 (&a1)[VPT], uint4 (&b1)[VPT], float& best, int& bidx,
+                             float& bval) {
+  constexpr int esize = 16 / E::EPV;
+  const int k = p.k;
+  for (int i = 0; i < k; i += 2) {
+    k5_position<E, VPT, TRUNC>(p, sm, b, i, n, x0, nv, c, a0, b0, best, bidx, bval);
+    if (i + 2 < k) {
+      load_slice<E, VPT>(row_ptr(p, b, i + 2, esize), x0, nv, a0);
+      load_slice<E, VPT>(row_ptr(p, b, k + 3 + i, esize), x0, nv, b0);
+    }
+    if (i + 1 < k) {
+      k5_position<E, VPT, TRUNC>(p, sm, b, i + 1, n, x0, nv, c, a1, b1, best, bidx, bval);
+      if (i + 3 < k) {
+        load_slice<E, VPT>(row_ptr(p, b, i + 3, esize), x0, nv, a1);
+        load_slice<E, VPT>(row_ptr(p, b, k + 4 + i, esize), x0, nv, b1);
+      }
+    }
+  }
+}
+
+// One K5 work item: slice s of batch row b.
+template <class E, int VPT>
+__device__ void k5_item(const Params& p, K5Smem& sm, int item, int b, int s) {
   constexpr int EPV = E::EPV;
   constexpr int esize = 16 / EPV;
-  __shared__ K5Smem sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int b = blockIdx.x / p.S5, s = blockIdx.x - b * p.S5;
+  const int tid = threadIdx.x;
+  SV_TRACE5_AT(p, item, 0);
   const int k = p.k, rows = p.rows;
+  const int x0 = s * p.L5;
+  const int nv = min(p.L5, p.V - x0) / EPV;
   const RowParams q = row_params(p, b);
-  bool ok = q.ok;
-  for (int i = 0; i < k; ++i) {
-    const int x = p.draft_tokens[(size_t)b * k + i];
-    ok = ok && x >= 0 && x < p.V;
-  }
-  float gv = 0.0f;
-  if (ok && !q.greedy && tid < 2 * k) {
-    const int i = tid < k ? tid : tid - k;
-    gv = E::load1(row_ptr(p, b, tid < k ? i : k + 1 + i, esize), p.draft_tokens[(size_t)b * k + i]);
+  // Everything else independent is issued at once: the first two positions' slices, the rows'
+  // statistics (with the logits at the draft tokens), the draft tokens and the accept uniforms.
+  uint4 a0[VPT], b0[VPT], a1[VPT], b1[VPT];
+  if (!q.greedy) {
+    if (k > 0) {
+      load_slice<E, VPT>(row_ptr(p, b, 0, esize), x0, nv, a0);
+      load_slice<E, VPT>(row_ptr(p, b, k + 1, esize), x0, nv, b0);
+    }
+    if (k > 1) {
+      load_slice<E, VPT>(row_ptr(p, b, 1, esize), x0, nv, a1);
+      load_slice<E, VPT>(row_ptr(p, b, k + 2, esize), x0, nv, b1);
+    }
   }
   if (tid < rows) {
     const RowInfo* ri = p.rinfo + (size_t)b * rows + tid;
     sm.m[tid] = ri->m;
     sm.arg[tid] = ri->arg;
     sm.Z[tid] = ri->Z;
-    sm.invZ[tid] = 1.0f / ri->Z;
-    sm.thr[tid] = ri->thr;
+    sm.lz[tid] = ri->lz;
+    sm.fthr[tid] = ri->fthr;
     sm.state[tid] = ri->state;
+    sm.gath[tid] = ri->gath;
   }
-  if (ok && !q.greedy && tid < k) {
+  if (tid < k) {
+    sm.tok[tid] = p.draft_tokens[(size_t)b * k + tid];
     const uint4 w4 = philox10(make_uint4((uint32_t)tid >> 2, (uint32_t)b, 0u, p.offset), p.key0, p.key1);
     const int qq = tid & 3;
     sm.u[tid] = u24(qq == 0 ? w4.x : qq == 1 ? w4.y : qq == 2 ? w4.z : w4.w);
   }
-  if (ok && !q.greedy && tid < 2 * k) sm.gath[tid] = gv;
   __syncthreads();
+  SV_TRACE5_AT(p, item, 1);
+  bool ok = q.ok;
+  for (int i = 0; i < k; ++i) ok = ok && sm.tok[i] >= 0 && sm.tok[i] < p.V;
   for (int r = 0; r < rows; ++r) ok = ok && sm.state[r] == 0;
   if (ok && !q.greedy) {
-    if (tid == 0) {
-      int n = k;  // k = 0 in sample mode: the draw below is the sampler's
-      for (int i = 0; i < k; ++i) {
-        const float lt = sm.gath[i], ld = sm.gath[k + i];
-        const float pt = key_of<E>(lt) >= sm.thr[i] ? fexp2((lt - sm.m[i]) * q.c) / sm.Z[i] : 0.0f;
-        const float qd = key_of<E>(ld) >= sm.thr[k + 1 + i] ? fexp2((ld - sm.m[k + 1 + i]) * q.c) / sm.Z[k + 1 + i] : 0.0f;
-        const bool accept = pt > 0.0f && (qd == 0.0f || sm.u[i] < pt / qd);
-        if (!accept) {
-          n = i;
-          break;
-        }
+    // accept decisions of all positions at once (lane i of wave 0); n = the first rejection, else k
+    // (k = 0 in sample mode: the draw below is the sampler's)
+    if (tid < 64) {
+      bool reject = false;
+      if (tid < k) {
+        const float pt = kept_p(sm.gath[tid], sm.m[tid], q.c, sm.lz[tid], sm.fthr[tid]);
+        const float qd =
+            kept_p(sm.gath[k + 1 + tid], sm.m[k + 1 + tid], q.c, sm.lz[k + 1 + tid], sm.fthr[k + 1 + tid]);
+        reject = !(pt > 0.0f && (qd == 0.0f || sm.u[tid] < pt / qd));
       }
-      sm.n = n;
+      const int fr = first_lane(reject);
+      if (tid == 0) sm.n = fr < k ? fr : k;
     }
     __syncthreads();
+    SV_TRACE5_AT(p, item, 2);
     const int n = sm.n;
-    const int x0 = s * p.L5;
-    const int x1 = min(x0 + p.L5, p.V);
-    const int nv = x0 < x1 ? (x1 - x0) / EPV : 0;
-    float best = 0.0f;
+    uint4 vc[VPT];
+    if (n == k) load_slice<E, VPT>(row_ptr(p, b, k, esize), x0, nv, vc);
+    float best = 0.0f, bval = 0.0f;
     int bidx = INT_MAX;
-    for (int i = 0; i < k; ++i) {
-      const uint4* vt = (const uint4*)(row_ptr(p, b, i, esize) + (size_t)x0 * esize);
-      const uint4* vd = (const uint4*)(row_ptr(p, b, k + 1 + i, esize) + (size_t)x0 * esize);
-      uint4 va[VPT], vb[VPT];
-#pragma unroll
-      for (int u = 0; u < VPT; ++u) {
-        const int j = tid + u * NT;
-        if (j < nv) {
-          va[u] = vt[j];
-          vb[u] = vd[j];
-        }
-      }
-      const float mt = sm.m[i], md = sm.m[k + 1 + i];
-      const float it = sm.invZ[i], id = sm.invZ[k + 1 + i];
-      const uint32_t tt = sm.thr[i], td = sm.thr[k + 1 + i];
-      float acc = 0.0f;
-#pragma unroll
-      for (int u = 0; u < VPT; ++u) {
-        const int j = tid + u * NT;
-        if (j < nv) {
-#pragma unroll
-          for (int g = 0; g < EPV; g += 4) {
-            float r4[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float lt = E::get(va[u], g + e), ld = E::get(vb[u], g + e);
-              const float pt = key_of<E>(lt) >= tt ? fexp2((lt - mt) * q.c) * it : 0.0f;
-              const float qd = key_of<E>(ld) >= td ? fexp2((ld - md) * q.c) * id : 0.0f;
-              acc += fminf(pt, qd);
-              r4[e] = pt - qd;
-            }
-            if (i == n) {
-              const int x = x0 + j * EPV + g;
-              const uint4 w4 = philox10(make_uint4((uint32_t)x >> 2, (uint32_t)b, (1u << 24) | (uint32_t)n, p.offset),
-                                        p.key0, p.key1);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                if (r4[e] > 0.0f) {
-                  const uint32_t word = e == 0 ? w4.x : e == 1 ? w4.y : e == 2 ? w4.z : w4.w;
-                  const float key = r4[e] / exp_race_E2(word);
-                  if (key > best) {
-                    best = key;
-                    bidx = x + e;
-                  }
-                }
-              }
-            }
-          }
-        }
-      }
-      acc = wave_sum(acc);
-      if (lane == 0) sm.wacc[i][wave] = acc;
-    }
+    if (q.trunc)
+      k5_positions<E, VPT, true>(p, sm, b, n, x0, nv, q.c, a0, b0, a1, b1, best, bidx, bval);
+    else
+      k5_positions<E, VPT, false>(p, sm, b, n, x0, nv, q.c, a0, b0, a1, b1, best, bidx, bval);
     if (n == k) {
       // bonus draw from p_k (verify stream), or the plain sampler's draw (its own stream)
       const bool smp = p.mode == MODE_SAMPLE;
       const uint32_t tag = smp ? 2u : 1u;
       const uint32_t sb = smp ? (uint32_t)(p.row_b ? p.row_b[b] : b) : (uint32_t)b;
       const uint32_t sj = smp ? (uint32_t)(p.row_pos ? p.row_pos[b] : 0) : (uint32_t)k;
-      const uint4* vt = (const uint4*)(row_ptr(p, b, k, esize) + (size_t)x0 * esize);
-      uint4 va[VPT];
-#pragma unroll
-      for (int u = 0; u < VPT; ++u) {
-        const int j = tid + u * NT;
-        if (j < nv) va[u] = vt[j];
-      }
-#pragma unroll
-      for (int u = 0; u < VPT; ++u) {
-        const int j = tid + u * NT;
-        if (j < nv) gumbel_row_partial<E>(va[u], x0 + j * EPV, sm.m[k], q.c, sm.thr[k], tag, sb, sj, p, best, bidx);
-      }
+      race_slice<E, VPT, false>(p, vc, vc, x0, nv, q.c, sm.m[k], 0.0f, sm.fthr[k], 0.0f, 0.0f, 0.0f, tag, sb, sj, best,
+                                bidx, bval);
     }
-    block_maxarg(sm.rs, best, bidx);  // its barriers also order the wacc writes before the reads below
+    SV_TRACE5_AT(p, item, 3);
+    block_race(sm.rs, best, bidx, bval);  // its barriers also order the wacc writes before the reads below
     FinalPart* fp = p.fin5 + (size_t)b * p.S5 + s;
     if (tid < k) {
       float v = 0.0f;
@@ -1212,21 +1347,33 @@ __global__ __launch_bounds__(NT) void k5_verify(Params p) {
     if (tid == 0) {
       stf(&fp->key, best);
       st32(&fp->idx, (uint32_t)bidx);
+      stf(&fp->val, bval);
     }
   }
+  SV_TRACE5_AT(p, item, 4);
   if (arrive_last(&p.cnt5[b], (uint32_t)p.S5, &sm.rs.flag)) {
+    SV_TRACE5_AT(p, item, 5);
     k5_finalize<E>(p, sm, b, ok, q);
     if (tid == 0) atomicExch(&p.cnt5[b], 0u);
+    SV_TRACE5_AT(p, item, 6);
   }
+  SV_TRACE5_AT(p, item, 7);
+}
+
+template <class E, int VPT>
+__global__ __launch_bounds__(NT) void k5_verify(Params p) {
+  __shared__ K5Smem sm;
+  int b, s;
+  item_rs(blockIdx.x, p.B, p.S5, b, s);
+  k5_item<E, VPT>(p, sm, blockIdx.x, b, s);
 }
 
 // ---------------------------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------------------------
 struct Geo {
-  int rows, R, S1, S3, S5, L1, L3, L5, esize, EPV;
-  size_t off_cnt1, off_cnt3, off_cnt5, off_st1, off_hw1, off_hb1, off_rinfo, off_fp3, off_fc3, off_fin5, off_trace,
-      total;
+  int rows, R, S1, S5, L1, L5, esize, EPV;
+  size_t off_cnt1, off_cnt5, off_st1, off_hw1, off_hc1, off_rinfo, off_fin5, off_trace, off_trace5, total;
 };
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -1238,13 +1385,11 @@ static bool make_geo(int32_t B, int32_t k, int32_t V, spec_dtype_t dtype, Geo& g
   g.EPV = 16 / g.esize;
   if (V % g.EPV != 0) return false;
   g.rows = 2 * k + 1;
-  if ((long long)B * g.rows > (1 << 24)) return false;  // grids stay below 2^31 workgroups
+  if ((long long)B * g.rows > (1 << 24)) return false;  // item counts stay below 2^31
   g.R = B * g.rows;
   g.L1 = NT * g.EPV * VPT1;
-  g.L3 = NT * g.EPV * VPT3;
   g.L5 = NT * g.EPV * VPT5;
   g.S1 = (V + g.L1 - 1) / g.L1;
-  g.S3 = (V + g.L3 - 1) / g.L3;
   g.S5 = (V + g.L5 - 1) / g.L5;
   const size_t R = (size_t)g.R;
   size_t off = 256;
@@ -1253,73 +1398,88 @@ static bool make_geo(int32_t B, int32_t k, int32_t V, spec_dtype_t dtype, Geo& g
     off = align_up(off + bytes, 256);
   };
   take(g.off_cnt1, R * 4);
-  take(g.off_cnt3, R * 4);
   take(g.off_cnt5, (size_t)B * 4);
   take(g.off_st1, R * g.S1 * sizeof(StatPart));
-  take(g.off_hw1, R * g.S1 * (WTOP / 2) * 4);
-  take(g.off_hb1, R * g.S1 * (NB / 2 + NB + 1) * 4);
+  const bool bf = dtype == SPEC_DTYPE_BF16;  // per-code and weight-bin partials: bf16 rows only
+  take(g.off_hw1, bf ? R * g.S1 * (WTOP / 2) * 4 : 0);
+  take(g.off_hc1, bf ? R * g.S1 * HCW * 4 : 0);
   take(g.off_rinfo, R * sizeof(RowInfo));
-  take(g.off_fp3, R * g.S3 * sizeof(FinePart));
-  take(g.off_fc3, R * g.S3 * (WF / 2) * 4);
   take(g.off_fin5, (size_t)B * g.S5 * sizeof(FinalPart));
   take(g.off_trace, R * g.S1 * TRACE_SLOTS * 8);
+  take(g.off_trace5, (size_t)B * g.S5 * TRACE_SLOTS * 8);
   g.total = off;
   return true;
 }
 
 struct DevInfo {
   int state;  // 0 unknown, 1 gfx950, 2 other
+  int cus;    // compute units
 };
 static DevInfo g_dev[MAXDEV];
 static std::mutex g_mu;
+static hipEvent_t g_prof[2 * NKERN];  // benchmark hook: events around each kernel (all null: off)
 
-static bool device_ok(int dev) {
+static bool device_ok(int dev, int& cus) {
   if (dev < 0 || dev >= MAXDEV) return false;
   std::lock_guard<std::mutex> lk(g_mu);
   if (g_dev[dev].state == 0) {
     hipDeviceProp_t pr;
     if (hipGetDeviceProperties(&pr, dev) != hipSuccess) return false;
     g_dev[dev].state = (std::strncmp(pr.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_dev[dev].cus = pr.multiProcessorCount > 0 ? pr.multiProcessorCount : 256;
   }
+  cus = g_dev[dev].cus;
   return g_dev[dev].state == 1;
 }
 
+static void prof_mark(int idx, hipStream_t st) {
+  if (g_prof[idx]) (void)hipEventRecord(g_prof[idx], st);
+}
+
+// Persistent grid: one workgroup per resident slot, a multiple of 8 (one per XCD), no more than items.
+static unsigned grid_for(long long items, int cus, int occ) {
+  long long g = std::min(items, (long long)cus * occ);
+  if (g >= 8) g &= ~7ll;
+  return (unsigned)std::max(g, 1ll);
+}
+
 template <class E>
-static void enqueue(const Params& p, hipStream_t st) {
-  hipLaunchKernelGGL((k1_stats<E, VPT1>), dim3((unsigned)p.S1 * p.R), dim3(NT), 0, st, p);
-  hipLaunchKernelGGL((k3_fine<E, VPT3>), dim3((unsigned)p.S3 * p.R), dim3(NT), 0, st, p);
-  hipLaunchKernelGGL((k5_verify<E, VPT5>), dim3((unsigned)p.S5 * p.B), dim3(NT), 0, st, p);
+static void enqueue(const Params& p, int cus, hipStream_t st) {
+  static_assert(WTOP / 2 == NT && NBC == NT, "K1 assumes one histogram word pair per thread");
+  (void)cus;
+  prof_mark(0, st);
+  hipLaunchKernelGGL((k1_stats<E, VPT1>), dim3((unsigned)(p.R * p.S1)), dim3(NT), 0, st, p);
+  prof_mark(1, st);
+  prof_mark(2, st);
+  hipLaunchKernelGGL((k5_verify<E, VPT5>), dim3((unsigned)(p.B * p.S5)), dim3(NT), 0, st, p);
+  prof_mark(3, st);
 }
 
 static spec_status_t launch(Params& p, const Geo& g, spec_dtype_t dtype, void* workspace, size_t workspace_bytes,
                             void* stream) {
   if (!workspace || workspace_bytes < g.total || ((uintptr_t)workspace & 15)) return SPEC_ERR_WORKSPACE;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || !device_ok(dev)) return SPEC_ERR_UNSUPPORTED_DEVICE;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || !device_ok(dev, cus)) return SPEC_ERR_UNSUPPORTED_DEVICE;
   p.rows = g.rows;
   p.R = g.R;
   p.S1 = g.S1;
-  p.S3 = g.S3;
   p.S5 = g.S5;
   p.L1 = g.L1;
-  p.L3 = g.L3;
   p.L5 = g.L5;
   uint8_t* ws = (uint8_t*)workspace;
   p.cnt1 = (uint32_t*)(ws + g.off_cnt1);
-  p.cnt3 = (uint32_t*)(ws + g.off_cnt3);
   p.cnt5 = (uint32_t*)(ws + g.off_cnt5);
   p.st1 = (StatPart*)(ws + g.off_st1);
   p.hw1 = (uint32_t*)(ws + g.off_hw1);
-  p.hb1 = (uint32_t*)(ws + g.off_hb1);
+  p.hc1 = (uint32_t*)(ws + g.off_hc1);
   p.rinfo = (RowInfo*)(ws + g.off_rinfo);
-  p.fp3 = (FinePart*)(ws + g.off_fp3);
-  p.fc3 = (uint32_t*)(ws + g.off_fc3);
   p.fin5 = (FinalPart*)(ws + g.off_fin5);
   p.trace = TRACE_SLOTS > 0 ? (unsigned long long*)(ws + g.off_trace) : nullptr;
+  p.trace5 = TRACE_SLOTS > 0 ? (unsigned long long*)(ws + g.off_trace5) : nullptr;
   if (dtype == SPEC_DTYPE_BF16)
-    enqueue<BF16>(p, (hipStream_t)stream);
+    enqueue<BF16>(p, cus, (hipStream_t)stream);
   else
-    enqueue<F32>(p, (hipStream_t)stream);
+    enqueue<F32>(p, cus, (hipStream_t)stream);
   if (hipGetLastError() != hipSuccess) return SPEC_ERR_LAUNCH;
   return SPEC_OK;
 }
@@ -1414,4 +1574,14 @@ extern "C" spec_status_t spec_sample(const void* logits, spec_dtype_t dtype, con
   p.tokens = tokens;
   p.logprobs = logprobs;
   return launch(p, g, dtype, workspace, workspace_bytes, stream);
+}
+
+extern "C" spec_status_t spec_set_kernel_events(void* const* events, int32_t count) {
+  if (events == nullptr) {
+    for (auto& e : g_prof) e = nullptr;
+    return SPEC_OK;
+  }
+  if (count != 2 * NKERN) return SPEC_ERR_INVALID_ARGUMENT;
+  for (int j = 0; j < 2 * NKERN; ++j) g_prof[j] = (hipEvent_t)events[j];
+  return SPEC_OK;
 }

@@ -35,16 +35,57 @@ struct F32 {
   __device__ static inline float load1(const void* row, int x) { return ((const float*)row)[x]; }
 };
 
-// Order-preserving unsigned key of a float (-0 canonicalised to +0); bf16 values use the top 16 bits.
+// Order-preserving unsigned keys (larger value -> larger key; -0 and +0 share one key; key 0 never
+// occurs for a bf16 value, so a threshold key of 0 can mean "keep everything").
+//   fp32:  key32(f) = f >= 0 ? bits | 2^31 : ~bits                  (-0 canonicalised to +0 first)
+//   bf16:  key16(h) = h | 0x8000 for h < 0x8000 (+0 -> 0x8000), (2^16 - h) mod 2^16 otherwise
+//          (-0 -> 0x8000, the smallest negative -> 0x7fff, -inf 0xff80 -> 0x0080)
 __device__ inline uint32_t key32(float f) {
   uint32_t u = __float_as_uint(f);
   if (u == 0x80000000u) u = 0;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+__device__ inline uint32_t key16(uint32_t h) { return (h & 0x8000u) ? ((0u - h) & 0xffffu) : (h | 0x8000u); }
+__device__ inline uint32_t key16f(float f) { return key16(__float_as_uint(f) >> 16); }
+
+// key16 of both bf16 halves of a 32-bit word at once (packed 16-bit operations).
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t key16x2(uint32_t w) {
+  const s16x2 h = __builtin_bit_cast(s16x2, w);
+  const uint32_t sgn = __builtin_bit_cast(uint32_t, (s16x2)(h >> (short)15));  // 0xffff in negative halves
+  const uint32_t neg = __builtin_bit_cast(uint32_t, (u16x2)((u16x2)0 - __builtin_bit_cast(u16x2, w)));
+  const uint32_t pos = w | 0x80008000u;
+  return (neg & sgn) | (pos & ~sgn);
+}
+// Per-half difference a - b modulo 2^16.
+__device__ inline uint32_t sub16x2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, (u16x2)(__builtin_bit_cast(u16x2, a) - __builtin_bit_cast(u16x2, b)));
+}
+// Per-half minimum.
+__device__ inline uint32_t min16x2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
+}
+
 template <class E>
 __device__ inline uint32_t key_of(float f) {
-  return E::KEYBITS == 16 ? (key32(f) >> 16) : key32(f);
+  return E::KEYBITS == 16 ? key16f(f) : key32(f);
 }
+// Value of a key (inverse of key_of); used for keys of values that occur, so never NaN.
+__device__ inline float key16_value(uint32_t k) {
+  const uint32_t h = (k & 0x8000u) ? (k & 0x7fffu) : ((0x10000u - k) & 0xffffu);
+  return __uint_as_float(h << 16);
+}
+__device__ inline float key32_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+template <class E>
+__device__ inline float key_value(uint32_t k) {
+  return E::KEYBITS == 16 ? key16_value(k) : key32_value(k);
+}
+
+// NaN-propagating maximum (v_maximum3_f32 on gfx950): a NaN anywhere in a row reaches its maximum.
+__device__ inline float nan_max(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 // ---------------------------------------------------------------------------------------------
 // Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11).  The multiplies map to v_mad_u64_u32.

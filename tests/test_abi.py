@@ -48,6 +48,13 @@ def test_workspace_sizes(L):
     assert L.spec_sample_workspace_size(16, 4096, 0) > 0
 
 
+def test_kernel_event_hook_arguments(L):
+    """The benchmark hook checks its count, and NULL turns it off."""
+    assert L.spec_set_kernel_events(None, 0) == 0
+    arr = (ctypes.c_void_p * 3)()
+    assert L.spec_set_kernel_events(arr, 3) == 1
+
+
 def test_status_strings(L):
     for s in range(5):
         assert L.spec_verify_status_string(s)
