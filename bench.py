@@ -60,7 +60,15 @@ def main():
     ap.add_argument("--config", default="3", help="workload: 1, 2, 3, 4a, 4b, 5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB, 5 times (PMC calibration)")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="summarise rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of this benchmark and of the copy "
+                         "probe into profiles/traffic_config<C>.json (no GPU needed)")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
@@ -72,6 +80,15 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 5}), flush=True)
+        return
     w = W.CONFIGS[args.config]()
     B, k, V = w.B, w.k, w.V
     bf16 = w.dtype == "bf16"
@@ -171,6 +188,54 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, drafts.cpu().numpy(), args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def _pmc_per_kernel(run_dir, counter):
+    """Mean value of one counter per kernel name over the dispatches of a rocprofv3 --pmc CSV run."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    vals = {}
+    for r in csv.DictReader(open(files[0])):
+        if r.get("Counter_Name") != counter:
+            continue
+        name = r.get("Kernel_Name", "").split("(")[0]
+        vals.setdefault(name, []).append(float(r["Counter_Value"]))
+    return {k: (float(np.mean(v)), len(v)) for k, v in vals.items()}
+
+
+def pmc_summary(args):
+    """HBM traffic of the statistics kernel from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by
+    the ratio of true bytes to the same counter's reading for a plain copy kernel of known size."""
+    fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.pmc_summary
+    copy_bytes = (args.copy_probe_mb or 256) << 20
+
+    def copy_kernel(d):
+        # the largest-reading kernel of the copy-probe run is the probe's copy
+        return max(d.items(), key=lambda kv: kv[1][0])
+
+    cf_name, (cf_kib, _) = copy_kernel(_pmc_per_kernel(cfetch_dir, "FETCH_SIZE"))
+    cw_name, (cw_kib, _) = copy_kernel(_pmc_per_kernel(cwrite_dir, "WRITE_SIZE"))
+    f_scale = copy_bytes / (cf_kib * 1024.0)
+    w_scale = copy_bytes / (cw_kib * 1024.0)
+    fetch = _pmc_per_kernel(fetch_dir, "FETCH_SIZE")
+    write = _pmc_per_kernel(write_dir, "WRITE_SIZE")
+    out = {"config": args.config, "kernel_digest": kernel_digest(), "copy_probe_bytes": copy_bytes,
+           "copy_kernel": cf_name, "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
+    for name, (kib, n) in fetch.items():
+        if "sv::" not in name:
+            continue
+        wk = write.get(name, (0.0, 0))[0]
+        out["kernels"][name] = {"fetch_kib_raw": kib, "write_kib_raw": wk, "dispatches": n,
+                                "fetch_bytes": kib * 1024.0 * f_scale, "write_bytes": wk * 1024.0 * w_scale}
+    k1 = [v for k, v in out["kernels"].items() if "k1_stats" in k]
+    out["bytes_per_launch"] = (k1[0]["fetch_bytes"] + k1[0]["write_bytes"]) if k1 else None
+    path = os.path.join(ROOT, "profiles", f"traffic_config{args.config}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def kernel_durations(sv, step, n, stream):
