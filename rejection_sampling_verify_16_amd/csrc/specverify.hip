@@ -50,7 +50,7 @@ constexpr int MODE_SAMPLE = 1;  // plain sampler: k = 0, one logit row per batch
 constexpr int MAXDEV = 64;
 constexpr int VPT1 = 8;         // K1: 16-byte vectors per thread per slice
 constexpr int VPT5 = 2;         // K5
-constexpr int OCC1 = 8;         // K1 workgroups per CU (register budget of its launch bounds)
+constexpr int OCC1 = 7;         // K1 workgroups per CU (register budget of its launch bounds)
 constexpr int OCC5 = 4;         // K5 workgroups per CU
 constexpr int FVPT = 2;         // whole-row passes of one workgroup: vectors per thread per step
 constexpr int WTOP = 512;       // K1: exact per-code window below the slice max
@@ -62,7 +62,14 @@ constexpr int MB = 8;           // merge: slices whose histogram words are loade
 constexpr int HCW = NBC / 2 + 1;  // words per slice of packed bin counts + the slice's base bin
 constexpr int NKERN = 2;        // kernels per call
 
-constexpr uint32_t ST_BAD = 1u;  // NaN / +inf entries, or every entry -inf
+constexpr int WC = 64;          // K1: candidate window (codes below the slice max) of truncated rows
+constexpr int NC = 128;         // K1: candidates recorded per slice at most
+constexpr int NFLAG = 128;      // K1: staged candidate-holding vectors per slice at most
+constexpr int KMAX = 1024;      // kept entries per row at most for the candidate (sparse) path of K5
+constexpr int HT = 2048;        // K5 sparse path: hash table entries (power of two, > KMAX)
+
+constexpr uint32_t ST_BAD = 1u;     // NaN / +inf entries, or every entry -inf
+constexpr uint32_t ST_SPARSE = 2u;  // every kept entry is among the row's recorded candidates
 
 struct StatPart {  // K1, per (logit row, slice)
   float m;         // slice max (NaN if the slice holds a NaN, for non-greedy rows)
@@ -114,6 +121,8 @@ struct Params {
   StatPart* st1;      // [R][S1]
   uint32_t* hw1;      // [R][S1][WTOP/2] packed 16-bit code counts
   uint32_t* hc1;      // [R][S1][HCW] packed 16-bit bin counts, then the slice's base bin (float)
+  unsigned long long* cand1;  // [R][S1][NC] candidates of truncated rows: index << 16 | bf16 bits
+  uint32_t* ncand1;   // [R][S1] candidates found per slice (may exceed NC: then the list is incomplete)
   RowInfo* rinfo;     // [R]
   FinalPart* fin5;    // [B][S5]
   unsigned long long* trace;   // K1 phase timestamps per item: instrumented builds only
@@ -289,6 +298,19 @@ __device__ void block_maxarg(RedSmem& rs, float& m, int& a) {
   a = rs.i[0];
   for (int w = 1; w < NWAVE; ++w) maxarg_combine(m, a, rs.f[w], rs.i[w]);
   __syncthreads();
+}
+
+// Workgroup sum into every thread.
+__device__ uint32_t block_sum_u32(RedSmem& rs, uint32_t v) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if (lane == 0) rs.u[wave] = v;
+  __syncthreads();
+  uint32_t t = 0;
+  for (int w = 0; w < NWAVE; ++w) t += rs.u[w];
+  __syncthreads();
+  return t;
 }
 
 // Lowest thread index whose predicate holds, into every thread (NT if none).
@@ -536,9 +558,15 @@ struct K1Smem {
     struct {                    // streaming phase; entries past WTOP / NBC absorb out-of-range
       uint32_t hw[WTOP + 64];   // logits, one per lane, so the atomics need no branch
       uint32_t hc[NBC + 64];
+      unsigned long long cand[NC];  // logits within WC codes of the slice max: index << 16 | bits
+      uint32_t ncand;
+      uint4 fvec[NFLAG];        // staged vectors that hold a candidate, and their vector indices
+      uint32_t fidx[NFLAG];
+      uint32_t nflag;
     } st;
     struct {               // merge phase
       uint32_t keyms[MAXS1];  // slice max keys
+      uint32_t ncs[MAXS1];    // slice candidate counts
       float cbs[MAXS1];       // slice base bins
       uint32_t bc[NBC];       // merged weight-bin counts (row-relative)
       uint32_t cnt[WF];       // merged per-code counts: the top codes, later the exact window
@@ -672,6 +700,7 @@ __device__ void k1_merge(const Params& p, K1Smem& sm, int r, int b, int i, const
     sum = ldf(&sp->s);
     fl = ld32(&sp->flags);
     if (tid == sg) sm.win[1] = ld32(&sp->g);
+    if (hist) sm.u.mg.ncs[tid] = ld32(&p.ncand1[(size_t)r * S + tid]);
   }
   uint32_t hwv[MB];
   if (hist) {
@@ -689,6 +718,7 @@ __device__ void k1_merge(const Params& p, K1Smem& sm, int r, int b, int i, const
   const bool bad = fl != 0 || !(m > -INFINITY) || m == INFINITY;
   uint32_t thr = 0;
   float Z = sum;
+  bool sparse = false;
   if (!bad && q.trunc) {
     bool done = false;
     const double ztot = (double)sum * 0x1p40;
@@ -721,6 +751,13 @@ __device__ void k1_merge(const Params& p, K1Smem& sm, int r, int b, int i, const
         thr = keym - (uint32_t)sel;
         Z = (float)((double)zsel * 0x1p-40);
         done = true;
+        // Candidate (sparse) path of K5: every slice recorded all its logits within WC codes of its max,
+        // so it recorded every kept one if its max is within WC codes of the threshold; the kept set must
+        // also be small.
+        const uint32_t kept = block_sum_u32(sm.rs, (tid <= sel ? cnt[tid] : 0u) + (tid + NT <= sel ? cnt[tid + NT] : 0u));
+        const bool slice_ok = tid >= S || (sm.u.mg.ncs[tid] <= (uint32_t)NC && sm.u.mg.keyms[tid] < thr + (uint32_t)WC);
+        const bool all_slices = __syncthreads_and(slice_ok) != 0;
+        sparse = kept <= (uint32_t)KMAX && all_slices;
       } else if (coarse) {
         // merged weight bins, row-relative: slice bin j is row bin cbs[s] + j - A_m
         const float Am = floorf(-m * (q.c * BRC));
@@ -759,34 +796,79 @@ __device__ void k1_merge(const Params& p, K1Smem& sm, int r, int b, int i, const
     ri->Z = Z;
     ri->lz = __builtin_amdgcn_logf(Z);
     ri->fthr = thr == 0 ? -INFINITY : key_value<E>(thr);
-    ri->state = bad ? ST_BAD : 0u;
+    ri->state = bad ? ST_BAD : (sparse ? ST_SPARSE : 0u);
     ri->Ztot = sum;
     ri->gath = sg >= 0 ? __uint_as_float(sm.win[1]) : 0.0f;
     atomicExch(&p.cnt1[r], 0u);
   }
 }
 
+// 16-byte vector u (runtime index) of a per-thread slice held in registers.
+template <int VPT>
+__device__ inline uint4 pick_vec(const uint4 (&v)[VPT], int u) {
+  uint4 r = v[0];
+#pragma unroll
+  for (int t = 1; t < VPT; ++t)
+    if (u == t) r = v[t];
+  return r;
+}
+
+// Slots for a wave: every lane asks for cnt < 16 consecutive slots of an LDS counter; one atomic per
+// wave reserves them all, and each lane gets its first slot (lanes in order).  All lanes of the wave
+// must be active.
+__device__ inline uint32_t wave_reserve(uint32_t* counter, uint32_t cnt) {
+  uint32_t excl = 0, total = 0;
+#pragma unroll
+  for (int bit = 0; bit < 4; ++bit) {
+    const unsigned long long mk = __ballot((cnt >> bit) & 1u);
+    excl += __builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u)) << bit;
+    total += (uint32_t)__popcll(mk) << bit;
+  }
+  uint32_t base = 0;
+  if (total != 0 && (threadIdx.x & 63) == 0) base = atomicAdd(counter, total);
+  return __builtin_amdgcn_readfirstlane(base) + excl;
+}
+
+// Bit e set: entry e of a bf16 vector lies within WC codes of the slice max (keyms2: its key in both
+// halves); key distances are taken as in the histogram pass.
+__device__ inline uint32_t cand_bits(const uint4& v, uint32_t keyms2) {
+  const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+  uint32_t bits = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t d2 = sub16x2(keyms2, key16x2(wv[q]));
+    bits |= ((d2 & 0xffffu) < (uint32_t)WC ? 1u : 0u) << (2 * q);
+    bits |= ((d2 >> 16) < (uint32_t)WC ? 1u : 0u) << (2 * q + 1);
+  }
+  return bits;
+}
+
 // Histogram pass of a truncated bf16 slice (values held in registers), relative to the slice max ms:
 // per-code counts of the WTOP codes below ms; top-p-only rows also add the normaliser sum and the
 // weight-bin counts (bin floor(-l c BRC) - cbase).  Out-of-range entries go to a per-lane spare bin.
 template <int VPT, bool TOPP_ONLY>
-__device__ void k1_hist(K1Smem& sm, const uint4 (&v)[VPT], int nv, float ms, float c, float cbase, float& sum) {
+__device__ void k1_hist(K1Smem& sm, const uint4 (&v)[VPT], int nv, int x0, float ms, float c, float cbase,
+                        float& sum) {
   const int tid = threadIdx.x;
   const uint32_t lane = tid & 63;
-  const uint32_t keyms2 = key16f(ms) * 0x10001u;
+  const uint32_t keyms = key16f(ms);
+  const uint32_t keyms2 = keyms * 0x10001u;
   const uint32_t spare2 = (WTOP + lane) * 0x10001u;
   const uint32_t spare_c = NBC + lane;
   const float cb = c * BRC;
+  uint32_t cmask = 0;  // bit u: vector u holds a candidate (an entry within WC codes of the slice max)
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
     const int j = tid + u * NT;
     if (j < nv) {
       const uint32_t wv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      uint32_t dmin = 0xffffffffu;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const uint32_t d2 = min16x2(sub16x2(keyms2, key16x2(wv[q])), spare2);
         atomicAdd(&sm.u.st.hw[d2 & 0xffffu], 1u);
         atomicAdd(&sm.u.st.hw[d2 >> 16], 1u);
+        dmin = min16x2(dmin, d2);
         if (TOPP_ONLY) {
           const float f0 = __uint_as_float(wv[q] << 16), f1 = __uint_as_float(wv[q] & 0xffff0000u);
           sum += fexp2((f0 - ms) * c);
@@ -796,6 +878,44 @@ __device__ void k1_hist(K1Smem& sm, const uint4 (&v)[VPT], int nv, float ms, flo
           atomicAdd(&sm.u.st.hc[j0], 1u);
           atomicAdd(&sm.u.st.hc[j1], 1u);
         }
+      }
+      if (min(dmin & 0xffffu, dmin >> 16) < (uint32_t)WC) cmask |= 1u << u;
+    }
+  }
+  // Candidates: the logits within WC codes of the slice max (index and raw bits).  The vectors flagged
+  // above are staged in LDS, then one thread per staged vector appends its candidates.  More than
+  // NFLAG staged vectors, or more than NC candidates, leave ncand above NC: the slice then has no
+  // usable candidate list.
+  if (__ballot(cmask != 0) != 0) {
+    uint32_t at = wave_reserve(&sm.u.st.nflag, (uint32_t)__popc(cmask));
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      if (cmask & (1u << u)) {
+        if (at < (uint32_t)NFLAG) {
+          sm.u.st.fvec[at] = v[u];
+          sm.u.st.fidx[at] = (uint32_t)(tid + u * NT);
+        }
+        ++at;
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t nflag = sm.u.st.nflag;
+  if (nflag > (uint32_t)NFLAG) {
+    if (tid == 0) sm.u.st.ncand = NC + 1;
+  } else if ((uint32_t)(tid & ~63) < nflag) {  // waves holding a staged vector
+    const bool mine = (uint32_t)tid < nflag;
+    const uint4 vv = mine ? sm.u.st.fvec[tid] : make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t bits = mine ? cand_bits(vv, keyms2) : 0u;
+    const int xb = x0 + (mine ? (int)sm.u.st.fidx[tid] : 0) * BF16::EPV;
+    uint32_t c = wave_reserve(&sm.u.st.ncand, (uint32_t)__popc(bits));
+    const uint32_t wv[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+    for (int e = 0; e < BF16::EPV; ++e) {
+      if (bits & (1u << e)) {
+        const uint32_t h = (e & 1) ? (wv[e >> 1] >> 16) : (wv[e >> 1] & 0xffffu);
+        if (c < (uint32_t)NC) sm.u.st.cand[c] = ((unsigned long long)(xb + e) << 16) | h;
+        ++c;
       }
     }
   }
@@ -878,18 +998,28 @@ __device__ void k1_item(const Params& p, K1Smem& sm, int item, int r, int s) {
       sm.u.st.hw[tid] = 0;
       sm.u.st.hw[tid + NT] = 0;
       if (topp_only) sm.u.st.hc[tid] = 0;
+      if (tid == 0) {
+        sm.u.st.ncand = 0;
+        sm.u.st.nflag = 0;
+      }
       const float ms = block_nan_max(sm.rs, m);
       const float cbase = floorf(-ms * (q.c * BRC));
       if (ms > -INFINITY && ms < INFINITY) {  // not NaN, +inf or an all -inf slice
         if (topp_only)
-          k1_hist<VPT, true>(sm, v, nv, ms, q.c, cbase, sum);
+          k1_hist<VPT, true>(sm, v, nv, x0, ms, q.c, cbase, sum);
         else
-          k1_hist<VPT, false>(sm, v, nv, ms, q.c, cbase, sum);
+          k1_hist<VPT, false>(sm, v, nv, x0, ms, q.c, cbase, sum);
       }
       m = ms;  // the sums above are relative to the slice max
       __syncthreads();
       uint32_t* hw = p.hw1 + ((size_t)r * p.S1 + s) * (WTOP / 2);
       st32(&hw[tid], sm.u.st.hw[2 * tid] | (sm.u.st.hw[2 * tid + 1] << 16));  // WTOP / 2 == NT
+      const uint32_t nc = sm.u.st.ncand;
+      if (tid < (int)min(nc, (uint32_t)NC)) {
+        unsigned long long* cd = p.cand1 + ((size_t)r * p.S1 + s) * NC + tid;
+        __hip_atomic_store(cd, sm.u.st.cand[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (tid == 0) st32(&p.ncand1[(size_t)r * p.S1 + s], nc);
       if (topp_only) {
         uint32_t* hc = p.hc1 + ((size_t)r * p.S1 + s) * HCW;
         if (tid < NBC / 2) st32(&hc[tid], sm.u.st.hc[2 * tid] | (sm.u.st.hc[2 * tid + 1] << 16));
@@ -935,6 +1065,11 @@ struct K5Smem {
   float u[MAXK];
   float wacc[MAXK][NWAVE];
   int32_t n;
+  // sparse path
+  int32_t hidx[HT];
+  float hlq[HT];
+  uint32_t ncs[MAXS1], ncs2[MAXS1];  // candidate counts per slice: target row, draft row
+  unsigned long long asum[NWAVE];
 };
 
 // p(x) = exp2((l - m) c - log2 Z) on the kept entries, 0 below the kept threshold.
@@ -1128,16 +1263,6 @@ __device__ inline void load_slice(const uint8_t* row, int x0, int nv, uint4 (&v)
   }
 }
 
-// 16-byte vector u (runtime index) of a per-thread slice held in registers.
-template <int VPT>
-__device__ inline uint4 pick_vec(const uint4 (&v)[VPT], int u) {
-  uint4 r = v[0];
-#pragma unroll
-  for (int t = 1; t < VPT; ++t)
-    if (u == t) r = v[t];
-  return r;
-}
-
 // Gumbel-max race over the 4-entry groups of a slice held in registers, one vector at a time (the
 // Philox rounds of different groups are not interleaved, which keeps register use flat).  Weights:
 // RESID: r(x) = max(p(x) - q(x), 0) of a target / draft pair; otherwise w(x) = exp2((l - m) c) on the
@@ -1258,6 +1383,193 @@ __device__ void k5_positions(const Params& p, K5Smem& sm, int b, int n, int x0, 
 }
 
 // One K5 work item: slice s of batch row b.
+// ---------------------------------------------------------------------------------------------
+// K5 candidate (sparse) path: a truncated batch row whose every logit row kept at most KMAX entries,
+// all of them among the candidates K1 recorded, is finished from those candidates, one workgroup per
+// draft position: the same weights, accept chain, alpha and Philox race keys as the streaming path,
+// without re-reading the rows.  bf16 rows only.
+// ---------------------------------------------------------------------------------------------
+
+// Loads row r's candidate slots (slice s, entry e < count) with key >= thr: thread t takes slots t,
+// t + NT, ... of the S x NC slot grid from base on; all of a thread's loads are issued before any is
+// used.  Empty or filtered slots get index 0xffffffff.
+template <int NSLOT>
+__device__ inline void sparse_load(const Params& p, const uint32_t* ncs, int r, uint32_t thr, uint32_t (&xs)[NSLOT],
+                                   float (&fs)[NSLOT], int base) {
+  const int tid = threadIdx.x, S = p.S1;
+  unsigned long long c[NSLOT];
+#pragma unroll
+  for (int t = 0; t < NSLOT; ++t) {
+    const int g = base + tid + t * NT, sl = g / NC, e = g - sl * NC;
+    c[t] = (sl < S && (uint32_t)e < min(ncs[sl], (uint32_t)NC))
+               ? __hip_atomic_load(p.cand1 + ((size_t)r * S + sl) * NC + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+               : ~0ull;  // no slot (a recorded candidate has an index below 2^20)
+  }
+#pragma unroll
+  for (int t = 0; t < NSLOT; ++t) {
+    const float f = __uint_as_float((uint32_t)(c[t] & 0xffffu) << 16);
+    const bool keep = c[t] != ~0ull && key16f(f) >= thr;
+    xs[t] = keep ? (uint32_t)(c[t] >> 16) : 0xffffffffu;
+    fs[t] = f;
+  }
+}
+
+__device__ inline uint32_t hslot(uint32_t x) { return (x * 2654435761u) >> (32 - 11); }  // HT == 2^11
+__device__ inline uint32_t thr_key(float fthr) { return fthr == -INFINITY ? 0u : key16f(fthr); }
+
+// Race over target candidates with weights exp2((l - m) c) (a plain draw from that row's kept set).
+template <int NSLOT>
+__device__ inline void sparse_plain_race(const Params& p, const uint32_t (&xs)[NSLOT], const float (&fs)[NSLOT],
+                                         float m, float c, uint32_t tag, uint32_t sb, uint32_t sj, float& best,
+                                         int& bidx, float& bval) {
+#pragma unroll
+  for (int t = 0; t < NSLOT; ++t) {
+    if (xs[t] == 0xffffffffu) continue;
+    const float w = fexp2((fs[t] - m) * c);
+    if (w > 0.0f) {
+      const uint4 w4 = philox10(make_uint4(xs[t] >> 2, sb, (tag << 24) | sj, p.offset), p.key0, p.key1);
+      const uint32_t qq = xs[t] & 3u;
+      race_take(best, bidx, bval, race_key(w, qq == 0 ? w4.x : qq == 1 ? w4.y : qq == 2 ? w4.z : w4.w), (int)xs[t],
+                fs[t]);
+    }
+  }
+}
+
+// Position i of a candidate-path batch row (one workgroup per position): alpha_i for i < k, and the
+// token draw where this position is the one that draws (the first rejection n, or the bonus position
+// k when every draft was accepted), with the row's outputs.
+template <class E>
+__device__ void k5_sparse(const Params& p, K5Smem& sm, int b, int n, int i, const RowParams& q) {
+  constexpr int NSLOT = 4;  // slots per thread per pass: NT * NSLOT = 1024 slots
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int k = p.k, S = p.S1;
+  const int nslots = S * NC;
+  const bool pair = i < k;
+  const bool draw = pair ? i == n : n == k;
+  if (!pair && !draw) return;
+  const int rt = i, rd = k + 1 + i;
+  const int Rt = b * p.rows + rt, Rd = b * p.rows + rd;
+  // candidate counts of both rows in one round trip; the index -> log2 q table cleared meanwhile
+  if (tid < S) sm.ncs[tid] = ld32(&p.ncand1[(size_t)Rt * S + tid]);
+  if (pair && tid >= 64 && tid < 64 + S) sm.ncs2[tid - 64] = ld32(&p.ncand1[(size_t)Rd * S + tid - 64]);
+  if (pair)
+    for (int j = tid; j < HT; j += NT) sm.hidx[j] = -1;
+  __syncthreads();
+  const float mt = sm.m[rt], lt = sm.lz[rt];
+  const uint32_t kt = thr_key(sm.fthr[rt]);
+  uint32_t xt[NSLOT];
+  float ft[NSLOT];
+  sparse_load<NSLOT>(p, sm.ncs, Rt, kt, xt, ft, 0);  // first pass of the target row, in flight with the draft's
+  if (pair) {
+    const float md = sm.m[rd], ld = sm.lz[rd];
+    const uint32_t kd = thr_key(sm.fthr[rd]);
+    for (int base = 0; base < nslots; base += NT * NSLOT) {
+      uint32_t xs[NSLOT];
+      float fs[NSLOT];
+      sparse_load<NSLOT>(p, sm.ncs2, Rd, kd, xs, fs, base);
+#pragma unroll
+      for (int t = 0; t < NSLOT; ++t) {
+        if (xs[t] == 0xffffffffu) continue;
+        uint32_t h = hslot(xs[t]);
+        for (int probe = 0; probe < HT; ++probe) {  // bounded: the table holds at most KMAX < HT entries
+          const int prev = atomicCAS(&sm.hidx[h], -1, (int)xs[t]);
+          if (prev == -1 || prev == (int)xs[t]) {
+            sm.hlq[h] = fmaf(fs[t] - md, q.c, -ld);
+            break;
+          }
+          h = (h + 1) & (HT - 1);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // target kept entries: alpha (2^40 fixed point: the candidates' slot order varies from call to call,
+  // and this sum does not depend on it) and the residual or bonus race
+  float best = 0.0f, bval = 0.0f;
+  int bidx = INT_MAX;
+  unsigned long long acc = 0;
+  const bool smp = p.mode == MODE_SAMPLE;
+  const uint32_t tag = smp ? 2u : 1u;
+  const uint32_t sb = smp ? (uint32_t)(p.row_b ? p.row_b[b] : b) : (uint32_t)b;
+  const uint32_t sj = smp ? (uint32_t)(p.row_pos ? p.row_pos[b] : 0) : (uint32_t)i;
+  for (int base = 0; base < nslots; base += NT * NSLOT) {
+    if (base > 0) sparse_load<NSLOT>(p, sm.ncs, Rt, kt, xt, ft, base);
+    if (!pair) {
+      sparse_plain_race<NSLOT>(p, xt, ft, mt, q.c, tag, sb, sj, best, bidx, bval);
+      continue;
+    }
+#pragma unroll
+    for (int t = 0; t < NSLOT; ++t) {
+      if (xt[t] == 0xffffffffu) continue;
+      const uint32_t x = xt[t];
+      const float lp = fmaf(ft[t] - mt, q.c, -lt);
+      float lq = -INFINITY;
+      uint32_t h = hslot(x);
+      for (int probe = 0; probe < HT; ++probe) {
+        const int v = sm.hidx[h];
+        if (v == (int)x) {
+          lq = sm.hlq[h];
+          break;
+        }
+        if (v == -1) break;
+        h = (h + 1) & (HT - 1);
+      }
+      acc += fixmass(fexp2(fminf(lp, lq)));
+      if (draw) {
+        const float w = fexp2(lp) - fexp2(lq);
+        if (w > 0.0f) {
+          const uint4 w4 = philox10(make_uint4(x >> 2, sb, (tag << 24) | sj, p.offset), p.key0, p.key1);
+          const uint32_t qq = x & 3u;
+          race_take(best, bidx, bval, race_key(w, qq == 0 ? w4.x : qq == 1 ? w4.y : qq == 2 ? w4.z : w4.w), (int)x,
+                    ft[t]);
+        }
+      }
+    }
+  }
+  if (pair) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (lane == 0) sm.asum[wave] = acc;
+    __syncthreads();
+    if (tid == 0) {
+      unsigned long long v = 0;
+      for (int w = 0; w < NWAVE; ++w) v += sm.asum[w];
+      p.alpha[(size_t)b * k + i] = (float)((double)v * 0x1p-40);
+    }
+  }
+  if (!draw) return;
+  block_race(sm.rs, best, bidx, bval);
+  if (bidx == INT_MAX && pair) {
+    // The residual mass vanished in fp32 (rounding only): draw from p_n (its kept entries).
+    for (int base = 0; base < nslots; base += NT * NSLOT) {
+      sparse_load<NSLOT>(p, sm.ncs, Rt, kt, xt, ft, base);
+      sparse_plain_race<NSLOT>(p, xt, ft, mt, q.c, 1u, (uint32_t)b, (uint32_t)n, best, bidx, bval);
+    }
+    block_race(sm.rs, best, bidx, bval);
+  }
+  const int y = bidx;
+  if (y < 0 || y >= p.V) return write_sentinel(p, b);  // no candidate: not reachable for a valid row
+  if (smp) {
+    if (tid == 0) {
+      p.tokens[b] = y;
+      p.logprobs[b] = (bval - sm.m[0]) / q.T - logf(sm.Z[0]);
+    }
+    return;
+  }
+  if (tid <= k) {
+    int t = -1;
+    float lp = 0.0f;
+    if (tid <= n) {
+      t = tid < n ? sm.tok[tid] : y;
+      const float l = tid < n ? sm.gath[tid] : bval;
+      lp = (l - sm.m[tid]) / q.T - logf(sm.Z[tid]);
+    }
+    p.tokens[(size_t)b * (k + 1) + tid] = t;
+    p.logprobs[(size_t)b * (k + 1) + tid] = lp;
+  }
+  if (tid == 0) p.accept_len[b] = n + 1;
+}
+
 template <class E, int VPT>
 __device__ void k5_item(const Params& p, K5Smem& sm, int item, int b, int s) {
   constexpr int EPV = E::EPV;
@@ -1270,8 +1582,9 @@ __device__ void k5_item(const Params& p, K5Smem& sm, int item, int b, int s) {
   const RowParams q = row_params(p, b);
   // Everything else independent is issued at once: the first two positions' slices, the rows'
   // statistics (with the logits at the draft tokens), the draft tokens and the accept uniforms.
+  // Truncated rows wait for their statistics: they may take the candidate path instead.
   uint4 a0[VPT], b0[VPT], a1[VPT], b1[VPT];
-  if (!q.greedy) {
+  if (!q.greedy && !q.trunc) {
     if (k > 0) {
       load_slice<E, VPT>(row_ptr(p, b, 0, esize), x0, nv, a0);
       load_slice<E, VPT>(row_ptr(p, b, k + 1, esize), x0, nv, b0);
@@ -1301,7 +1614,21 @@ __device__ void k5_item(const Params& p, K5Smem& sm, int item, int b, int s) {
   SV_TRACE5_AT(p, item, 1);
   bool ok = q.ok;
   for (int i = 0; i < k; ++i) ok = ok && sm.tok[i] >= 0 && sm.tok[i] < p.V;
-  for (int r = 0; r < rows; ++r) ok = ok && sm.state[r] == 0;
+  bool sparse = E::KEYBITS == 16 && q.trunc;
+  for (int r = 0; r < rows; ++r) {
+    ok = ok && (sm.state[r] & ST_BAD) == 0;
+    sparse = sparse && (sm.state[r] & ST_SPARSE) != 0;
+  }
+  if (ok && q.trunc && !q.greedy && !sparse) {  // truncated rows streamed after all: their first slices
+    if (k > 0) {
+      load_slice<E, VPT>(row_ptr(p, b, 0, esize), x0, nv, a0);
+      load_slice<E, VPT>(row_ptr(p, b, k + 1, esize), x0, nv, b0);
+    }
+    if (k > 1) {
+      load_slice<E, VPT>(row_ptr(p, b, 1, esize), x0, nv, a1);
+      load_slice<E, VPT>(row_ptr(p, b, k + 2, esize), x0, nv, b1);
+    }
+  }
   if (ok && !q.greedy) {
     // accept decisions of all positions at once (lane i of wave 0); n = the first rejection, else k
     // (k = 0 in sample mode: the draw below is the sampler's)
@@ -1319,6 +1646,17 @@ __device__ void k5_item(const Params& p, K5Smem& sm, int item, int b, int s) {
     __syncthreads();
     SV_TRACE5_AT(p, item, 2);
     const int n = sm.n;
+    if constexpr (E::KEYBITS == 16) {
+      if (sparse) {  // workgroup s finishes positions s, s + S5, ... from the candidates; no arrivals
+        for (int pi = s; pi <= k; pi += p.S5) {
+          k5_sparse<E>(p, sm, b, n, pi, q);
+          __syncthreads();  // the shared tables are reused by the next position
+        }
+        if (s <= k) SV_TRACE5_AT(p, item, 3);
+        SV_TRACE5_AT(p, item, 7);
+        return;
+      }
+    }
     uint4 vc[VPT];
     if (n == k) load_slice<E, VPT>(row_ptr(p, b, k, esize), x0, nv, vc);
     float best = 0.0f, bval = 0.0f;
@@ -1373,7 +1711,8 @@ __global__ __launch_bounds__(NT) void k5_verify(Params p) {
 // ---------------------------------------------------------------------------------------------
 struct Geo {
   int rows, R, S1, S5, L1, L5, esize, EPV;
-  size_t off_cnt1, off_cnt5, off_st1, off_hw1, off_hc1, off_rinfo, off_fin5, off_trace, off_trace5, total;
+  size_t off_cnt1, off_cnt5, off_st1, off_hw1, off_hc1, off_cand1, off_ncand1, off_rinfo, off_fin5, off_trace, off_trace5,
+      total;
 };
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -1403,6 +1742,8 @@ static bool make_geo(int32_t B, int32_t k, int32_t V, spec_dtype_t dtype, Geo& g
   const bool bf = dtype == SPEC_DTYPE_BF16;  // per-code and weight-bin partials: bf16 rows only
   take(g.off_hw1, bf ? R * g.S1 * (WTOP / 2) * 4 : 0);
   take(g.off_hc1, bf ? R * g.S1 * HCW * 4 : 0);
+  take(g.off_cand1, bf ? R * g.S1 * NC * 8 : 0);
+  take(g.off_ncand1, bf ? R * g.S1 * 4 : 0);
   take(g.off_rinfo, R * sizeof(RowInfo));
   take(g.off_fin5, (size_t)B * g.S5 * sizeof(FinalPart));
   take(g.off_trace, R * g.S1 * TRACE_SLOTS * 8);
@@ -1472,6 +1813,8 @@ static spec_status_t launch(Params& p, const Geo& g, spec_dtype_t dtype, void* w
   p.st1 = (StatPart*)(ws + g.off_st1);
   p.hw1 = (uint32_t*)(ws + g.off_hw1);
   p.hc1 = (uint32_t*)(ws + g.off_hc1);
+  p.cand1 = (unsigned long long*)(ws + g.off_cand1);
+  p.ncand1 = (uint32_t*)(ws + g.off_ncand1);
   p.rinfo = (RowInfo*)(ws + g.off_rinfo);
   p.fin5 = (FinalPart*)(ws + g.off_fin5);
   p.trace = TRACE_SLOTS > 0 ? (unsigned long long*)(ws + g.off_trace) : nullptr;

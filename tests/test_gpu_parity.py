@@ -100,6 +100,42 @@ def test_small_cases(o, case):
     _check(o, w, [0, 7], name)
 
 
+def _shift_bf16(a, delta):
+    return W.bf16_rne(W.bf16_to_f32(a) + np.float32(delta))
+
+
+def test_candidate_path_edges(o):
+    """Truncated bf16 rows with few kept entries (finished from the candidates recorded by the
+    statistics pass): clustered values with ties at the top-k threshold, token 0 kept with logit
+    +0 (its packed candidate is all zero bits), slices that are entirely -inf, and a row whose
+    maximum lies a few codes above -inf."""
+    neg_inf, most_neg = np.uint16(0xFF80), np.uint16(0xFF7F)
+    clustered = W.make(6, 3, 30000, seed=4101, target_sigma=0.3, noise_sigma=0.05, top_k=20,
+                       name="clustered_topk")
+    _check(o, clustered, [0, 5], "clustered_topk")
+    w = W.make(6, 2, 40000, seed=4102, temperature=0.9, top_k=3, top_p=0.9, name="cand_edges")
+    w.target = _shift_bf16(w.target, -12.0).reshape(w.target.shape)
+    w.draft = _shift_bf16(w.draft, -12.0).reshape(w.draft.shape)
+    w.target[0:2, :, 0] = np.uint16(0x0000)   # +0: the row maximum at index 0
+    w.draft[0:2, :, 0] = np.uint16(0x0000)
+    w.target[1, 1, 0] = np.uint16(0x8000)     # -0 ties +0
+    w.target[2:4, :, 1000:] = neg_inf         # every slice but the first is all -inf
+    w.draft[2:4, :, 1000:] = neg_inf
+    w.target[4, :, :] = neg_inf               # maxima just above -inf
+    w.target[4, :, 7::11] = most_neg
+    w.target[4, :, 3] = np.uint16(0xFF7E)
+    w.draft[4, :, :] = neg_inf
+    w.draft[4, :, 5::13] = most_neg
+    _check(o, w, [0, 2], "cand_edges")
+    # one small slice whose values all lie within 64 codes of -inf (the candidate window reaches -inf)
+    tiny = W.make(3, 1, 64, seed=4103, temperature=1.0, top_k=4, name="near_neginf")
+    rng = np.random.default_rng(4103)
+    for a in (tiny.target, tiny.draft):
+        a[...] = rng.integers(0xFF41, 0xFF80, size=a.shape, dtype=np.uint16)
+        a[..., ::9] = neg_inf
+    _check(o, tiny, [0, 1], "near_neginf")
+
+
 def test_special_values_and_sentinels(o):
     w = W.make(10, 2, 16384, seed=77, temperature=1.0, top_p=0.8, name="special")
     drafts = w.draft_tokens(parity.oracle_sampler(o))
