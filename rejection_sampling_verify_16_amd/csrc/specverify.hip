@@ -63,9 +63,10 @@ constexpr int HCW = NBC / 2 + 1;  // words per slice of packed bin counts + the 
 constexpr int NKERN = 2;        // kernels per call
 
 constexpr int WC = 64;          // K1: candidate window (codes below the slice max) of truncated rows
-constexpr int NC = 128;         // K1: candidates recorded per slice at most
-constexpr int NFLAG = 128;      // K1: staged candidate-holding vectors per slice at most
-constexpr int KMAX = 1024;      // kept entries per row at most for the candidate (sparse) path of K5
+constexpr int NC = 192;         // K1: candidates recorded per slice at most
+constexpr int NFLAG = 192;      // K1: staged candidate-holding vectors per slice at most
+constexpr int KMAX = 1024;
+constexpr int KC = 64;          // bf16 top-k rows with K <= KC take their kept threshold from the candidates      // kept entries per row at most for the candidate (sparse) path of K5
 constexpr int HT = 2048;        // K5 sparse path: hash table entries (power of two, > KMAX)
 
 constexpr uint32_t ST_BAD = 1u;     // NaN / +inf entries, or every entry -inf
@@ -77,7 +78,8 @@ struct StatPart {  // K1, per (logit row, slice)
   float s;         // sum of exp2((l - m) c) over the slice (rows that need the whole-row normaliser)
   uint32_t flags;  // bit 0: NaN or +inf seen
   float g;         // the row's logit at its draft token, if the token falls in this slice
-  uint32_t pad[3];
+  uint32_t floor;  // candidate rows: every finite logit of the slice with key >= floor was recorded
+  uint32_t pad[2];
 };
 
 struct RowInfo {    // per logit row
@@ -206,6 +208,7 @@ struct RowParams {
   float T, P, c;
   int K;
   bool ok, greedy, trunc, useK, useP;
+  bool cand;  // top-k with K <= KC (bf16 rows: kept threshold selected from the recorded candidates)
 };
 __device__ inline RowParams row_params(const Params& p, int b) {
   RowParams q;
@@ -219,6 +222,7 @@ __device__ inline RowParams row_params(const Params& p, int b) {
   q.useK = q.ok && !q.greedy && q.K > 0 && q.K < p.V;
   q.useP = q.ok && !q.greedy && q.P < 1.0f;
   q.trunc = q.useK || q.useP;
+  q.cand = q.useK && q.K <= KC;
   return q;
 }
 
@@ -249,7 +253,7 @@ struct RedSmem {
 };
 
 // Workgroup (max, argmax, sum, flags) into every thread.
-__device__ void block_stats(RedSmem& rs, float& m, int& a, float& s, uint32_t& fl, float c) {
+__device__ __forceinline__ void block_stats(RedSmem& rs, float& m, int& a, float& s, uint32_t& fl, float c) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   wave_stats(m, a, s, fl, c);
   if (lane == 0) {
@@ -274,7 +278,7 @@ __device__ void block_stats(RedSmem& rs, float& m, int& a, float& s, uint32_t& f
 }
 
 // Workgroup NaN-propagating max into every thread.
-__device__ float block_nan_max(RedSmem& rs, float m) {
+__device__ __forceinline__ float block_nan_max(RedSmem& rs, float m) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = nan_max(m, __shfl_xor(m, o, 64));
@@ -286,7 +290,7 @@ __device__ float block_nan_max(RedSmem& rs, float m) {
   return m;
 }
 
-__device__ void block_maxarg(RedSmem& rs, float& m, int& a) {
+__device__ __forceinline__ void block_maxarg(RedSmem& rs, float& m, int& a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   wave_maxarg(m, a);
   if (lane == 0) {
@@ -301,7 +305,7 @@ __device__ void block_maxarg(RedSmem& rs, float& m, int& a) {
 }
 
 // Workgroup sum into every thread.
-__device__ uint32_t block_sum_u32(RedSmem& rs, uint32_t v) {
+__device__ __forceinline__ uint32_t block_sum_u32(RedSmem& rs, uint32_t v) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -313,8 +317,20 @@ __device__ uint32_t block_sum_u32(RedSmem& rs, uint32_t v) {
   return t;
 }
 
+__device__ __forceinline__ uint32_t block_max_u32(RedSmem& rs, uint32_t v) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor(v, o, 64));
+  if (lane == 0) rs.u[wave] = v;
+  __syncthreads();
+  uint32_t t = 0;
+  for (int w = 0; w < NWAVE; ++w) t = max(t, rs.u[w]);
+  __syncthreads();
+  return t;
+}
+
 // Lowest thread index whose predicate holds, into every thread (NT if none).
-__device__ int block_first(RedSmem& rs, bool pred) {
+__device__ __forceinline__ int block_first(RedSmem& rs, bool pred) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int fl = first_lane(pred);
   if (lane == 0) rs.i[wave] = fl < 64 ? wave * 64 + fl : NT;
@@ -339,7 +355,7 @@ struct RadixSmem {
 
 // One digit histogram of the entries whose key is >= thr and matches `prefix` above the digit.
 template <class E, bool COUNTS>
-__device__ void radix_hist(RadixSmem& sm, const uint4* src, int nvec, int lev, uint32_t prefix, uint32_t thr,
+__device__ __forceinline__ void radix_hist(RadixSmem& sm, const uint4* src, int nvec, int lev, uint32_t prefix, uint32_t thr,
                            float m, float c) {
   const int tid = threadIdx.x;
   const int shift = E::KEYBITS - 8 * (lev + 1);
@@ -370,7 +386,7 @@ __device__ void radix_hist(RadixSmem& sm, const uint4* src, int nvec, int lev, u
 }
 
 template <class E>
-__device__ void row_cutoff(RadixSmem& sm, RedSmem& rs, const uint8_t* row, int V, float m, float c, int K, float P,
+__device__ __forceinline__ void row_cutoff(RadixSmem& sm, RedSmem& rs, const uint8_t* row, int V, float m, float c, int K, float P,
                            uint32_t& thr_out, float& Z_out) {
   const int tid = threadIdx.x;
   const int nvec = V / E::EPV;
@@ -467,7 +483,7 @@ __device__ inline unsigned long long code_mass(uint32_t cnt, uint32_t code, floa
   return cnt ? (unsigned long long)cnt * fixmass(fexp2((key16_value(code) - m) * c)) : 0ull;
 }
 
-__device__ bool select_run(const uint32_t* cnt, int n, uint32_t ktop, float m, float c, SelState& ss, RedSmem& rs,
+__device__ __forceinline__ bool select_run(const uint32_t* cnt, int n, uint32_t ktop, float m, float c, SelState& ss, RedSmem& rs,
                            uint32_t base_cnt, unsigned long long base_mass, double ztot_fixed, bool useK, int K,
                            bool useP, float P, int& sel, unsigned long long& zsel) {
   const int tid = threadIdx.x;
@@ -547,6 +563,30 @@ __device__ bool select_run(const uint32_t* cnt, int n, uint32_t ktop, float m, f
   return true;
 }
 
+// Loads row r's candidate slots (slice s, entry e < count) with key >= thr: thread t takes slots t,
+// t + NT, ... of the S x NC slot grid from base on; all of a thread's loads are issued before any is
+// used.  Empty or filtered slots get index 0xffffffff.
+template <int NSLOT>
+__device__ inline void sparse_load(const Params& p, const uint32_t* ncs, int r, uint32_t thr, uint32_t (&xs)[NSLOT],
+                                   float (&fs)[NSLOT], int base) {
+  const int tid = threadIdx.x, S = p.S1;
+  unsigned long long c[NSLOT];
+#pragma unroll
+  for (int t = 0; t < NSLOT; ++t) {
+    const int g = base + tid + t * NT, sl = g / NC, e = g - sl * NC;
+    c[t] = (sl < S && (uint32_t)e < min(ncs[sl], (uint32_t)NC))
+               ? __hip_atomic_load(p.cand1 + ((size_t)r * S + sl) * NC + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+               : ~0ull;  // no slot (a recorded candidate has an index below 2^20)
+  }
+#pragma unroll
+  for (int t = 0; t < NSLOT; ++t) {
+    const float f = __uint_as_float((uint32_t)(c[t] & 0xffffu) << 16);
+    const bool keep = c[t] != ~0ull && key16f(f) >= thr;
+    xs[t] = keep ? (uint32_t)(c[t] >> 16) : 0xffffffffu;
+    fs[t] = f;
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // K1: row statistics (every logit read once), merged by the last slice of each row.
 // ---------------------------------------------------------------------------------------------
@@ -580,7 +620,7 @@ struct K1Smem {
 // so its weights exp2((l - m) c) lie in (2^(hi_j - 1/BRC), 2^hi_j], hi_j = -(A_m + j)/BRC - m c.
 // With these bounds and Z (the row normaliser) the threshold bin lies between the first bin whose
 // upper-bound cumulative mass can reach P Z and the first whose lower-bound cumulative mass must.
-__device__ bool coarse_window(K1Smem& sm, float m, float c, float P, float Ztot, int V, uint32_t keym, uint32_t& klo,
+__device__ __forceinline__ bool coarse_window(K1Smem& sm, float m, float c, float P, float Ztot, int V, uint32_t keym, uint32_t& klo,
                               uint32_t& khi) {
   const int tid = threadIdx.x;  // NT == NBC: thread t owns bin t
   const float Am = floorf(-m * (c * BRC));
@@ -617,7 +657,7 @@ __device__ bool coarse_window(K1Smem& sm, float m, float c, float P, float Ztot,
 
 // Exact per-code counts of [klo, khi] over the whole row by this workgroup (entry i counts code khi - i),
 // plus the exact count and fixed-point mass above khi; then the threshold search over the window.
-__device__ bool window_pass(K1Smem& sm, const uint8_t* row, int V, float m, float c, uint32_t klo, uint32_t khi,
+__device__ __forceinline__ bool window_pass(K1Smem& sm, const uint8_t* row, int V, float m, float c, uint32_t klo, uint32_t khi,
                             bool useK, int K, bool useP, float P, double ztot_fixed, uint32_t& thr, float& Z) {
   const int tid = threadIdx.x;
   const int width = (int)(khi - klo + 1);
@@ -676,17 +716,55 @@ __device__ bool window_pass(K1Smem& sm, const uint8_t* row, int V, float m, floa
 // thread t's word of each slice's packed code counts are all loaded before any is used, so they cost
 // one round trip for up to MB slices; the weight-bin counts are loaded only when the top codes do not
 // hold the threshold.
+// Kept threshold of a top-k row (K <= KC) from the recorded candidates.  Slice s recorded every finite
+// logit with key >= floor_s, so with Fe = max(floor_s, key of the smallest finite value) the merged
+// counts of the codes from the row max down to Fe are exact; the selection succeeds when the kept
+// threshold lies among them.  Also reports whether the row can take K5's candidate path.
+__device__ __forceinline__ bool cand_select(const Params& p, K1Smem& sm, int r, float m, const RowParams& q, uint32_t flo,
+                            uint32_t& thr, float& Z, bool& sparse) {
+  const int tid = threadIdx.x, S = p.S1;
+  const uint32_t kinf = key16f(-INFINITY);
+  const uint32_t Fe = max(block_max_u32(sm.rs, tid < S ? flo : 0u), kinf + 1u);
+  const uint32_t keym = key16f(m);
+  const int nb = (int)(keym - Fe) + 1;  // m is finite, so keym >= Fe
+  const bool over = __syncthreads_or(tid < S && sm.u.mg.ncs[tid] > (uint32_t)NC) != 0;
+  if (over || nb > WF) return false;
+  uint32_t* cnt = sm.u.mg.cnt;
+  for (int j = tid; j < nb; j += NT) cnt[j] = 0;
+  __syncthreads();
+  for (int base = 0; base < S * NC; base += NT * 4) {
+    uint32_t xs[4];
+    float fs[4];
+    sparse_load<4>(p, sm.u.mg.ncs, r, Fe, xs, fs, base);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (xs[t] != 0xffffffffu) atomicAdd(&cnt[keym - key16f(fs[t])], 1u);
+  }
+  __syncthreads();
+  int sel = -1;
+  unsigned long long zsel = 0;
+  if (!select_run(cnt, nb, keym, m, q.c, sm.ss, sm.rs, 0u, 0ull, 0.0, q.useK, q.K, q.useP, q.P, sel, zsel))
+    return false;
+  thr = keym - (uint32_t)sel;
+  Z = (float)((double)zsel * 0x1p-40);
+  uint32_t kc = 0;
+  for (int j = tid; j <= sel; j += NT) kc += cnt[j];
+  sparse = block_sum_u32(sm.rs, kc) <= (uint32_t)KMAX;
+  return true;
+}
+
 template <class E>
-__device__ void k1_merge(const Params& p, K1Smem& sm, int r, int b, int i, const RowParams& q) {
+__device__ __forceinline__ void k1_merge(const Params& p, K1Smem& sm, int r, int b, int i, const RowParams& q) {
   constexpr bool BF = E::KEYBITS == 16;
   constexpr int esize = 16 / E::EPV;
   const int tid = threadIdx.x;
   const int S = p.S1;
-  const bool hist = BF && q.trunc;
+  const bool cmode = BF && q.cand;
+  const bool hist = BF && q.trunc && !cmode;
   const bool coarse = hist && !q.useK;
   float m = -INFINITY, sum = 0.0f;
   int a = INT_MAX;
-  uint32_t fl = 0;
+  uint32_t fl = 0, flo = 0;
   // slice holding this row's draft token (-1: none or out of range)
   int sg = -1;
   if (p.mode == MODE_VERIFY && i != p.k) {
@@ -700,7 +778,8 @@ __device__ void k1_merge(const Params& p, K1Smem& sm, int r, int b, int i, const
     sum = ldf(&sp->s);
     fl = ld32(&sp->flags);
     if (tid == sg) sm.win[1] = ld32(&sp->g);
-    if (hist) sm.u.mg.ncs[tid] = ld32(&p.ncand1[(size_t)r * S + tid]);
+    if (hist || cmode) sm.u.mg.ncs[tid] = ld32(&p.ncand1[(size_t)r * S + tid]);
+    if (cmode) flo = ld32(&sp->floor);
   }
   uint32_t hwv[MB];
   if (hist) {
@@ -722,7 +801,9 @@ __device__ void k1_merge(const Params& p, K1Smem& sm, int r, int b, int i, const
   if (!bad && q.trunc) {
     bool done = false;
     const double ztot = (double)sum * 0x1p40;
-    if (BF) {
+    if (cmode) {
+      done = cand_select(p, sm, r, m, q, flo, thr, Z, sparse);
+    } else if (BF) {
       const uint32_t keym = key16f(m);
       // merged counts of the row's top WTOP codes: entry co is code keym - co.  Slice s's word tid holds
       // its codes keyms[s] - 2 tid and keyms[s] - 2 tid - 1, i.e. entries off + 2 tid (+1) with
@@ -847,7 +928,7 @@ __device__ inline uint32_t cand_bits(const uint4& v, uint32_t keyms2) {
 // per-code counts of the WTOP codes below ms; top-p-only rows also add the normaliser sum and the
 // weight-bin counts (bin floor(-l c BRC) - cbase).  Out-of-range entries go to a per-lane spare bin.
 template <int VPT, bool TOPP_ONLY>
-__device__ void k1_hist(K1Smem& sm, const uint4 (&v)[VPT], int nv, int x0, float ms, float c, float cbase,
+__device__ __forceinline__ void k1_hist(K1Smem& sm, const uint4 (&v)[VPT], int nv, int x0, float ms, float c, float cbase,
                         float& sum) {
   const int tid = threadIdx.x;
   const uint32_t lane = tid & 63;
@@ -921,9 +1002,68 @@ __device__ void k1_hist(K1Smem& sm, const uint4 (&v)[VPT], int nv, int x0, float
   }
 }
 
+// Bit e set: entry e of a bf16 vector has key >= fe.
+__device__ inline uint32_t cand_bits_ge(const uint4& v, uint32_t fe) {
+  const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+  uint32_t bits = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t k2 = key16x2(wv[q]);
+    bits |= ((k2 & 0xffffu) >= fe ? 1u : 0u) << (2 * q);
+    bits |= ((k2 >> 16) >= fe ? 1u : 0u) << (2 * q + 1);
+  }
+  return bits;
+}
+
+// Candidates of a top-k slice: every logit with key >= fe (index and raw bits).  vm holds the vector
+// maxima; vectors whose maximum reaches fe are staged in LDS, then one thread per staged vector
+// appends its candidates.  More than NFLAG staged vectors, or more than NC candidates, leave ncand
+// above NC: the slice then has no usable candidate list.
+template <int VPT>
+__device__ __forceinline__ void k1_capture(K1Smem& sm, const uint4 (&v)[VPT], const float (&vm)[VPT], int x0, uint32_t fe) {
+  const int tid = threadIdx.x;
+  const float fcand = key16_value(fe);
+  uint32_t cmask = 0;
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) cmask |= (vm[u] >= fcand ? 1u : 0u) << u;
+  if (__ballot(cmask != 0) != 0) {
+    uint32_t at = wave_reserve(&sm.u.st.nflag, (uint32_t)__popc(cmask));
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      if (cmask & (1u << u)) {
+        if (at < (uint32_t)NFLAG) {
+          sm.u.st.fvec[at] = v[u];
+          sm.u.st.fidx[at] = (uint32_t)(tid + u * NT);
+        }
+        ++at;
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t nflag = sm.u.st.nflag;
+  if (nflag > (uint32_t)NFLAG) {
+    if (tid == 0) sm.u.st.ncand = NC + 1;
+  } else if ((uint32_t)(tid & ~63) < nflag) {  // waves holding a staged vector
+    const bool mine = (uint32_t)tid < nflag;
+    const uint4 vv = mine ? sm.u.st.fvec[tid] : make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t bits = mine ? cand_bits_ge(vv, fe) : 0u;
+    const int xb = x0 + (mine ? (int)sm.u.st.fidx[tid] : 0) * BF16::EPV;
+    uint32_t c = wave_reserve(&sm.u.st.ncand, (uint32_t)__popc(bits));
+    const uint32_t wv[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+    for (int e = 0; e < BF16::EPV; ++e) {
+      if (bits & (1u << e)) {
+        const uint32_t h = (e & 1) ? (wv[e >> 1] >> 16) : (wv[e >> 1] & 0xffffu);
+        if (c < (uint32_t)NC) sm.u.st.cand[c] = ((unsigned long long)(xb + e) << 16) | h;
+        ++c;
+      }
+    }
+  }
+}
+
 // One K1 work item: slice s of logit row r.
 template <class E, int VPT>
-__device__ void k1_item(const Params& p, K1Smem& sm, int item, int r, int s) {
+__device__ __forceinline__ void k1_item(const Params& p, K1Smem& sm, int item, int r, int s) {
   constexpr int EPV = E::EPV;
   constexpr int esize = 16 / EPV;
   constexpr bool BF = E::KEYBITS == 16;
@@ -949,7 +1089,7 @@ __device__ void k1_item(const Params& p, K1Smem& sm, int item, int r, int s) {
   }
   float m = -INFINITY, sum = 0.0f;
   int a = INT_MAX;
-  uint32_t fl = 0;
+  uint32_t fl = 0, flo = 0;
   if (q.greedy) {
     // lowest argmax; NaN never compares greater, so it is flagged separately
     bool nan = false;
@@ -969,6 +1109,52 @@ __device__ void k1_item(const Params& p, K1Smem& sm, int item, int r, int s) {
       }
     }
     fl = (nan || m == INFINITY) ? 1u : 0u;
+  } else if (BF && q.cand) {
+    // Top-k row with K <= KC: no histograms.  The slice records every logit at or above a floor that
+    // lies at or below its KC-th largest thread maximum; at least KC distinct logits reach that, so the
+    // slice's top KC logits are all recorded, and the merge selects the kept threshold from the records.
+    float vm[VPT];
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int j = tid + u * NT;
+      vm[u] = -INFINITY;
+      if (j < nv) {
+        float x = E::get(v[u], 0);
+#pragma unroll
+        for (int e = 1; e < EPV; ++e) x = nan_max(x, E::get(v[u], e));
+        vm[u] = x;
+        m = nan_max(m, x);
+      }
+    }
+    SV_TRACE_AT(p, item, 1);
+    sm.u.st.hc[tid] = 0;
+    if (tid == 0) {
+      sm.u.st.ncand = 0;
+      sm.u.st.nflag = 0;
+    }
+    const float ms = block_nan_max(sm.rs, m);  // its barriers also publish the cleared counts
+    const uint32_t kinf = key16f(-INFINITY);
+    if (ms > -INFINITY && ms < INFINITY) {  // not NaN, +inf or an all -inf slice
+      // thread maxima binned by their distance below the slice max, BRC bins per unit, NT bins
+      atomicAdd(&sm.u.st.hc[(int)fminf(floorf((ms - m) * BRC), (float)(NT - 1))], 1u);
+      __syncthreads();
+      const uint32_t incl = block_inclusive_scan<uint32_t>(sm.u.st.hc[tid], sm.rs.scan32);
+      const int bstar = block_first(sm.rs, incl >= (uint32_t)KC);  // the bin holding the KC-th maximum
+      // one bin of margin for rounding; then the largest bf16 at or below that value
+      const uint32_t fu = __float_as_uint(ms - (float)(bstar + 2) * (1.0f / BRC));
+      const uint32_t fh = (fu >> 16) + ((fu & 0x8000ffffu) > 0x80000000u ? 1u : 0u);
+      flo = max(key16(fh), kinf);
+      k1_capture<VPT>(sm, v, vm, x0, max(flo, kinf + 1u));
+    }
+    m = ms;
+    __syncthreads();
+    const uint32_t nc = sm.u.st.ncand;
+    if (tid < (int)min(nc, (uint32_t)NC)) {
+      unsigned long long* cd = p.cand1 + ((size_t)r * p.S1 + s) * NC + tid;
+      __hip_atomic_store(cd, sm.u.st.cand[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (tid == 0) st32(&p.ncand1[(size_t)r * p.S1 + s], nc);
+    if (!(m == m) || m == INFINITY) fl = 1u;
   } else {
     // NaN-propagating max: a NaN or +inf anywhere shows in the row max
 #pragma unroll
@@ -1036,6 +1222,7 @@ __device__ void k1_item(const Params& p, K1Smem& sm, int item, int r, int s) {
     stf(&sp->s, sum);
     st32(&sp->flags, fl);
     stf(&sp->g, gval);
+    st32(&sp->floor, flo);
   }
   SV_TRACE_AT(p, item, 2);
   if (arrive_last(&p.cnt1[r], (uint32_t)p.S1, &sm.rs.flag)) {
@@ -1091,7 +1278,7 @@ __device__ inline void race_take(float& best, int& bidx, float& bval, float key,
 }
 
 // Workgroup race winner (key, index, logit) into every thread.
-__device__ void block_race(RedSmem& rs, float& best, int& bidx, float& bval) {
+__device__ __forceinline__ void block_race(RedSmem& rs, float& best, int& bidx, float& bval) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -1116,7 +1303,7 @@ __device__ void block_race(RedSmem& rs, float& best, int& bidx, float& bval) {
 // Gumbel-max candidates over w(x) = exp2((l - m) c) on the kept entries of one 16-byte vector
 // (stream tag, b, position j).  Groups of four entries with no kept entry draw nothing.
 template <class E>
-__device__ void gumbel_vec(const uint4& v, int xbase, float m, float c, float fthr, uint32_t tag, uint32_t b,
+__device__ __forceinline__ void gumbel_vec(const uint4& v, int xbase, float m, float c, float fthr, uint32_t tag, uint32_t b,
                            uint32_t j, const Params& p, float& best, int& bidx, float& bval) {
 #pragma unroll
   for (int g = 0; g < E::EPV; g += 4) {
@@ -1142,7 +1329,7 @@ __device__ void gumbel_vec(const uint4& v, int xbase, float m, float c, float ft
   }
 }
 
-__device__ void write_sentinel(const Params& p, int b) {
+__device__ __forceinline__ void write_sentinel(const Params& p, int b) {
   const int k = p.k, tid = threadIdx.x;
   if (p.mode == MODE_SAMPLE) {
     if (tid == 0) {
@@ -1160,7 +1347,7 @@ __device__ void write_sentinel(const Params& p, int b) {
 }
 
 template <class E>
-__device__ void k5_finalize(const Params& p, K5Smem& sm, int b, bool ok, const RowParams& q) {
+__device__ __forceinline__ void k5_finalize(const Params& p, K5Smem& sm, int b, bool ok, const RowParams& q) {
   const int k = p.k, S = p.S5;
   const int tid = threadIdx.x;
   constexpr int esize = 16 / E::EPV;
@@ -1270,7 +1457,7 @@ __device__ inline void load_slice(const uint8_t* row, int x0, int nv, uint4 (&v)
 // a vector with no entry >= tt is skipped before any exp2.  Stream (tag, b, position j).  The winner's
 // (target) logit rides along.
 template <class E, int VPT, bool RESID>
-__device__ void race_slice(const Params& p, const uint4 (&va)[VPT], const uint4 (&vb)[VPT], int x0, int nv, float c,
+__device__ __forceinline__ void race_slice(const Params& p, const uint4 (&va)[VPT], const uint4 (&vb)[VPT], int x0, int nv, float c,
                            float mt, float lt, float tt, float md, float ld, float td, uint32_t tag, uint32_t sb,
                            uint32_t sj, float& best, int& bidx, float& bval) {
   constexpr int EPV = E::EPV;
@@ -1319,7 +1506,7 @@ __device__ void race_slice(const Params& p, const uint4 (&va)[VPT], const uint4 
 // costs one exp2.  TRUNC: the batch row is truncated (some entries have p = 0); then a vector without
 // a kept target entry adds nothing and is skipped.
 template <class E, int VPT, bool TRUNC>
-__device__ void k5_position(const Params& p, K5Smem& sm, int b, int i, int n, int x0, int nv, float c,
+__device__ __forceinline__ void k5_position(const Params& p, K5Smem& sm, int b, int i, int n, int x0, int nv, float c,
                             const uint4 (&va)[VPT], const uint4 (&vb)[VPT], float& best, int& bidx, float& bval) {
   constexpr int EPV = E::EPV;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1361,7 +1548,7 @@ __device__ void k5_position(const Params& p, K5Smem& sm, int b, int i, int n, in
 // Every draft position of this slice, two positions' slices in flight: (a0, b0) and (a1, b1) hold
 // positions 0 and 1 on entry; position i + 2 is loaded into the pair that position i has just used.
 template <class E, int VPT, bool TRUNC>
-__device__ void k5_positions(const Params& p, K5Smem& sm, int b, int n, int x0, int nv, float c, uint4 (&a0)[VPT],
+__device__ __forceinline__ void k5_positions(const Params& p, K5Smem& sm, int b, int n, int x0, int nv, float c, uint4 (&a0)[VPT],
                              uint4 (&b0)[VPT], uint4 (&a1)[VPT], uint4 (&b1)[VPT], float& best, int& bidx,
                              float& bval) {
   constexpr int esize = 16 / E::EPV;
@@ -1390,30 +1577,6 @@ __device__ void k5_positions(const Params& p, K5Smem& sm, int b, int n, int x0, 
 // without re-reading the rows.  bf16 rows only.
 // ---------------------------------------------------------------------------------------------
 
-// Loads row r's candidate slots (slice s, entry e < count) with key >= thr: thread t takes slots t,
-// t + NT, ... of the S x NC slot grid from base on; all of a thread's loads are issued before any is
-// used.  Empty or filtered slots get index 0xffffffff.
-template <int NSLOT>
-__device__ inline void sparse_load(const Params& p, const uint32_t* ncs, int r, uint32_t thr, uint32_t (&xs)[NSLOT],
-                                   float (&fs)[NSLOT], int base) {
-  const int tid = threadIdx.x, S = p.S1;
-  unsigned long long c[NSLOT];
-#pragma unroll
-  for (int t = 0; t < NSLOT; ++t) {
-    const int g = base + tid + t * NT, sl = g / NC, e = g - sl * NC;
-    c[t] = (sl < S && (uint32_t)e < min(ncs[sl], (uint32_t)NC))
-               ? __hip_atomic_load(p.cand1 + ((size_t)r * S + sl) * NC + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-               : ~0ull;  // no slot (a recorded candidate has an index below 2^20)
-  }
-#pragma unroll
-  for (int t = 0; t < NSLOT; ++t) {
-    const float f = __uint_as_float((uint32_t)(c[t] & 0xffffu) << 16);
-    const bool keep = c[t] != ~0ull && key16f(f) >= thr;
-    xs[t] = keep ? (uint32_t)(c[t] >> 16) : 0xffffffffu;
-    fs[t] = f;
-  }
-}
-
 __device__ inline uint32_t hslot(uint32_t x) { return (x * 2654435761u) >> (32 - 11); }  // HT == 2^11
 __device__ inline uint32_t thr_key(float fthr) { return fthr == -INFINITY ? 0u : key16f(fthr); }
 
@@ -1439,7 +1602,7 @@ __device__ inline void sparse_plain_race(const Params& p, const uint32_t (&xs)[N
 // token draw where this position is the one that draws (the first rejection n, or the bonus position
 // k when every draft was accepted), with the row's outputs.
 template <class E>
-__device__ void k5_sparse(const Params& p, K5Smem& sm, int b, int n, int i, const RowParams& q) {
+__device__ __forceinline__ void k5_sparse(const Params& p, K5Smem& sm, int b, int n, int i, const RowParams& q) {
   constexpr int NSLOT = 4;  // slots per thread per pass: NT * NSLOT = 1024 slots
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k = p.k, S = p.S1;
@@ -1571,7 +1734,7 @@ __device__ void k5_sparse(const Params& p, K5Smem& sm, int b, int n, int i, cons
 }
 
 template <class E, int VPT>
-__device__ void k5_item(const Params& p, K5Smem& sm, int item, int b, int s) {
+__device__ __forceinline__ void k5_item(const Params& p, K5Smem& sm, int item, int b, int s) {
   constexpr int EPV = E::EPV;
   constexpr int esize = 16 / EPV;
   const int tid = threadIdx.x;

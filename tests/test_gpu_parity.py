@@ -136,6 +136,26 @@ def test_candidate_path_edges(o):
     _check(o, tiny, [0, 1], "near_neginf")
 
 
+def test_topk_candidate_selection_fallbacks(o):
+    """Top-k rows with small K select their threshold from recorded candidates; rows where that cannot
+    work fall back to the whole-row selection: a flat row (every slice overflows its record), a top-k
+    range that crosses zero (too many codes between the maximum and the threshold), several outliers
+    per slice, and K at the candidate-mode limit."""
+    w = W.make(6, 1, 40000, seed=4104, temperature=1.0, top_k=10, name="topk_fallbacks")
+    w.target[0, :, :] = np.uint16(0x3F80)      # flat: every logit 1.0
+    w.draft[0, :, :] = np.uint16(0x3F80)
+    w.target[1] = _shift_bf16(w.target[1], -15.0).reshape(w.target[1].shape)  # bulk around -15
+    w.target[1, :, 100:20000:3999] = np.uint16(0x41F0)                          # five +30 outliers
+    rng = np.random.default_rng(4104)
+    for b in (2, 3):
+        for i in range(2):
+            idx = rng.choice(40000, size=24, replace=False)
+            w.target[b, i, idx] = W.bf16_rne(rng.uniform(12.0, 14.0, size=24).astype(np.float32))
+    w.top_k[4] = 64
+    w.top_k[5] = 65                            # one above the limit: histogram selection
+    _check(o, w, [0, 3], "topk_fallbacks")
+
+
 def test_special_values_and_sentinels(o):
     w = W.make(10, 2, 16384, seed=77, temperature=1.0, top_p=0.8, name="special")
     drafts = w.draft_tokens(parity.oracle_sampler(o))
