@@ -1782,6 +1782,10 @@ __device__ __forceinline__ void k5_item(const Params& p, K5Smem& sm, int item, i
     ok = ok && (sm.state[r] & ST_BAD) == 0;
     sparse = sparse && (sm.state[r] & ST_SPARSE) != 0;
   }
+  if (ok && sparse && s > k) {  // candidate-path row: this workgroup has no position to finish
+    SV_TRACE5_AT(p, item, 7);
+    return;
+  }
   if (ok && q.trunc && !q.greedy && !sparse) {  // truncated rows streamed after all: their first slices
     if (k > 0) {
       load_slice<E, VPT>(row_ptr(p, b, 0, esize), x0, nv, a0);
@@ -1865,7 +1869,10 @@ template <class E, int VPT>
 __global__ __launch_bounds__(NT) void k5_verify(Params p) {
   __shared__ K5Smem sm;
   int b, s;
-  item_rs(blockIdx.x, p.B, p.S5, b, s);
+  // row-major items: workgroups go to the XCDs round-robin, so each batch row's slices spread over
+  // all of them and a run of expensive rows does not pile onto one XCD
+  b = blockIdx.x / p.S5;
+  s = blockIdx.x - b * p.S5;
   k5_item<E, VPT>(p, sm, blockIdx.x, b, s);
 }
 
