@@ -65,6 +65,7 @@ constexpr int NKERN = 2;        // kernels per call
 constexpr int WC = 64;          // K1: candidate window (codes below the slice max) of truncated rows
 constexpr int NC = 192;         // K1: candidates recorded per slice at most
 constexpr int NFLAG = 192;      // K1: staged candidate-holding vectors per slice at most
+constexpr int NFW = 64;         // K1 top-k slices: staged candidate-holding vectors per wave at most
 constexpr int KMAX = 1024;
 constexpr int KC = 64;          // bf16 top-k rows with K <= KC take their kept threshold from the candidates      // kept entries per row at most for the candidate (sparse) path of K5
 constexpr int HT = 2048;        // K5 sparse path: hash table entries (power of two, > KMAX)
@@ -587,6 +588,19 @@ __device__ inline void sparse_load(const Params& p, const uint32_t* ncs, int r, 
   }
 }
 
+// Bit e set: entry e of a bf16 vector has key >= fe.
+__device__ inline uint32_t cand_bits_ge(const uint4& v, uint32_t fe) {
+  const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+  uint32_t bits = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t k2 = key16x2(wv[q]);
+    bits |= ((k2 & 0xffffu) >= fe ? 1u : 0u) << (2 * q);
+    bits |= ((k2 >> 16) >= fe ? 1u : 0u) << (2 * q + 1);
+  }
+  return bits;
+}
+
 // ---------------------------------------------------------------------------------------------
 // K1: row statistics (every logit read once), merged by the last slice of each row.
 // ---------------------------------------------------------------------------------------------
@@ -600,9 +614,12 @@ struct K1Smem {
       uint32_t hc[NBC + 64];
       unsigned long long cand[NC];  // logits within WC codes of the slice max: index << 16 | bits
       uint32_t ncand;
-      uint4 fvec[NFLAG];        // staged vectors that hold a candidate, and their vector indices
-      uint32_t fidx[NFLAG];
+      uint4 fvec[NWAVE * NFW];  // staged vectors that hold a candidate, and their vector indices
+      uint32_t fidx[NWAVE * NFW];
       uint32_t nflag;
+      uint32_t over;            // a wave could not stage all its candidate-holding vectors
+      float wmax[NWAVE];        // per-wave slice max and candidate floor key (top-k slices)
+      uint32_t wfloor[NWAVE];
     } st;
     struct {               // merge phase
       uint32_t keyms[MAXS1];  // slice max keys
@@ -719,19 +736,26 @@ __device__ __forceinline__ bool window_pass(K1Smem& sm, const uint8_t* row, int 
 // Kept threshold of a top-k row (K <= KC) from the recorded candidates.  Slice s recorded every finite
 // logit with key >= floor_s, so with Fe = max(floor_s, key of the smallest finite value) the merged
 // counts of the codes from the row max down to Fe are exact; the selection succeeds when the kept
-// threshold lies among them.  Also reports whether the row can take K5's candidate path.
-__device__ __forceinline__ bool cand_select(const Params& p, K1Smem& sm, int r, float m, const RowParams& q, uint32_t flo,
-                            uint32_t& thr, float& Z, bool& sparse) {
+// threshold lies among them.  A slice whose record overflowed is read again instead.  Also reports
+// whether the row can take K5's candidate path.
+__device__ __forceinline__ bool cand_select(const Params& p, K1Smem& sm, int r, const uint8_t* row, float m,
+                                            const RowParams& q, uint32_t flo, uint32_t& thr, float& Z,
+                                            bool& sparse) {
   const int tid = threadIdx.x, S = p.S1;
   const uint32_t kinf = key16f(-INFINITY);
   const uint32_t Fe = max(block_max_u32(sm.rs, tid < S ? flo : 0u), kinf + 1u);
   const uint32_t keym = key16f(m);
   const int nb = (int)(keym - Fe) + 1;  // m is finite, so keym >= Fe
-  const bool over = __syncthreads_or(tid < S && sm.u.mg.ncs[tid] > (uint32_t)NC) != 0;
-  if (over || nb > WF) return false;
+  if (nb > WF) return false;
   uint32_t* cnt = sm.u.mg.cnt;
   for (int j = tid; j < nb; j += NT) cnt[j] = 0;
+  // overflowed slices (S <= 64: wave 0 holds one lane per slice); their records are not used
+  const bool ovf = tid < S && sm.u.mg.ncs[tid] > (uint32_t)NC;
+  const unsigned long long om = __ballot(ovf);
+  if (tid == 0) sm.win[2] = (uint32_t)om, sm.win[3] = (uint32_t)(om >> 32);
+  if (ovf) sm.u.mg.ncs[tid] = 0;
   __syncthreads();
+  const unsigned long long omask = ((unsigned long long)sm.win[3] << 32) | sm.win[2];
   for (int base = 0; base < S * NC; base += NT * 4) {
     uint32_t xs[4];
     float fs[4];
@@ -739,6 +763,36 @@ __device__ __forceinline__ bool cand_select(const Params& p, K1Smem& sm, int r, 
 #pragma unroll
     for (int t = 0; t < 4; ++t)
       if (xs[t] != 0xffffffffu) atomicAdd(&cnt[keym - key16f(fs[t])], 1u);
+  }
+  for (unsigned long long om2 = omask; om2 != 0; om2 &= om2 - 1) {
+    const int so = __ffsll((long long)om2) - 1;
+    const int x0 = so * p.L1;
+    const int nvs = min(p.L1, p.V - x0) / BF16::EPV;
+    const uint4* src = (const uint4*)(row + (size_t)x0 * 2);
+    for (int j0 = 0; j0 < nvs; j0 += NT * FVPT) {
+      uint4 vv[FVPT];
+#pragma unroll
+      for (int u = 0; u < FVPT; ++u) {
+        const int j = j0 + tid + u * NT;
+        if (j < nvs) vv[u] = src[j];
+      }
+#pragma unroll
+      for (int u = 0; u < FVPT; ++u) {
+        const int j = j0 + tid + u * NT;
+        if (j < nvs) {
+          const uint32_t bits = cand_bits_ge(vv[u], Fe);
+          if (bits) {
+            const uint32_t wv[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
+#pragma unroll 1
+            for (int e = 0; e < BF16::EPV; ++e)
+              if (bits & (1u << e)) {
+                const uint32_t w = (e >> 1) == 0 ? wv[0] : (e >> 1) == 1 ? wv[1] : (e >> 1) == 2 ? wv[2] : wv[3];
+                atomicAdd(&cnt[keym - key16((e & 1) ? (w >> 16) : (w & 0xffffu))], 1u);
+              }
+          }
+        }
+      }
+    }
   }
   __syncthreads();
   int sel = -1;
@@ -749,7 +803,7 @@ __device__ __forceinline__ bool cand_select(const Params& p, K1Smem& sm, int r, 
   Z = (float)((double)zsel * 0x1p-40);
   uint32_t kc = 0;
   for (int j = tid; j <= sel; j += NT) kc += cnt[j];
-  sparse = block_sum_u32(sm.rs, kc) <= (uint32_t)KMAX;
+  sparse = omask == 0 && block_sum_u32(sm.rs, kc) <= (uint32_t)KMAX;
   return true;
 }
 
@@ -802,7 +856,7 @@ __device__ __forceinline__ void k1_merge(const Params& p, K1Smem& sm, int r, int
     bool done = false;
     const double ztot = (double)sum * 0x1p40;
     if (cmode) {
-      done = cand_select(p, sm, r, m, q, flo, thr, Z, sparse);
+      done = cand_select(p, sm, r, row_ptr(p, b, i, esize), m, q, flo, thr, Z, sparse);
     } else if (BF) {
       const uint32_t keym = key16f(m);
       // merged counts of the row's top WTOP codes: entry co is code keym - co.  Slice s's word tid holds
@@ -1002,61 +1056,80 @@ __device__ __forceinline__ void k1_hist(K1Smem& sm, const uint4 (&v)[VPT], int n
   }
 }
 
-// Bit e set: entry e of a bf16 vector has key >= fe.
-__device__ inline uint32_t cand_bits_ge(const uint4& v, uint32_t fe) {
-  const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-  uint32_t bits = 0;
+// Exclusive prefix over the lanes of a wave of per-lane counts cnt < 16, and their total.
+__device__ inline uint32_t wave_excl_prefix(uint32_t cnt, uint32_t& total) {
+  uint32_t excl = 0;
+  total = 0;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t k2 = key16x2(wv[q]);
-    bits |= ((k2 & 0xffffu) >= fe ? 1u : 0u) << (2 * q);
-    bits |= ((k2 >> 16) >= fe ? 1u : 0u) << (2 * q + 1);
+  for (int bit = 0; bit < 4; ++bit) {
+    const unsigned long long mk = __ballot((cnt >> bit) & 1u);
+    excl += __builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u)) << bit;
+    total += (uint32_t)__popcll(mk) << bit;
   }
-  return bits;
+  return excl;
 }
 
-// Candidates of a top-k slice: every logit with key >= fe (index and raw bits).  vm holds the vector
-// maxima; vectors whose maximum reaches fe are staged in LDS, then one thread per staged vector
-// appends its candidates.  More than NFLAG staged vectors, or more than NC candidates, leave ncand
-// above NC: the slice then has no usable candidate list.
+// Largest 16-bit key t with at least kth lanes of the wave holding a key >= t (the wave's kth largest
+// key); bit by bit from the top, one ballot each.
+__device__ inline uint32_t wave_kth_key(uint32_t key, int kth) {
+  uint32_t t = 0;
+#pragma unroll
+  for (int bit = 15; bit >= 0; --bit) {
+    const uint32_t c = t | (1u << bit);
+    if (__popcll(__ballot(key >= c)) >= (unsigned)kth) t = c;
+  }
+  return t;
+}
+
+// Candidates of a top-k slice: every logit with key >= fe, written (index << 16 | bits) to the slice's
+// record in the workspace.  vm holds the vector maxima.  Each wave stages its own vectors whose maximum
+// reaches fe in its LDS region, then one lane per staged vector appends that vector's candidates, with
+// one slot reservation per wave.  A wave with more than NFW such vectors sets `over`; more than NC
+// candidates leave ncand above NC.  Either way the slice has no usable record.
 template <int VPT>
-__device__ __forceinline__ void k1_capture(K1Smem& sm, const uint4 (&v)[VPT], const float (&vm)[VPT], int x0, uint32_t fe) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void k1_capture(const Params& p, K1Smem& sm, const uint4 (&v)[VPT], const float (&vm)[VPT],
+                                           int x0, int r, int s, uint32_t fe) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float fcand = key16_value(fe);
   uint32_t cmask = 0;
 #pragma unroll
   for (int u = 0; u < VPT; ++u) cmask |= (vm[u] >= fcand ? 1u : 0u) << u;
-  if (__ballot(cmask != 0) != 0) {
-    uint32_t at = wave_reserve(&sm.u.st.nflag, (uint32_t)__popc(cmask));
+  uint32_t total;
+  uint32_t at = wave_excl_prefix((uint32_t)__popc(cmask), total);
+  if (total == 0) return;
+  if (total > (uint32_t)NFW) {
+    if (lane == 0) sm.u.st.over = 1;
+    return;
+  }
+  uint4* fv = sm.u.st.fvec + wave * NFW;
+  uint32_t* fi = sm.u.st.fidx + wave * NFW;
 #pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      if (cmask & (1u << u)) {
-        if (at < (uint32_t)NFLAG) {
-          sm.u.st.fvec[at] = v[u];
-          sm.u.st.fidx[at] = (uint32_t)(tid + u * NT);
-        }
-        ++at;
-      }
+  for (int u = 0; u < VPT; ++u) {
+    if (cmask & (1u << u)) {
+      fv[at] = v[u];
+      fi[at] = (uint32_t)(tid + u * NT);
+      ++at;
     }
   }
-  __syncthreads();
-  const uint32_t nflag = sm.u.st.nflag;
-  if (nflag > (uint32_t)NFLAG) {
-    if (tid == 0) sm.u.st.ncand = NC + 1;
-  } else if ((uint32_t)(tid & ~63) < nflag) {  // waves holding a staged vector
-    const bool mine = (uint32_t)tid < nflag;
-    const uint4 vv = mine ? sm.u.st.fvec[tid] : make_uint4(0u, 0u, 0u, 0u);
-    const uint32_t bits = mine ? cand_bits_ge(vv, fe) : 0u;
-    const int xb = x0 + (mine ? (int)sm.u.st.fidx[tid] : 0) * BF16::EPV;
-    uint32_t c = wave_reserve(&sm.u.st.ncand, (uint32_t)__popc(bits));
-    const uint32_t wv[4] = {vv.x, vv.y, vv.z, vv.w};
+  // the wave reads back what its lanes wrote: LDS operations of one wave complete in order
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const bool mine = (uint32_t)lane < total;
+  const uint4 vv = mine ? fv[lane] : make_uint4(0u, 0u, 0u, 0u);
+  const uint32_t bits = mine ? cand_bits_ge(vv, fe) : 0u;
+  const int xb = x0 + (mine ? (int)fi[lane] : 0) * BF16::EPV;
+  uint32_t c = wave_reserve(&sm.u.st.ncand, (uint32_t)__popc(bits));
+  unsigned long long* dst = p.cand1 + ((size_t)r * p.S1 + s) * NC;
+  const uint32_t wv[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
-    for (int e = 0; e < BF16::EPV; ++e) {
-      if (bits & (1u << e)) {
-        const uint32_t h = (e & 1) ? (wv[e >> 1] >> 16) : (wv[e >> 1] & 0xffffu);
-        if (c < (uint32_t)NC) sm.u.st.cand[c] = ((unsigned long long)(xb + e) << 16) | h;
-        ++c;
-      }
+  for (int e = 0; e < BF16::EPV; ++e) {
+    if (bits & (1u << e)) {
+      const uint32_t h = (e & 1) ? (wv[e >> 1] >> 16) : (wv[e >> 1] & 0xffffu);
+      if (c < (uint32_t)NC)
+        __hip_atomic_store(dst + c, ((unsigned long long)(xb + e) << 16) | h, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      ++c;
     }
   }
 }
@@ -1110,9 +1183,11 @@ __device__ __forceinline__ void k1_item(const Params& p, K1Smem& sm, int item, i
     }
     fl = (nan || m == INFINITY) ? 1u : 0u;
   } else if (BF && q.cand) {
-    // Top-k row with K <= KC: no histograms.  The slice records every logit at or above a floor that
-    // lies at or below its KC-th largest thread maximum; at least KC distinct logits reach that, so the
-    // slice's top KC logits are all recorded, and the merge selects the kept threshold from the records.
+    // Top-k row with K <= KC: no histograms.  The slice records every logit at or above a floor: the
+    // smallest over the waves of each wave's (KC / NWAVE)-th largest thread maximum.  At least KC
+    // distinct logits reach it, so the slice's top KC logits are all recorded, and the merge selects
+    // the kept threshold from the records.
+    const int lane = tid & 63, wave = tid >> 6;
     float vm[VPT];
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
@@ -1127,33 +1202,32 @@ __device__ __forceinline__ void k1_item(const Params& p, K1Smem& sm, int item, i
       }
     }
     SV_TRACE_AT(p, item, 1);
-    sm.u.st.hc[tid] = 0;
     if (tid == 0) {
       sm.u.st.ncand = 0;
-      sm.u.st.nflag = 0;
+      sm.u.st.over = 0;
     }
-    const float ms = block_nan_max(sm.rs, m);  // its barriers also publish the cleared counts
+    float wm = m;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) wm = nan_max(wm, __shfl_xor(wm, o, 64));
+    const uint32_t wf = wave_kth_key(key16f(m), KC / NWAVE);
+    if (lane == 0) {
+      sm.u.st.wmax[wave] = wm;
+      sm.u.st.wfloor[wave] = wf;
+    }
+    __syncthreads();
+    float ms = sm.u.st.wmax[0];
+    uint32_t fk = sm.u.st.wfloor[0];
+#pragma unroll
+    for (int w = 1; w < NWAVE; ++w) {
+      ms = nan_max(ms, sm.u.st.wmax[w]);
+      fk = min(fk, sm.u.st.wfloor[w]);
+    }
     const uint32_t kinf = key16f(-INFINITY);
     if (ms > -INFINITY && ms < INFINITY) {  // not NaN, +inf or an all -inf slice
-      // thread maxima binned by their distance below the slice max, BRC bins per unit, NT bins
-      atomicAdd(&sm.u.st.hc[(int)fminf(floorf((ms - m) * BRC), (float)(NT - 1))], 1u);
-      __syncthreads();
-      const uint32_t incl = block_inclusive_scan<uint32_t>(sm.u.st.hc[tid], sm.rs.scan32);
-      const int bstar = block_first(sm.rs, incl >= (uint32_t)KC);  // the bin holding the KC-th maximum
-      // one bin of margin for rounding; then the largest bf16 at or below that value
-      const uint32_t fu = __float_as_uint(ms - (float)(bstar + 2) * (1.0f / BRC));
-      const uint32_t fh = (fu >> 16) + ((fu & 0x8000ffffu) > 0x80000000u ? 1u : 0u);
-      flo = max(key16(fh), kinf);
-      k1_capture<VPT>(sm, v, vm, x0, max(flo, kinf + 1u));
+      flo = max(fk, kinf);
+      k1_capture<VPT>(p, sm, v, vm, x0, r, s, max(flo, kinf + 1u));
     }
     m = ms;
-    __syncthreads();
-    const uint32_t nc = sm.u.st.ncand;
-    if (tid < (int)min(nc, (uint32_t)NC)) {
-      unsigned long long* cd = p.cand1 + ((size_t)r * p.S1 + s) * NC + tid;
-      __hip_atomic_store(cd, sm.u.st.cand[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (tid == 0) st32(&p.ncand1[(size_t)r * p.S1 + s], nc);
     if (!(m == m) || m == INFINITY) fl = 1u;
   } else {
     // NaN-propagating max: a NaN or +inf anywhere shows in the row max
@@ -1223,6 +1297,7 @@ __device__ __forceinline__ void k1_item(const Params& p, K1Smem& sm, int item, i
     st32(&sp->flags, fl);
     stf(&sp->g, gval);
     st32(&sp->floor, flo);
+    if (BF && q.cand) st32(&p.ncand1[(size_t)r * p.S1 + s], sm.u.st.over ? (uint32_t)NC + 1u : sm.u.st.ncand);
   }
   SV_TRACE_AT(p, item, 2);
   if (arrive_last(&p.cnt1[r], (uint32_t)p.S1, &sm.rs.flag)) {
