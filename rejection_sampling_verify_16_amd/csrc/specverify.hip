@@ -477,6 +477,7 @@ __device__ __forceinline__ void row_cutoff(RadixSmem& sm, RedSmem& rs, const uin
 // ---------------------------------------------------------------------------------------------
 struct SelState {
   int32_t sel_k, sel_p;
+  uint32_t ck;  // entries at or above the top-k cut
   unsigned long long zk, zp;
 };
 
@@ -510,9 +511,11 @@ __device__ __forceinline__ bool select_run(const uint32_t* cnt, int n, uint32_t 
       if (i0 < n && e0 < (uint32_t)K && e0 + a0 >= (uint32_t)K) {
         ss.sel_k = i0;
         ss.zk = f0 + b0;
+        ss.ck = e0 + a0;
       } else if (i1 < n && e0 + a0 < (uint32_t)K && ic >= (uint32_t)K) {
         ss.sel_k = i1;
         ss.zk = im;
+        ss.ck = ic;
       }
       if (tid == NT - 1) {
         rs.u[0] = ic;
@@ -801,9 +804,7 @@ __device__ __forceinline__ bool cand_select(const Params& p, K1Smem& sm, int r, 
     return false;
   thr = keym - (uint32_t)sel;
   Z = (float)((double)zsel * 0x1p-40);
-  uint32_t kc = 0;
-  for (int j = tid; j <= sel; j += NT) kc += cnt[j];
-  sparse = omask == 0 && block_sum_u32(sm.rs, kc) <= (uint32_t)KMAX;
+  sparse = omask == 0 && sm.ss.ck <= (uint32_t)KMAX;  // top-p only shrinks the top-k set
   return true;
 }
 
