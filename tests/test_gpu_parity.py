@@ -90,6 +90,9 @@ SMALL = [
     ("f32_greedy", 6, 3, 8192, "f32", dict(temperature=0.0, tie_fraction=0.2)),
     ("min_V", 3, 1, 8, "bf16", dict(temperature=1.0)),
     ("k1_T2", 16, 1, 32768, "bf16", dict(temperature=2.0, top_k=1000, top_p=0.99)),
+    # the largest vocabulary: 64 slices per bf16 row (the candidate records' limit), 128 per fp32 row
+    ("maxV_bf16_mixed", 4, 2, 1 << 20, "bf16", dict(boost=8.0, mixed_params=True)),
+    ("maxV_f32_topk", 2, 1, 1 << 20, "f32", dict(temperature=0.8, top_k=40, top_p=0.9)),
 ]
 
 
