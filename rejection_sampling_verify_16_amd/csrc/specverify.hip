@@ -51,7 +51,6 @@ constexpr int MAXDEV = 64;
 constexpr int VPT1 = 8;         // K1: 16-byte vectors per thread per slice
 constexpr int VPT5 = 2;         // K5
 constexpr int OCC1 = 7;         // K1 workgroups per CU (register budget of its launch bounds)
-constexpr int OCC5 = 4;         // K5 workgroups per CU
 constexpr int FVPT = 2;         // whole-row passes of one workgroup: vectors per thread per step
 constexpr int WTOP = 512;       // K1: exact per-code window below the slice max
 constexpr int NBC = 256;        // K1: weight bins of top-p-only rows
@@ -1621,26 +1620,19 @@ __device__ __forceinline__ void k5_position(const Params& p, K5Smem& sm, int b, 
   if (lane == 0) sm.wacc[i][wave] = acc;
 }
 
-// Every draft position of this slice, two positions' slices in flight: (a0, b0) and (a1, b1) hold
-// positions 0 and 1 on entry; position i + 2 is loaded into the pair that position i has just used.
+// Every draft position of this slice, one position's slices at a time: (a0, b0) hold position 0 on
+// entry, and position i + 1 is loaded once position i is done.  A second pair in flight would need 16
+// more VGPRs and cost a workgroup per CU (4 instead of 5), which loses more than the overlap gains.
 template <class E, int VPT, bool TRUNC>
-__device__ __forceinline__ void k5_positions(const Params& p, K5Smem& sm, int b, int n, int x0, int nv, float c, uint4 (&a0)[VPT],
-                             uint4 (&b0)[VPT], uint4 (&a1)[VPT], uint4 (&b1)[VPT], float& best, int& bidx,
-                             float& bval) {
+__device__ __forceinline__ void k5_positions(const Params& p, K5Smem& sm, int b, int n, int x0, int nv, float c,
+                                             uint4 (&a0)[VPT], uint4 (&b0)[VPT], float& best, int& bidx, float& bval) {
   constexpr int esize = 16 / E::EPV;
   const int k = p.k;
-  for (int i = 0; i < k; i += 2) {
+  for (int i = 0; i < k; ++i) {
     k5_position<E, VPT, TRUNC>(p, sm, b, i, n, x0, nv, c, a0, b0, best, bidx, bval);
-    if (i + 2 < k) {
-      load_slice<E, VPT>(row_ptr(p, b, i + 2, esize), x0, nv, a0);
-      load_slice<E, VPT>(row_ptr(p, b, k + 3 + i, esize), x0, nv, b0);
-    }
     if (i + 1 < k) {
-      k5_position<E, VPT, TRUNC>(p, sm, b, i + 1, n, x0, nv, c, a1, b1, best, bidx, bval);
-      if (i + 3 < k) {
-        load_slice<E, VPT>(row_ptr(p, b, i + 3, esize), x0, nv, a1);
-        load_slice<E, VPT>(row_ptr(p, b, k + 4 + i, esize), x0, nv, b1);
-      }
+      load_slice<E, VPT>(row_ptr(p, b, i + 1, esize), x0, nv, a0);
+      load_slice<E, VPT>(row_ptr(p, b, k + 2 + i, esize), x0, nv, b0);
     }
   }
 }
@@ -1819,19 +1811,13 @@ __device__ __forceinline__ void k5_item(const Params& p, K5Smem& sm, int item, i
   const int x0 = s * p.L5;
   const int nv = min(p.L5, p.V - x0) / EPV;
   const RowParams q = row_params(p, b);
-  // Everything else independent is issued at once: the first two positions' slices, the rows'
+  // Everything else independent is issued at once: the first position's slices, the rows'
   // statistics (with the logits at the draft tokens), the draft tokens and the accept uniforms.
   // Truncated rows wait for their statistics: they may take the candidate path instead.
-  uint4 a0[VPT], b0[VPT], a1[VPT], b1[VPT];
-  if (!q.greedy && !q.trunc) {
-    if (k > 0) {
-      load_slice<E, VPT>(row_ptr(p, b, 0, esize), x0, nv, a0);
-      load_slice<E, VPT>(row_ptr(p, b, k + 1, esize), x0, nv, b0);
-    }
-    if (k > 1) {
-      load_slice<E, VPT>(row_ptr(p, b, 1, esize), x0, nv, a1);
-      load_slice<E, VPT>(row_ptr(p, b, k + 2, esize), x0, nv, b1);
-    }
+  uint4 a0[VPT], b0[VPT];
+  if (!q.greedy && !q.trunc && k > 0) {
+    load_slice<E, VPT>(row_ptr(p, b, 0, esize), x0, nv, a0);
+    load_slice<E, VPT>(row_ptr(p, b, k + 1, esize), x0, nv, b0);
   }
   if (tid < rows) {
     const RowInfo* ri = p.rinfo + (size_t)b * rows + tid;
@@ -1862,15 +1848,9 @@ __device__ __forceinline__ void k5_item(const Params& p, K5Smem& sm, int item, i
     SV_TRACE5_AT(p, item, 7);
     return;
   }
-  if (ok && q.trunc && !q.greedy && !sparse) {  // truncated rows streamed after all: their first slices
-    if (k > 0) {
-      load_slice<E, VPT>(row_ptr(p, b, 0, esize), x0, nv, a0);
-      load_slice<E, VPT>(row_ptr(p, b, k + 1, esize), x0, nv, b0);
-    }
-    if (k > 1) {
-      load_slice<E, VPT>(row_ptr(p, b, 1, esize), x0, nv, a1);
-      load_slice<E, VPT>(row_ptr(p, b, k + 2, esize), x0, nv, b1);
-    }
+  if (ok && q.trunc && !q.greedy && !sparse && k > 0) {  // truncated rows streamed after all
+    load_slice<E, VPT>(row_ptr(p, b, 0, esize), x0, nv, a0);
+    load_slice<E, VPT>(row_ptr(p, b, k + 1, esize), x0, nv, b0);
   }
   if (ok && !q.greedy) {
     // accept decisions of all positions at once (lane i of wave 0); n = the first rejection, else k
@@ -1905,9 +1885,9 @@ __device__ __forceinline__ void k5_item(const Params& p, K5Smem& sm, int item, i
     float best = 0.0f, bval = 0.0f;
     int bidx = INT_MAX;
     if (q.trunc)
-      k5_positions<E, VPT, true>(p, sm, b, n, x0, nv, q.c, a0, b0, a1, b1, best, bidx, bval);
+      k5_positions<E, VPT, true>(p, sm, b, n, x0, nv, q.c, a0, b0, best, bidx, bval);
     else
-      k5_positions<E, VPT, false>(p, sm, b, n, x0, nv, q.c, a0, b0, a1, b1, best, bidx, bval);
+      k5_positions<E, VPT, false>(p, sm, b, n, x0, nv, q.c, a0, b0, best, bidx, bval);
     if (n == k) {
       // bonus draw from p_k (verify stream), or the plain sampler's draw (its own stream)
       const bool smp = p.mode == MODE_SAMPLE;
@@ -2021,13 +2001,6 @@ static bool device_ok(int dev, int& cus) {
 
 static void prof_mark(int idx, hipStream_t st) {
   if (g_prof[idx]) (void)hipEventRecord(g_prof[idx], st);
-}
-
-// Persistent grid: one workgroup per resident slot, a multiple of 8 (one per XCD), no more than items.
-static unsigned grid_for(long long items, int cus, int occ) {
-  long long g = std::min(items, (long long)cus * occ);
-  if (g >= 8) g &= ~7ll;
-  return (unsigned)std::max(g, 1ll);
 }
 
 template <class E>
