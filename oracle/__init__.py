@@ -103,6 +103,8 @@ class Oracle:
         L.oracle_spec_verify.restype = ctypes.c_int
         L.oracle_sample.argtypes = [_P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _U64, _U64, _P, _P, _P, _I32]
         L.oracle_sample.restype = ctypes.c_int
+        L.oracle_raw_logprobs.argtypes = [_P, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _I32]
+        L.oracle_raw_logprobs.restype = ctypes.c_int
 
     # -- random streams ---------------------------------------------------------------
     def philox(self, ctr, key) -> np.ndarray:
@@ -164,6 +166,30 @@ class Oracle:
             raise ValueError("oracle_spec_verify rejected its scalar arguments")
         return VerifyResult(tokens, acc, lp, al, diag[:, 0].copy(), diag[:, 1].copy(), diag[:, 2].copy(),
                             diag[:, 3].copy(), (fl & 1) != 0, (fl & 2) != 0, (fl >> 8).astype(np.int32))
+
+    # -- raw logprobs of the committed tokens --------------------------------------------
+    def raw_logprobs(self, target, tokens, accept_len, temperature=None, num_threads: int = 0) -> np.ndarray:
+        """ln softmax of each committed position's unprocessed target logits at its token: float64 [B, k+1]
+        (0 after the committed slots, NaN for rows with accept_len 0).  ``temperature`` only feeds a
+        negative-control mutant; the definition does not use it."""
+        target = np.ascontiguousarray(target)
+        if target.dtype == np.uint16:
+            dtype = DTYPE_BF16
+        elif target.dtype == np.float32:
+            dtype = DTYPE_F32
+        else:
+            raise TypeError("logits must be uint16 (bf16 bits) or float32")
+        B, k1, V = target.shape
+        tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(B, k1))
+        acc = np.ascontiguousarray(np.asarray(accept_len, dtype=np.int32).reshape(B))
+        T = np.ascontiguousarray(np.ones(B, np.float32) if temperature is None
+                                 else np.asarray(temperature, dtype=np.float32).reshape(B))
+        out = np.zeros((B, k1), dtype=np.float64)
+        rc = self.lib.oracle_raw_logprobs(_ptr(target), dtype, _ptr(tok), _ptr(acc), B, k1 - 1, V, _ptr(T),
+                                          _ptr(out), int(num_threads))
+        if rc != 0:
+            raise ValueError("oracle_raw_logprobs rejected its arguments")
+        return out
 
     # -- plain sampler ---------------------------------------------------------------------
     def sample(self, logits, temperature, top_k, top_p, row_b, row_pos, seed: int = 0, offset: int = 0,

@@ -508,6 +508,50 @@ int oracle_spec_verify(const void* target_logits, const void* draft_logits, int3
   return 0;
 }
 
+// The raw logprob of each committed token: the natural-log softmax of its position's unprocessed target
+// logits (no temperature, no truncation), the other reading of the logprobs that plain sampling reports
+// (AReno pull request "feat(engine): MTP training loss and speculative decoding for bailing_v3", section
+// "What does this PR do?", Phase-2 paragraph: speculative decoding leaves them unchanged).  Slots after
+// the committed ones are 0; sentinel rows (accept_len 0) are NaN.
+int oracle_raw_logprobs(const void* target_logits, int32_t dtype, const int32_t* tokens, const int32_t* accept_len,
+                        int32_t B, int32_t k, int32_t V, const float* temperature, double* out,
+                        int32_t num_threads) {
+  if (B < 1 || k < 0 || V < 1) return 1;
+  if (dtype != ORACLE_DTYPE_BF16 && dtype != ORACLE_DTYPE_F32) return 1;
+  parallel_rows(B, num_threads, [&](int32_t b) {
+    const int32_t committed = accept_len[b];
+    std::vector<double> l;
+    for (int32_t i = 0; i <= k; ++i) {
+      const size_t o = (size_t)b * (k + 1) + i;
+      if (committed == 0) {
+        out[o] = kNaN;
+        continue;
+      }
+      if (i >= committed) {
+        out[o] = 0.0;
+        continue;
+      }
+      load_row(target_logits, dtype, (size_t)b * (k + 1) + i, V, l);
+#if ORACLE_MUTANT == 15
+      for (double& v : l) v /= (double)temperature[b];  // MUTANT 15: the temperature is applied
+#else
+      (void)temperature;
+#endif
+      double m = -kInf;
+      for (int32_t x = 0; x < V; ++x) m = std::max(m, l[(size_t)x]);
+      double s = 0.0;
+      for (int32_t x = 0; x < V; ++x) s += std::exp(l[(size_t)x] - m);
+      const int32_t y = tokens[o];
+#if ORACLE_MUTANT == 14
+      out[o] = (l[(size_t)y] - m) / std::log(2.0) - std::log2(s);  // MUTANT 14: base-2 logarithm
+#else
+      out[o] = (l[(size_t)y] - m) - std::log(s);
+#endif
+    }
+  });
+  return 0;
+}
+
 int oracle_sample(const void* logits, int32_t dtype, const float* temperature, const int32_t* top_k,
                   const float* top_p, const int32_t* row_b, const int32_t* row_pos, int32_t R, int32_t V,
                   uint64_t seed, uint64_t offset, int32_t* tokens, double* logprobs, double* gap,

@@ -390,6 +390,43 @@ def _check_logprobs(r, t, B, k, T, K, P):
                 assert r.tokens[b, i] == -1 and r.logprobs[b, i] == 0.0
 
 
+def pin_raw_logprobs(o):
+    """Raw logprobs are ln softmax of the unprocessed target logits at each committed token, whatever the
+    sampling parameters: closed forms (a uniform row gives -ln V; a row with one raised entry gives
+    a - ln(e^a + (V-1))), scipy's log_softmax on random rows at T != 1 with truncation, equality with the
+    processed logprobs when T = 1 without truncation, NaN for sentinel rows and 0 after the committed slots."""
+    V = 64
+    flat = np.zeros((1, 2, V), np.float32)
+    got = o.raw_logprobs(flat, np.array([[3, 9]]), np.array([2]), temperature=np.array([0.5], np.float32))
+    np.testing.assert_allclose(got, [[-math.log(V), -math.log(V)]], rtol=0, atol=1e-15)
+    a = 2.5
+    two = np.zeros((1, 2, V), np.float32)
+    two[0, :, 7] = a
+    got = o.raw_logprobs(two, np.array([[7, 8]]), np.array([2]), temperature=np.array([2.0], np.float32))
+    z = math.exp(a) + (V - 1)
+    np.testing.assert_allclose(got, [[a - math.log(z), -math.log(z)]], rtol=0, atol=1e-14)
+    got = o.raw_logprobs(two, np.array([[7, -1]]), np.array([1]))
+    assert got[0, 1] == 0.0
+    got = o.raw_logprobs(two, np.array([[-1, -1]]), np.array([0]))
+    assert np.all(np.isnan(got))
+    rng = np.random.default_rng(52)
+    B, k, V = 40, 2, 30
+    t, d = _tiny_case(rng, B, k, V, 1.5, 0.9)
+    for T, K, P in ((1.0, 0, 1.0), (0.7, 8, 0.85)):
+        Ta, Ka, Pa = _params(B, T, K, P)
+        r = o.spec_verify(t, d, _fresh_drafts(o, d, Ta, Ka, Pa), Ta, Ka, Pa, seed=4)
+        raw = o.raw_logprobs(t, r.tokens, r.accept_len, temperature=Ta)
+        for b in range(B):
+            for i in range(k + 1):
+                if i < r.accept_len[b]:
+                    ref = special.log_softmax(t[b, i].astype(np.float64))[r.tokens[b, i]]
+                    np.testing.assert_allclose(raw[b, i], ref, rtol=0, atol=1e-12)
+                    if T == 1.0 and K == 0 and P == 1.0:
+                        np.testing.assert_allclose(raw[b, i], r.logprobs[b, i], rtol=0, atol=1e-12)
+                else:
+                    assert raw[b, i] == 0.0
+
+
 def pin_residual_mass(o):
     """At a rejection, the residual mass equals 1 - alpha at that position."""
     rng = np.random.default_rng(52)

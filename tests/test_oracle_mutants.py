@@ -4,14 +4,15 @@ Each mutant is the oracle built with -DORACLE_MUTANT=<n>, which changes one step
 (swapped p/q in the accept test, resampling from p instead of the residual, strict top-p
 inequality, highest-index ties, no renormalisation after top-k, accept length without
 the extra token, wrong alpha, wrong Gumbel sign, temperature multiplying, top-k off by
-one, Philox one round short, bonus at the wrong position, residual without the clamp).
+one, Philox one round short, bonus at the wrong position, residual without the clamp, raw logprobs
+in base 2, raw logprobs with the temperature applied).
 """
 import pytest
 
 import oracle
 import oracle_pins
 
-MUTANTS = list(range(1, 14))
+MUTANTS = list(range(1, 16))
 
 
 @pytest.mark.parametrize("mutant", MUTANTS)
