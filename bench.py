@@ -59,6 +59,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--config", default="3", help="workload: 1, 2, 3, 4a, 4b, 5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--raw-logprobs", action="store_true",
+                    help="time spec_verify_raw (also the raw logprobs of the committed tokens)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, 5 times (PMC calibration)")
@@ -113,7 +115,7 @@ def main():
 
     n_sets = max(2, math.ceil(ROTATE_BYTES / w.logit_bytes))
     sets = [(tgt0, drf0)] + [(tgt0.clone(), drf0.clone()) for _ in range(n_sets - 1)]
-    out = sv.alloc_outputs(B, k, dev)
+    out = sv.alloc_outputs(B, k, dev, raw=args.raw_logprobs)
     ws = sv.make_workspace(B, k, V, sv.SPEC_DTYPE_BF16 if bf16 else sv.SPEC_DTYPE_F32, dev)
     stream = torch.cuda.current_stream(dev)
     offsets = w.offsets
@@ -121,7 +123,7 @@ def main():
     def step(i):
         t_, d_ = sets[i % n_sets]
         sv.spec_verify(t_, d_, drafts, T, K, P, seed=w.seed, offset=offsets[i % len(offsets)], out=out,
-                       workspace=ws, stream=stream)
+                       workspace=ws, stream=stream, raw=args.raw_logprobs)
 
     for i in range(args.warmup):
         step(i)
@@ -163,6 +165,7 @@ def main():
         "dtype": "bf16" if bf16 else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "k": k, "V": V, "logit_bytes_per_step": logit_bytes,
+                   "raw_logprobs": bool(args.raw_logprobs),
                    "rotating_input_sets": n_sets},
         "logits_GBps": logit_bytes / (ms_per_step * 1e-3) / 1e9,
         "pct_hbm_peak": 100.0 * logit_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,

@@ -88,6 +88,25 @@ spec_status_t spec_verify(const void* target_logits, const void* draft_logits, s
                           size_t workspace_bytes, void* stream);
 
 /*
+ * The verify step with raw logprobs as well: spec_verify's arguments and outputs, plus
+ *
+ *   raw_logprobs   out float [B, k+1]  for i <= n: ln softmax of target row i's unprocessed logits (no
+ *                                     temperature, no truncation) at tokens[b,i]; 0 after; NaN for a
+ *                                     sentinel row
+ *
+ * This is the other reading of "the reported logprobs" that speculative decoding leaves unchanged (AReno
+ * pull request above, section "What does this PR do?", Phase-2 paragraph): the model's own log-probability
+ * of each committed token rather than its log-probability under the sampler distribution.  Greedy rows
+ * get a finite value too.  It costs an extra exp per target logit in the statistics kernel.
+ * raw_logprobs must not be NULL (SPEC_ERR_INVALID_ARGUMENT); the workspace is spec_verify's.
+ */
+spec_status_t spec_verify_raw(const void* target_logits, const void* draft_logits, spec_dtype_t dtype,
+                              const int32_t* draft_tokens, const float* temperature, const int32_t* top_k,
+                              const float* top_p, int32_t B, int32_t k, int32_t V, uint64_t seed, uint64_t offset,
+                              int32_t* tokens, int32_t* accept_len, float* logprobs, float* raw_logprobs,
+                              float* alpha, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Plain (non-speculative) sampler: one token per logit row from the same sampler distribution
  * (temperature, top-k, top-p as above) by Gumbel-max on the plain-sampler stream.  This is the step
  * either side of verify: it draws the draft tokens from q, and it is what "sampler-equivalent" refers

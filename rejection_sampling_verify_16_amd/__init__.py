@@ -39,7 +39,10 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_workspace_size.argtypes = [I32, I32, I32, ctypes.c_int]
         L.spec_verify_workspace_size.restype = SZ
         L.spec_verify.argtypes = [P, P, ctypes.c_int, P, P, P, P, I32, I32, I32, U64, U64, P, P, P, P, P, SZ, P]
+        L.spec_verify_raw.argtypes = [P, P, ctypes.c_int, P, P, P, P, I32, I32, I32, U64, U64, P, P, P, P, P, P,
+                                      SZ, P]
         L.spec_verify.restype = ctypes.c_int
+        L.spec_verify_raw.restype = ctypes.c_int
         L.spec_sample_workspace_size.argtypes = [I32, I32, ctypes.c_int]
         L.spec_sample_workspace_size.restype = SZ
         L.spec_sample.argtypes = [P, ctypes.c_int, P, P, P, P, P, I32, I32, U64, U64, P, P, P, SZ, P]
@@ -74,22 +77,27 @@ def make_workspace(B: int, k: int, V: int, dtype: int = SPEC_DTYPE_BF16, device=
     return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
-def alloc_outputs(B: int, k: int, device="cuda"):
+def alloc_outputs(B: int, k: int, device="cuda", raw: bool = False):
     import torch
-    return dict(tokens=torch.empty((B, k + 1), dtype=torch.int32, device=device),
-                accept_len=torch.empty((B,), dtype=torch.int32, device=device),
-                logprobs=torch.empty((B, k + 1), dtype=torch.float32, device=device),
-                alpha=torch.empty((B, k), dtype=torch.float32, device=device))
+    out = dict(tokens=torch.empty((B, k + 1), dtype=torch.int32, device=device),
+               accept_len=torch.empty((B,), dtype=torch.int32, device=device),
+               logprobs=torch.empty((B, k + 1), dtype=torch.float32, device=device),
+               alpha=torch.empty((B, k), dtype=torch.float32, device=device))
+    if raw:
+        out["raw_logprobs"] = torch.empty((B, k + 1), dtype=torch.float32, device=device)
+    return out
 
 
 def spec_verify(target_logits, draft_logits, draft_tokens, temperature, top_k, top_p, seed: int = 0,
-                offset: int = 0, out=None, workspace=None, stream=None):
+                offset: int = 0, out=None, workspace=None, stream=None, raw: bool = False):
     """Run the verify step on device tensors; returns a dict of output tensors.
 
     target_logits [B, k+1, V] and draft_logits [B, k, V] (bf16 or fp32, contiguous, same device),
     draft_tokens int32 [B, k], temperature float32 [B], top_k int32 [B], top_p float32 [B].
     ``out`` (from alloc_outputs) and ``workspace`` (from make_workspace) may be passed in to
-    avoid allocations; ``stream`` defaults to torch's current stream.
+    avoid allocations; ``stream`` defaults to torch's current stream.  ``raw=True`` calls
+    spec_verify_raw and adds "raw_logprobs" (ln softmax of the unprocessed target logits at each
+    committed token).
     """
     import torch
     B, k1, V = target_logits.shape
@@ -99,16 +107,21 @@ def spec_verify(target_logits, draft_logits, draft_tokens, temperature, top_k, t
         if not t.is_contiguous():
             raise ValueError("all inputs must be contiguous")
     if out is None:
-        out = alloc_outputs(B, k, target_logits.device)
+        out = alloc_outputs(B, k, target_logits.device, raw=raw)
+    if raw and "raw_logprobs" not in out:
+        raise ValueError("raw=True needs out['raw_logprobs'] (alloc_outputs(..., raw=True))")
     if workspace is None:
         workspace = make_workspace(B, k, V, dt, target_logits.device)
     if stream is None:
         stream = torch.cuda.current_stream(target_logits.device)
-    st = lib().spec_verify(target_logits.data_ptr(), draft_logits.data_ptr(), dt, draft_tokens.data_ptr(),
-                           temperature.data_ptr(), top_k.data_ptr(), top_p.data_ptr(), B, k, V, int(seed),
-                           int(offset), out["tokens"].data_ptr(), out["accept_len"].data_ptr(),
-                           out["logprobs"].data_ptr(), out["alpha"].data_ptr(), workspace.data_ptr(),
-                           workspace.numel(), ctypes.c_void_p(stream.cuda_stream))
+    head = (target_logits.data_ptr(), draft_logits.data_ptr(), dt, draft_tokens.data_ptr(), temperature.data_ptr(),
+            top_k.data_ptr(), top_p.data_ptr(), B, k, V, int(seed), int(offset), out["tokens"].data_ptr(),
+            out["accept_len"].data_ptr(), out["logprobs"].data_ptr())
+    tail = (out["alpha"].data_ptr(), workspace.data_ptr(), workspace.numel(), ctypes.c_void_p(stream.cuda_stream))
+    if raw:
+        st = lib().spec_verify_raw(*head, out["raw_logprobs"].data_ptr(), *tail)
+    else:
+        st = lib().spec_verify(*head, *tail)
     if st != 0:
         raise SpecVerifyError(st)
     return out

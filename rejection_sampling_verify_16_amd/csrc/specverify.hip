@@ -79,7 +79,7 @@ struct StatPart {  // K1, per (logit row, slice)
   uint32_t flags;  // bit 0: NaN or +inf seen
   float g;         // the row's logit at its draft token, if the token falls in this slice
   uint32_t floor;  // candidate rows: every finite logit of the slice with key >= floor was recorded
-  uint32_t pad[2];
+  float rmax, rsum;  // raw logprobs requested, target rows: the slice max and sum of exp(l - rmax)
 };
 
 struct RowInfo {    // per logit row
@@ -89,7 +89,7 @@ struct RowInfo {    // per logit row
   float lz;         // log2(Z)
   float fthr;       // smallest kept value (-inf: every entry kept)
   uint32_t state;   // ST_BAD
-  float Ztot;       // whole-row normaliser (rows that needed it)
+  float rlz;        // raw logprobs requested, target rows: log2 of the sum of exp(l - m) (no T, no truncation)
   float gath;       // logit at the draft token of this position (draft-position rows of a valid token)
 };
 
@@ -118,6 +118,7 @@ struct Params {
   int32_t* accept_len;
   float* logprobs;
   float* alpha;
+  float* raw_logprobs;  // NULL, or [B][k+1] raw logprobs of the committed tokens
   uint32_t* cnt1;     // [R] K1 arrivals
   uint32_t* cnt5;     // [B] K5 arrivals
   StatPart* st1;      // [R][S1]
@@ -807,7 +808,7 @@ __device__ __forceinline__ bool cand_select(const Params& p, K1Smem& sm, int r, 
   return true;
 }
 
-template <class E>
+template <class E, bool RAW>
 __device__ __forceinline__ void k1_merge(const Params& p, K1Smem& sm, int r, int b, int i, const RowParams& q) {
   constexpr bool BF = E::KEYBITS == 16;
   constexpr int esize = 16 / E::EPV;
@@ -849,6 +850,21 @@ __device__ __forceinline__ void k1_merge(const Params& p, K1Smem& sm, int r, int
   if (hist && tid < S) sm.u.mg.keyms[tid] = key16f(m);
   block_stats(sm.rs, m, a, sum, fl, q.c);  // its barriers publish keyms / cbs and the cleared counts
   const bool bad = fl != 0 || !(m > -INFINITY) || m == INFINITY;
+  float rlz = 0.0f;
+  if constexpr (RAW) {
+    if (p.mode == MODE_VERIFY && i <= p.k) {  // the row's raw normaliser, relative to its max
+      float rm = -INFINITY, rsm = 0.0f;
+      int ra = INT_MAX;
+      uint32_t rf = 0;
+      if (tid < S) {
+        const StatPart* sp = p.st1 + (size_t)r * S + tid;
+        rm = ldf(&sp->rmax);
+        rsm = ldf(&sp->rsum);
+      }
+      block_stats(sm.rs, rm, ra, rsm, rf, 1.4426950408889634f);
+      rlz = __builtin_amdgcn_logf(rsm) + (rm - m) * 1.4426950408889634f;
+    }
+  }
   uint32_t thr = 0;
   float Z = sum;
   bool sparse = false;
@@ -932,7 +948,7 @@ __device__ __forceinline__ void k1_merge(const Params& p, K1Smem& sm, int r, int
     ri->lz = __builtin_amdgcn_logf(Z);
     ri->fthr = thr == 0 ? -INFINITY : key_value<E>(thr);
     ri->state = bad ? ST_BAD : (sparse ? ST_SPARSE : 0u);
-    ri->Ztot = sum;
+    ri->rlz = rlz;
     ri->gath = sg >= 0 ? __uint_as_float(sm.win[1]) : 0.0f;
     atomicExch(&p.cnt1[r], 0u);
   }
@@ -1135,7 +1151,7 @@ __device__ __forceinline__ void k1_capture(const Params& p, K1Smem& sm, const ui
 }
 
 // One K1 work item: slice s of logit row r.
-template <class E, int VPT>
+template <class E, int VPT, bool RAW>
 __device__ __forceinline__ void k1_item(const Params& p, K1Smem& sm, int item, int r, int s) {
   constexpr int EPV = E::EPV;
   constexpr int esize = 16 / EPV;
@@ -1288,9 +1304,40 @@ __device__ __forceinline__ void k1_item(const Params& p, K1Smem& sm, int item, i
     }
     if (!(m == m) || m == INFINITY) fl = 1u;
   }
+  // raw logprobs: the sum of exp(l - slice max) of target rows, whatever the sampling parameters
+  float rmax = -INFINITY, rsum = 0.0f;
+  if constexpr (RAW) {
+    if (p.mode == MODE_VERIFY && i <= p.k) {
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) {
+        const int j = tid + u * NT;
+        if (j < nv) {
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) rmax = nan_max(rmax, E::get(v[u], e));
+        }
+      }
+      if (rmax > -INFINITY) {
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+          const int j = tid + u * NT;
+          if (j < nv) {
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) rsum += fexp2((E::get(v[u], e) - rmax) * 1.4426950408889634f);
+          }
+        }
+      }
+      int ra = INT_MAX;
+      uint32_t rf = 0;
+      block_stats(sm.rs, rmax, ra, rsum, rf, 1.4426950408889634f);
+    }
+  }
   block_stats(sm.rs, m, a, sum, fl, q.c);
   if (tid == 0) {
     StatPart* sp = p.st1 + (size_t)r * p.S1 + s;
+    if (RAW) {
+      stf(&sp->rmax, rmax);
+      stf(&sp->rsum, rsum);
+    }
     stf(&sp->m, m);
     st32(&sp->arg, (uint32_t)a);
     stf(&sp->s, sum);
@@ -1302,17 +1349,17 @@ __device__ __forceinline__ void k1_item(const Params& p, K1Smem& sm, int item, i
   SV_TRACE_AT(p, item, 2);
   if (arrive_last(&p.cnt1[r], (uint32_t)p.S1, &sm.rs.flag)) {
     SV_TRACE_AT(p, item, 3);
-    k1_merge<E>(p, sm, r, b, i, q);
+    k1_merge<E, RAW>(p, sm, r, b, i, q);
     SV_TRACE_AT(p, item, 7);
   }
 }
 
-template <class E, int VPT>
+template <class E, int VPT, bool RAW>
 __global__ __launch_bounds__(NT, OCC1) void k1_stats(Params p) {
   __shared__ K1Smem sm;
   int r, s;
   item_rs(blockIdx.x, p.R, p.S1, r, s);
-  k1_item<E, VPT>(p, sm, blockIdx.x, r, s);
+  k1_item<E, VPT, RAW>(p, sm, blockIdx.x, r, s);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1320,7 +1367,7 @@ __global__ __launch_bounds__(NT, OCC1) void k1_stats(Params p) {
 // ---------------------------------------------------------------------------------------------
 struct K5Smem {
   RedSmem rs;
-  float m[MAXROWS], Z[MAXROWS], lz[MAXROWS], fthr[MAXROWS], gath[MAXROWS];
+  float m[MAXROWS], Z[MAXROWS], lz[MAXROWS], fthr[MAXROWS], gath[MAXROWS], rlz[MAXROWS];
   int32_t arg[MAXROWS];
   uint32_t state[MAXROWS];
   int32_t tok[MAXK];
@@ -1404,6 +1451,11 @@ __device__ __forceinline__ void gumbel_vec(const uint4& v, int xbase, float m, f
   }
 }
 
+// Raw logprob of a committed token with logit l at position i: ln of the softmax of the unprocessed row.
+__device__ inline float raw_lp(const K5Smem& sm, int i, float l) {
+  return (l - sm.m[i]) - sm.rlz[i] * 0.6931471805599453f;
+}
+
 __device__ __forceinline__ void write_sentinel(const Params& p, int b) {
   const int k = p.k, tid = threadIdx.x;
   if (p.mode == MODE_SAMPLE) {
@@ -1416,6 +1468,7 @@ __device__ __forceinline__ void write_sentinel(const Params& p, int b) {
   if (tid <= k) {
     p.tokens[(size_t)b * (k + 1) + tid] = -1;
     p.logprobs[(size_t)b * (k + 1) + tid] = __builtin_nanf("");
+    if (p.raw_logprobs) p.raw_logprobs[(size_t)b * (k + 1) + tid] = __builtin_nanf("");
   }
   if (tid < k) p.alpha[(size_t)b * k + tid] = __builtin_nanf("");
   if (tid == 0) p.accept_len[b] = 0;
@@ -1447,6 +1500,9 @@ __device__ __forceinline__ void k5_finalize(const Params& p, K5Smem& sm, int b, 
       const int t = tid < n ? sm.tok[tid] : (tid == n ? y : -1);
       p.tokens[(size_t)b * (k + 1) + tid] = t;
       p.logprobs[(size_t)b * (k + 1) + tid] = 0.0f;
+      if (p.raw_logprobs)  // the committed token of row n is its argmax, whose logit is the row max
+        p.raw_logprobs[(size_t)b * (k + 1) + tid] =
+            tid < n ? raw_lp(sm, tid, sm.gath[tid]) : (tid == n ? raw_lp(sm, n, sm.m[n]) : 0.0f);
     }
     if (tid == 0) p.accept_len[b] = n + 1;
     return;
@@ -1502,14 +1558,16 @@ __device__ __forceinline__ void k5_finalize(const Params& p, K5Smem& sm, int b, 
   }
   if (tid <= k) {
     int t = -1;
-    float lp = 0.0f;
+    float lp = 0.0f, rlp = 0.0f;
     if (tid <= n) {
       t = tid < n ? sm.tok[tid] : y;
       const float l = tid < n ? sm.gath[tid] : yv;
       lp = (l - sm.m[tid]) / q.T - logf(sm.Z[tid]);
+      rlp = raw_lp(sm, tid, l);
     }
     p.tokens[(size_t)b * (k + 1) + tid] = t;
     p.logprobs[(size_t)b * (k + 1) + tid] = lp;
+    if (p.raw_logprobs) p.raw_logprobs[(size_t)b * (k + 1) + tid] = rlp;
   }
   if (tid == 0) p.accept_len[b] = n + 1;
 }
@@ -1789,14 +1847,16 @@ __device__ __forceinline__ void k5_sparse(const Params& p, K5Smem& sm, int b, in
   }
   if (tid <= k) {
     int t = -1;
-    float lp = 0.0f;
+    float lp = 0.0f, rlp = 0.0f;
     if (tid <= n) {
       t = tid < n ? sm.tok[tid] : y;
       const float l = tid < n ? sm.gath[tid] : bval;
       lp = (l - sm.m[tid]) / q.T - logf(sm.Z[tid]);
+      rlp = raw_lp(sm, tid, l);
     }
     p.tokens[(size_t)b * (k + 1) + tid] = t;
     p.logprobs[(size_t)b * (k + 1) + tid] = lp;
+    if (p.raw_logprobs) p.raw_logprobs[(size_t)b * (k + 1) + tid] = rlp;
   }
   if (tid == 0) p.accept_len[b] = n + 1;
 }
@@ -1828,6 +1888,7 @@ __device__ __forceinline__ void k5_item(const Params& p, K5Smem& sm, int item, i
     sm.fthr[tid] = ri->fthr;
     sm.state[tid] = ri->state;
     sm.gath[tid] = ri->gath;
+    if (p.raw_logprobs) sm.rlz[tid] = ri->rlz;
   }
   if (tid < k) {
     sm.tok[tid] = p.draft_tokens[(size_t)b * k + tid];
@@ -1921,7 +1982,7 @@ __device__ __forceinline__ void k5_item(const Params& p, K5Smem& sm, int item, i
   SV_TRACE5_AT(p, item, 7);
 }
 
-template <class E, int VPT>
+template <class E, int VPT, bool RAW>
 __global__ __launch_bounds__(NT) void k5_verify(Params p) {
   __shared__ K5Smem sm;
   int b, s;
@@ -1929,6 +1990,7 @@ __global__ __launch_bounds__(NT) void k5_verify(Params p) {
   // all of them and a run of expensive rows does not pile onto one XCD
   b = blockIdx.x / p.S5;
   s = blockIdx.x - b * p.S5;
+  if constexpr (!RAW) p.raw_logprobs = nullptr;  // every raw-output branch folds away
   k5_item<E, VPT>(p, sm, blockIdx.x, b, s);
 }
 
@@ -2008,10 +2070,16 @@ static void enqueue(const Params& p, int cus, hipStream_t st) {
   static_assert(WTOP / 2 == NT && NBC == NT, "K1 assumes one histogram word pair per thread");
   (void)cus;
   prof_mark(0, st);
-  hipLaunchKernelGGL((k1_stats<E, VPT1>), dim3((unsigned)(p.R * p.S1)), dim3(NT), 0, st, p);
+  if (p.raw_logprobs)
+    hipLaunchKernelGGL((k1_stats<E, VPT1, true>), dim3((unsigned)(p.R * p.S1)), dim3(NT), 0, st, p);
+  else
+    hipLaunchKernelGGL((k1_stats<E, VPT1, false>), dim3((unsigned)(p.R * p.S1)), dim3(NT), 0, st, p);
   prof_mark(1, st);
   prof_mark(2, st);
-  hipLaunchKernelGGL((k5_verify<E, VPT5>), dim3((unsigned)(p.B * p.S5)), dim3(NT), 0, st, p);
+  if (p.raw_logprobs)
+    hipLaunchKernelGGL((k5_verify<E, VPT5, true>), dim3((unsigned)(p.B * p.S5)), dim3(NT), 0, st, p);
+  else
+    hipLaunchKernelGGL((k5_verify<E, VPT5, false>), dim3((unsigned)(p.B * p.S5)), dim3(NT), 0, st, p);
   prof_mark(3, st);
 }
 
@@ -2067,11 +2135,11 @@ extern "C" const char* spec_verify_status_string(spec_status_t status) {
   return "unknown status";
 }
 
-extern "C" spec_status_t spec_verify(const void* target_logits, const void* draft_logits, spec_dtype_t dtype,
-                                     const int32_t* draft_tokens, const float* temperature, const int32_t* top_k,
-                                     const float* top_p, int32_t B, int32_t k, int32_t V, uint64_t seed,
-                                     uint64_t offset, int32_t* tokens, int32_t* accept_len, float* logprobs,
-                                     float* alpha, void* workspace, size_t workspace_bytes, void* stream) {
+static spec_status_t verify_impl(const void* target_logits, const void* draft_logits, spec_dtype_t dtype,
+                                 const int32_t* draft_tokens, const float* temperature, const int32_t* top_k,
+                                 const float* top_p, int32_t B, int32_t k, int32_t V, uint64_t seed, uint64_t offset,
+                                 int32_t* tokens, int32_t* accept_len, float* logprobs, float* raw_logprobs,
+                                 float* alpha, void* workspace, size_t workspace_bytes, void* stream) {
   Geo g;
   if (k < 1 || !make_geo(B, k, V, dtype, g)) return SPEC_ERR_INVALID_ARGUMENT;
   if (offset >= (1ull << 32)) return SPEC_ERR_INVALID_ARGUMENT;
@@ -2097,8 +2165,29 @@ extern "C" spec_status_t spec_verify(const void* target_logits, const void* draf
   p.tokens = tokens;
   p.accept_len = accept_len;
   p.logprobs = logprobs;
+  p.raw_logprobs = raw_logprobs;
   p.alpha = alpha;
   return launch(p, g, dtype, workspace, workspace_bytes, stream);
+}
+
+extern "C" spec_status_t spec_verify(const void* target_logits, const void* draft_logits, spec_dtype_t dtype,
+                                     const int32_t* draft_tokens, const float* temperature, const int32_t* top_k,
+                                     const float* top_p, int32_t B, int32_t k, int32_t V, uint64_t seed,
+                                     uint64_t offset, int32_t* tokens, int32_t* accept_len, float* logprobs,
+                                     float* alpha, void* workspace, size_t workspace_bytes, void* stream) {
+  return verify_impl(target_logits, draft_logits, dtype, draft_tokens, temperature, top_k, top_p, B, k, V, seed,
+                     offset, tokens, accept_len, logprobs, nullptr, alpha, workspace, workspace_bytes, stream);
+}
+
+extern "C" spec_status_t spec_verify_raw(const void* target_logits, const void* draft_logits, spec_dtype_t dtype,
+                                         const int32_t* draft_tokens, const float* temperature, const int32_t* top_k,
+                                         const float* top_p, int32_t B, int32_t k, int32_t V, uint64_t seed,
+                                         uint64_t offset, int32_t* tokens, int32_t* accept_len, float* logprobs,
+                                         float* raw_logprobs, float* alpha, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  if (!raw_logprobs) return SPEC_ERR_INVALID_ARGUMENT;
+  return verify_impl(target_logits, draft_logits, dtype, draft_tokens, temperature, top_k, top_p, B, k, V, seed,
+                     offset, tokens, accept_len, logprobs, raw_logprobs, alpha, workspace, workspace_bytes, stream);
 }
 
 extern "C" size_t spec_sample_workspace_size(int32_t R, int32_t V, spec_dtype_t dtype) {

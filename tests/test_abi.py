@@ -73,3 +73,12 @@ def test_invalid_scalars_rejected_before_launch(L):
     # misaligned logits
     st = L.spec_verify(ctypes.c_void_p(18), P, 0, P, P, P, P, 2, 2, 1024, 0, 0, P, P, P, P, P, 1 << 30, None)
     assert st == 1
+
+
+def test_raw_variant_rejects_missing_output(L):
+    # spec_verify_raw needs its extra output; size checks match spec_verify's, all before any device call
+    P = ctypes.c_void_p(16)
+    st = L.spec_verify_raw(P, P, 0, P, P, P, P, 2, 2, 1024, 0, 0, P, P, P, None, P, P, 1 << 30, None)
+    assert st == 1
+    st = L.spec_verify_raw(P, P, 0, P, P, P, P, 0, 2, 1024, 0, 0, P, P, P, P, P, P, 1 << 30, None)
+    assert st == 1

@@ -259,3 +259,42 @@ def test_plain_sampler_parity(o, case):
     np.testing.assert_array_equal(tok[strict], want[strict])
     np.testing.assert_allclose(lp[strict], want_lp[strict], atol=parity.LOGPROB_TOL, rtol=0)
     assert np.all((tok >= 0) & (tok < V))
+
+
+RAW_CASES = [
+    ("mixed_full", 64, 2, 157184, "bf16", dict(boost=8.0, mixed_params=True)),
+    ("greedy_ties", 24, 2, 40000, "bf16", dict(temperature=0.0, tie_fraction=0.2)),
+    ("f32_trunc", 8, 3, 12000, "f32", dict(temperature=0.7, top_k=30, top_p=0.9)),
+    ("k1_T2_topp", 16, 1, 32768, "bf16", dict(temperature=2.0, top_p=0.8)),
+]
+
+
+@pytest.mark.parametrize("case", RAW_CASES, ids=[c[0] for c in RAW_CASES])
+def test_raw_logprobs(o, case):
+    """spec_verify_raw: every output of spec_verify unchanged (bit-exact), plus ln softmax of the
+    unprocessed target logits at each committed token, checked against the oracle evaluated at the GPU's
+    own tokens (so margin rows are covered too); NaN in sentinel rows, 0 after the committed slots."""
+    import torch
+    import rejection_sampling_verify_16_amd as sv
+    name, B, k, V, dtype, kw = case
+    w = W.make(B, k, V, dtype=dtype, seed=5000 + B + V, name=name, **kw)
+    drafts = w.draft_tokens(parity.oracle_sampler(o))
+    dev = parity.device_inputs(w, drafts)
+    plain = parity.run_gpu(dev, 11, 2)
+    res = sv.spec_verify(dev["target"], dev["draft"], dev["drafts"], dev["T"], dev["K"], dev["P"], seed=11,
+                         offset=2, raw=True)
+    torch.cuda.synchronize()
+    res = {key: v.cpu().numpy() for key, v in res.items()}
+    for key in plain:
+        np.testing.assert_array_equal(res[key], plain[key], err_msg=f"{name}: {key} changed")
+    ref = o.raw_logprobs(w.target, res["tokens"], res["accept_len"])
+    sent = res["accept_len"] == 0
+    assert np.all(np.isnan(res["raw_logprobs"][sent]))
+    slot = np.arange(k + 1)[None, :] < res["accept_len"][:, None]
+    got = res["raw_logprobs"].astype(np.float64)
+    assert np.all(got[~sent][~slot[~sent]] == 0.0)
+    sel = slot & ~sent[:, None]
+    err = np.abs(got[sel] - ref[sel])
+    print(f"[raw] {name}: slots={int(sel.sum())} max err {err.max():.3g}", flush=True)
+    assert np.all(np.isfinite(got[sel]))
+    assert err.max() <= parity.LOGPROB_TOL
