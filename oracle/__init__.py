@@ -105,6 +105,8 @@ class Oracle:
         L.oracle_sample.restype = ctypes.c_int
         L.oracle_raw_logprobs.argtypes = [_P, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _I32]
         L.oracle_raw_logprobs.restype = ctypes.c_int
+        L.oracle_commit.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, ctypes.c_int64]
+        L.oracle_commit.restype = ctypes.c_int
 
     # -- random streams ---------------------------------------------------------------
     def philox(self, ctr, key) -> np.ndarray:
@@ -190,6 +192,34 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_raw_logprobs rejected its arguments")
         return out
+
+    # -- commit step ----------------------------------------------------------------------
+    def commit(self, tensors, state_slot, accept_len, seq_len=None):
+        """Commit step over a list of (verify_state, state_cache) numpy pairs, each
+        verify_state [L, B, k+1, ...] and state_cache [L, num_slots, ...] of one dtype:
+        state_cache[l, state_slot[b]] = verify_state[l, b, accept_len[b] - 1] for rows with
+        1 <= accept_len <= k+1 and a slot in range, every layer and every pair.  seq_len (int32 [B],
+        may be None) gains accept_len[b] on those rows, once.  The caches and seq_len are updated in
+        place; returns status int32 [B] (0 committed, 1 bad accept_len, 2 bad slot)."""
+        assert len(tensors) >= 1
+        B = int(np.asarray(state_slot).shape[0])
+        slot = np.ascontiguousarray(np.asarray(state_slot, dtype=np.int32).reshape(B))
+        acc = np.ascontiguousarray(np.asarray(accept_len, dtype=np.int32).reshape(B))
+        if seq_len is not None:
+            assert seq_len.dtype == np.int32 and seq_len.flags.c_contiguous and seq_len.shape == (B,)
+        status = np.zeros(B, dtype=np.int32)
+        for idx, (vs, cache) in enumerate(tensors):
+            vs = np.ascontiguousarray(vs)
+            L, B2, k1 = vs.shape[:3]
+            assert B2 == B and cache.flags.c_contiguous and cache.dtype == vs.dtype
+            assert cache.shape[0] == L and cache.shape[2:] == vs.shape[3:]
+            row_bytes = vs[0, 0, 0].nbytes
+            rc = self.lib.oracle_commit(_ptr(vs), _ptr(cache), _ptr(slot), _ptr(acc),
+                                        _ptr(seq_len if idx == 0 else None), _ptr(status), L, B, k1 - 1,
+                                        int(cache.shape[1]), int(row_bytes))
+            if rc != 0:
+                raise ValueError("oracle_commit rejected its arguments")
+        return status
 
     # -- plain sampler ---------------------------------------------------------------------
     def sample(self, logits, temperature, top_k, top_p, row_b, row_pos, seed: int = 0, offset: int = 0,

@@ -552,6 +552,61 @@ int oracle_raw_logprobs(const void* target_logits, int32_t dtype, const int32_t*
   return 0;
 }
 
+// The commit step after verify (AReno pull request above, section "What does this PR do?": the Phase-2
+// paragraph's recurrent and conv caches stacked across layers with one shared verify-state buffer, and
+// the per-step table's commit row; InfiniLM pull request "add mtp draft models for speculative
+// decoding", the state-consistency row of its mechanism table).  The verify forward is fed k+1 tokens
+// per row (the last committed token, then the k drafts) and leaves, for every layer l, row b and fed
+// position j, the state after position j in verify_state[l][b][j] (row_bytes bytes).  With n drafts
+// accepted, accept_len = n + 1 tokens were consumed (the last committed token and the n drafts; the
+// drawn token is fed at the next step), so the committed state is the one after position accept_len-1:
+//   state_cache[l][state_slot[b]] = verify_state[l][b][accept_len[b] - 1]   for every layer l,
+//   seq_len[b] += accept_len[b]  (keys and values of the rejected positions lie past the new length).
+// A row with accept_len outside 1..k+1 (0 marks a row whose inputs were unusable) or a slot outside
+// 0..num_slots-1 keeps its state and length; status[b] (may be NULL) is 0 for a committed row, 1 for
+// a bad accept_len, 2 for a bad slot.  seq_len may be NULL.  Plain byte copies, row by row.
+int oracle_commit(const void* verify_state, void* state_cache, const int32_t* state_slot,
+                  const int32_t* accept_len, int32_t* seq_len, int32_t* status, int32_t L, int32_t B, int32_t k,
+                  int32_t num_slots, int64_t row_bytes) {
+  if (L < 1 || B < 1 || k < 0 || num_slots < 1 || row_bytes < 1) return 1;
+  const uint8_t* src = (const uint8_t*)verify_state;
+  uint8_t* dst = (uint8_t*)state_cache;
+  const size_t rb = (size_t)row_bytes;
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t a = accept_len[b];
+    const int32_t slot = state_slot[b];
+    int32_t st = 0;
+    if (a < 1 || a > k + 1) st = 1;
+    else if (slot < 0 || slot >= num_slots) st = 2;
+    if (status) status[b] = st;
+    if (st != 0) continue;
+#if ORACLE_MUTANT == 16
+    const int32_t j = a < k + 1 ? a : k;  // MUTANT 16: the state after the drawn token's position
+#else
+    const int32_t j = a - 1;
+#endif
+    for (int32_t l = 0; l < L; ++l) {
+#if ORACLE_MUTANT == 17
+      const size_t from = (((size_t)b * L + l) * (size_t)(k + 1) + (size_t)j) * rb;  // MUTANT 17: [B][L] order
+#else
+      const size_t from = (((size_t)l * B + b) * (size_t)(k + 1) + (size_t)j) * rb;
+#endif
+#if ORACLE_MUTANT == 19
+      const size_t to = ((size_t)l * (size_t)num_slots + (size_t)b) * rb;  // MUTANT 19: slot map ignored
+#else
+      const size_t to = ((size_t)l * (size_t)num_slots + (size_t)slot) * rb;
+#endif
+      std::memcpy(dst + to, src + from, rb);
+    }
+#if ORACLE_MUTANT == 18
+    if (seq_len) seq_len[b] += a - 1;  // MUTANT 18: length grows by the accepted drafts only
+#else
+    if (seq_len) seq_len[b] += a;
+#endif
+  }
+  return 0;
+}
+
 int oracle_sample(const void* logits, int32_t dtype, const float* temperature, const int32_t* top_k,
                   const float* top_p, const int32_t* row_b, const int32_t* row_pos, int32_t R, int32_t V,
                   uint64_t seed, uint64_t offset, int32_t* tokens, double* logprobs, double* gap,

@@ -101,6 +101,18 @@ int oracle_sample(const void* logits, int32_t dtype, const float* temperature, c
                   uint64_t seed, uint64_t offset, int32_t* tokens, double* logprobs, double* gap,
                   int32_t num_threads);
 
+/*
+ * Commit step: for every row b with 1 <= accept_len[b] <= k+1 and 0 <= state_slot[b] < num_slots,
+ *   state_cache[l][state_slot[b]][:] = verify_state[l][b][accept_len[b]-1][:]  (all L layers)
+ *   seq_len[b] += accept_len[b]                                                  (seq_len may be NULL)
+ *   verify_state [L, B, k+1, row_bytes], state_cache [L, num_slots, row_bytes] (raw bytes)
+ *   status [B] out (may be NULL): 0 committed, 1 accept_len out of range, 2 slot out of range
+ * Other rows are left as they are.  Returns 0, or 1 for bad scalar arguments (nothing written).
+ */
+int oracle_commit(const void* verify_state, void* state_cache, const int32_t* state_slot,
+                  const int32_t* accept_len, int32_t* seq_len, int32_t* status, int32_t L, int32_t B, int32_t k,
+                  int32_t num_slots, int64_t row_bytes);
+
 #ifdef __cplusplus
 }
 #endif

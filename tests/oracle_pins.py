@@ -493,4 +493,103 @@ def pin_plain_sampler_marginal(o):
     np.testing.assert_allclose(lp, np.log(p[tok]), atol=1e-12)
 
 
+# ---------------------------------------------------------------------------------------
+# commit step
+# ---------------------------------------------------------------------------------------
+
+class _ToyHybrid:
+    """A toy hybrid model in exact integer arithmetic, L layers deep.  Each layer keeps a recurrent
+    state (a wrapping multiply-add of the fed token's embedding, so it depends on the order of every
+    token fed so far), a conv window holding the last W-1 fed embeddings, and a key/value list with one
+    entry per fed token.  ``step`` feeds one token, as plain decode does; ``verify`` feeds k+1 tokens from a
+    committed state and keeps the state after every position, as a verify forward does."""
+
+    def __init__(self, rng, L, D, rdtype, W, C, vocab=1000):
+        self.L, self.D, self.W, self.C = L, D, W, C
+        self.rdtype = rdtype
+        self.mult = (rng.integers(0, 1 << 15, size=L) * 2 + 1).astype(rdtype)
+        self.emb = rng.integers(0, 1 << 16, size=(vocab, max(D, C)), dtype=np.int64)
+
+    def e(self, x, l, n, dtype):
+        return ((self.emb[x, :n] + 977 * l) % (1 << 16)).astype(dtype)
+
+    def step(self, rec, conv, kv, x):
+        """rec [L, D], conv [L, W-1, C], kv list; returns the state after feeding token x."""
+        rec = rec.copy()
+        conv = conv.copy()
+        for l in range(self.L):
+            rec[l] = rec[l] * self.mult[l] + self.e(x, l, self.D, self.rdtype)
+            conv[l] = np.concatenate([conv[l, 1:], self.e(x, l, self.C, np.uint16)[None, :]], axis=0)
+        return rec, conv, kv + [x]
+
+    def verify(self, rec, conv, fed):
+        recs, convs = [], []
+        for x in fed:
+            rec, conv, _ = self.step(rec, conv, [], x)
+            recs.append(rec)
+            convs.append(conv)
+        return np.stack(recs, axis=1), np.stack(convs, axis=1)   # [L, k+1, ...]
+
+
+def _commit_rounds(o, L, D, rdtype, W, C, B, k, rounds, seed):
+    rng = np.random.default_rng(seed)
+    toy = _ToyHybrid(rng, L, D, rdtype, W, C)
+    num_slots = B + 3
+    slot = rng.permutation(num_slots)[:B].astype(np.int32)
+    rec_cache = rng.integers(0, 250, size=(L, num_slots, D)).astype(rdtype)
+    conv_cache = rng.integers(0, 60000, size=(L, num_slots, W - 1, C)).astype(np.uint16)
+    free = np.setdiff1d(np.arange(num_slots), slot)
+    free_rec, free_conv = rec_cache[:, free].copy(), conv_cache[:, free].copy()
+    # sequential-decode reference per row
+    seq = [(rec_cache[:, slot[b]].copy(), conv_cache[:, slot[b]].copy(), []) for b in range(B)]
+    kv = np.full((B, 4 * rounds * (k + 1)), -1, np.int64)   # verify writes every fed position
+    seq_len = np.zeros(B, np.int32)
+    last = rng.integers(0, 1000, size=B)
+    for r in range(rounds):
+        fed = np.concatenate([last[:, None], rng.integers(0, 1000, size=(B, k))], axis=1)
+        vrec = np.empty((L, B, k + 1, D), rdtype)
+        vconv = np.empty((L, B, k + 1, W - 1, C), np.uint16)
+        for b in range(B):
+            vrec[:, b], vconv[:, b] = toy.verify(rec_cache[:, slot[b]], conv_cache[:, slot[b]], fed[b])
+            kv[b, seq_len[b]:seq_len[b] + k + 1] = fed[b]
+        acc = rng.integers(1, k + 2, size=B).astype(np.int32)
+        acc[0] = k + 1                            # a full accept and a minimal one every round
+        acc[1 % B] = 1
+        bad_slot = np.zeros(B, bool)
+        if r == 1:
+            acc[2 % B] = 0                        # sentinel row: the step is discarded
+            acc[3 % B] = k + 2
+        if r == 2:
+            bad_slot[4 % B] = True
+        slot_arg = np.where(bad_slot, num_slots, slot).astype(np.int32)
+        status = o.commit([(vrec, rec_cache), (vconv, conv_cache)], slot_arg, acc, seq_len)
+        for b in range(B):
+            ok = 1 <= acc[b] <= k + 1 and not bad_slot[b]
+            assert status[b] == (0 if ok else (1 if not 1 <= acc[b] <= k + 1 else 2))
+            if ok:
+                st = seq[b]
+                for x in fed[b, :acc[b]]:
+                    st = toy.step(*st, x)
+                seq[b] = st
+                last[b] = rng.integers(0, 1000)    # the token drawn at this step, fed next time
+            rec_b, conv_b, kv_b = seq[b]
+            np.testing.assert_array_equal(rec_cache[:, slot[b]], rec_b)
+            np.testing.assert_array_equal(conv_cache[:, slot[b]], conv_b)
+            assert seq_len[b] == len(kv_b)
+            np.testing.assert_array_equal(kv[b, :seq_len[b]], kv_b)
+        np.testing.assert_array_equal(rec_cache[:, free], free_rec)
+        np.testing.assert_array_equal(conv_cache[:, free], free_conv)
+
+
+def pin_commit_matches_sequential_decode(o):
+    """After full and partial commits the recurrent state, the conv window and the key/value prefix of
+    every row equal those of decoding the committed tokens one at a time (the pages check exactly this on
+    their model).  Four rounds per case on a toy integer model with several layers, slots permuted in a
+    larger pool, rows that must be left alone (accept length 0 or k+2, slot out of range), and state rows
+    of 1, 3 and 68 bytes.  Slots no row maps to keep their bytes."""
+    _commit_rounds(o, L=3, D=1, rdtype=np.uint8, W=4, C=1, B=6, k=2, rounds=4, seed=70)
+    _commit_rounds(o, L=2, D=3, rdtype=np.uint8, W=2, C=3, B=5, k=1, rounds=4, seed=71)
+    _commit_rounds(o, L=4, D=17, rdtype=np.uint32, W=4, C=5, B=7, k=4, rounds=4, seed=72)
+
+
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_") and callable(v)]

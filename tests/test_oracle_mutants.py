@@ -5,14 +5,16 @@ Each mutant is the oracle built with -DORACLE_MUTANT=<n>, which changes one step
 inequality, highest-index ties, no renormalisation after top-k, accept length without
 the extra token, wrong alpha, wrong Gumbel sign, temperature multiplying, top-k off by
 one, Philox one round short, bonus at the wrong position, residual without the clamp, raw logprobs
-in base 2, raw logprobs with the temperature applied).
+in base 2, raw logprobs with the temperature applied, commit of the state after the drawn token's
+position, commit with layers and rows swapped, sequence length grown by the accepted drafts only,
+commit ignoring the slot map).
 """
 import pytest
 
 import oracle
 import oracle_pins
 
-MUTANTS = list(range(1, 16))
+MUTANTS = list(range(1, 20))
 
 
 @pytest.mark.parametrize("mutant", MUTANTS)
