@@ -8,7 +8,9 @@ Prints one JSON line.  Besides the throughput it reports
   roofline:     the statistics kernel (it streams every logit once): algorithmic logit bytes per
                 launch / its average duration (HIP events the library records around each of its
                 kernels, over a second pass of the same calls), against the 8 TB/s HBM peak;
-  cpu_baseline: the CPU oracle timed on this host on a bounded sample of the same workload.
+  cpu_baseline: the CPU oracle timed on this host on a bounded sample of the same workload;
+  commit:       the commit step after verify (spec_commit) on a hybrid-model state workload, with its own
+                throughput, roofline and CPU baseline (skip with --no-commit, alone with --commit-only).
 """
 from __future__ import annotations
 
@@ -62,6 +64,9 @@ def main():
     ap.add_argument("--raw-logprobs", action="store_true",
                     help="time spec_verify_raw (also the raw logprobs of the committed tokens)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-commit", action="store_true", help="skip the commit-step measurement")
+    ap.add_argument("--commit-only", action="store_true", help="only the commit-step measurement")
+    ap.add_argument("--commit-steps", type=int, default=100)
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, 5 times (PMC calibration)")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
@@ -90,6 +95,9 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "copies": 5}), flush=True)
+        return
+    if args.commit_only:
+        print(json.dumps({"commit": bench_commit(args, dev)}), flush=True)
         return
     w = W.CONFIGS[args.config]()
     B, k, V = w.B, w.k, w.V
@@ -191,7 +199,85 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, drafts.cpu().numpy(), args.cpu_seconds)
+    if not args.no_commit:
+        del sets, out, ws
+        torch.cuda.empty_cache()
+        result["commit"] = bench_commit(args, dev)
     print(json.dumps(result), flush=True)
+
+
+def bench_commit(args, dev):
+    """The commit step after verify on its own workload: one spec_commit call per step, inputs resident in
+    HBM; per-launch duration from HIP events around each call on the stream it runs on (one kernel per
+    call), against the HBM roofline with the bytes the committed rows move (read + write)."""
+    import torch
+    import rejection_sampling_verify_16_amd as sv
+    from rejection_sampling_verify_16_amd import workloads as W
+    w = W.commit_hybrid()
+    stream = torch.cuda.current_stream(dev)
+
+    def dev_bytes(a, lead):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.uint8).reshape(*a.shape[:lead], -1)).to(dev)
+
+    tensors = [(dev_bytes(t.verify_state, 3), dev_bytes(t.state_cache, 2)) for t in w.tensors]
+    slot = torch.from_numpy(w.state_slot).to(dev)
+    acc = torch.from_numpy(w.accept_len).to(dev)
+    seq = torch.from_numpy(w.seq_len.copy()).to(dev)
+    status = torch.empty(w.B, dtype=torch.int32, device=dev)
+
+    def step():
+        sv.spec_commit(tensors, slot, acc, seq_len=seq, status=status, stream=stream)
+
+    for _ in range(5):
+        step()
+    torch.cuda.synchronize()
+    n = args.commit_steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in evs]
+    ms_kernel = float(np.mean(per))
+    ms_step = e0.elapsed_time(e1) / n
+    moved = w.moved_bytes
+    gbps = moved / (ms_kernel * 1e-3) / 1e9
+    res = {
+        "metric": "committed rows/s + state HBM GB/s (% peak)",
+        "value": w.B / (ms_step * 1e-3),
+        "unit": "committed rows/s",
+        "steps": n,
+        "ms_per_step": ms_step,
+        "config": {"workload": w.name, "B": w.B, "k": w.k, "num_slots": w.num_slots,
+                   "tensors": {t.name: {"layers": int(t.verify_state.shape[0]),
+                                        "row_bytes": int(t.verify_state[0, 0, 0].nbytes)} for t in w.tensors},
+                   "committed_rows": int(((w.accept_len >= 1) & (w.accept_len <= w.k + 1)).sum())},
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None, "kernel": "k_commit",
+                     "kernel_ms_mean": ms_kernel, "algorithmic_bytes": moved},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        o = oracle.get()
+        host = [(np.ascontiguousarray(t.verify_state).view(np.uint8).reshape(*t.verify_state.shape[:3], -1),
+                 np.ascontiguousarray(t.state_cache).view(np.uint8).reshape(*t.state_cache.shape[:2], -1).copy())
+                for t in w.tensors]
+        seq_h = w.seq_len.copy()
+        calls, t0 = 0, time.perf_counter()
+        while True:
+            o.commit(host, w.state_slot, w.accept_len, seq_h)
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= min(args.cpu_seconds, 5.0) or calls >= 200:
+                break
+        res["cpu_baseline"] = {"value": w.B * calls / el, "unit": "committed rows/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{calls} full commits of the benchmark workload ({w.B} rows each), {el:.1f} s"}
+    return res
 
 
 def _pmc_per_kernel(run_dir, counter):

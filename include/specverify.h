@@ -128,6 +128,58 @@ spec_status_t spec_sample(const void* logits, spec_dtype_t dtype, const float* t
                           uint64_t seed, uint64_t offset, int32_t* tokens, float* logprobs, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/*
+ * Commit step: after verify, make each batch row's cached model state the state after its last consumed
+ * token (AReno pull request above, section "What does this PR do?": the Phase-2 paragraph keeps the
+ * recurrent and conv caches stacked across layers with one verify-state buffer, and its per-step table
+ * commits them in a few kernels; InfiniLM pull request "add mtp draft models for speculative decoding",
+ * the state-consistency row of its mechanism table: verify reads the committed state and writes elsewhere,
+ * and only (k, accepted count) decide what becomes committed).
+ *
+ * The verify forward is fed k+1 tokens per row (the last committed token, then the k drafts) and writes,
+ * for every layer l, row b and fed position j, the state after position j into verify_state[l][b][j].
+ * With accept_len = n + 1 (n drafts accepted), the last committed token and the n drafts were consumed
+ * and the drawn token will be fed at the next step, so the state after position accept_len - 1 is the
+ * one to keep.  For every row b with 1 <= accept_len[b] <= k+1 and 0 <= state_slot[b] < num_slots:
+ *
+ *   state_cache[l][state_slot[b]][:] = verify_state[l][b][accept_len[b] - 1][:]  for every tensor, layer
+ *   seq_len[b] += accept_len[b]
+ *
+ * Keys and values of full-attention layers need no copy: verify wrote all k+1 positions in place, and
+ * the ones past the new seq_len are overwritten by the next step, so seq_len is their whole commit.
+ * Other rows (accept_len 0 marks a sentinel row of spec_verify) keep their state and length.
+ *
+ *   tensors     HOST array of n_tensors descriptors (read during the call only); each names one stateful
+ *               tensor stacked across its layers:
+ *                 verify_state  device [layers, B, k+1, row_bytes] bytes (any dtype; copied bit for bit)
+ *                 state_cache   device [layers, num_slots, row_bytes] bytes
+ *                 row_bytes     one layer's state of one row, >= 1; layers >= 1; layers * B < 2^31
+ *               n_tensors 0 .. SPEC_COMMIT_MAX_TENSORS (0: only seq_len / status, e.g. a model whose
+ *               layers all keep keys and values)
+ *   state_slot  device int32 [B]   cache slot of each row (rows committed in one call need distinct slots)
+ *   accept_len  device int32 [B]   spec_verify's accept_len
+ *   seq_len     device int32 [B] in/out, may be NULL
+ *   status      device int32 [B] out, may be NULL: 0 committed, 1 accept_len outside 1..k+1,
+ *               2 slot outside 0..num_slots-1 (checked in that order)
+ *   B           1 .. 2^20;  k  0 .. 255;  num_slots >= 1
+ * No verify_state range may overlap any state_cache range, and state_cache ranges must not overlap
+ * each other (SPEC_ERR_INVALID_ARGUMENT).  Copies are fastest with row_bytes a multiple of 16 and
+ * 16-byte aligned tensors; any size and alignment is accepted.  Enqueues one kernel on `stream` and
+ * returns without synchronising; needs no workspace.
+ */
+#define SPEC_COMMIT_MAX_TENSORS 8
+
+typedef struct {
+  const void* verify_state;
+  void* state_cache;
+  int64_t row_bytes;
+  int32_t layers;
+} spec_state_tensor_t;
+
+spec_status_t spec_commit(const spec_state_tensor_t* tensors, int32_t n_tensors, const int32_t* state_slot,
+                          const int32_t* accept_len, int32_t* seq_len, int32_t* status, int32_t B, int32_t k,
+                          int32_t num_slots, void* stream);
+
 /* A static, human-readable name of a status code. */
 const char* spec_verify_status_string(spec_status_t status);
 

@@ -19,7 +19,15 @@ SPEC_NUM_KERNELS = 2  # kernels per call: 0 = row statistics / thresholds, 1 = a
 STATUS = {0: "SPEC_OK", 1: "SPEC_ERR_INVALID_ARGUMENT", 2: "SPEC_ERR_WORKSPACE",
           3: "SPEC_ERR_UNSUPPORTED_DEVICE", 4: "SPEC_ERR_LAUNCH"}
 
+SPEC_COMMIT_MAX_TENSORS = 8
+
 _lib = None
+
+
+class StateTensor(ctypes.Structure):
+    """spec_state_tensor_t: one stateful tensor of the commit step, stacked across layers."""
+    _fields_ = [("verify_state", ctypes.c_void_p), ("state_cache", ctypes.c_void_p),
+                ("row_bytes", ctypes.c_int64), ("layers", ctypes.c_int32)]
 
 
 class SpecVerifyError(RuntimeError):
@@ -49,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.spec_sample.restype = ctypes.c_int
         L.spec_verify_status_string.argtypes = [ctypes.c_int]
         L.spec_verify_status_string.restype = ctypes.c_char_p
+        L.spec_commit.argtypes = [ctypes.POINTER(StateTensor), I32, P, P, P, P, I32, I32, I32, P]
+        L.spec_commit.restype = ctypes.c_int
         L.spec_set_kernel_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), I32]
         L.spec_set_kernel_events.restype = ctypes.c_int
         _lib = L
@@ -154,6 +164,48 @@ def spec_sample(logits, temperature, top_k, top_p, row_b=None, row_pos=None, see
     if st != 0:
         raise SpecVerifyError(st, "spec_sample")
     return out
+
+
+def spec_commit(tensors, state_slot, accept_len, seq_len=None, status=None, stream=None, k=None):
+    """Commit step on device tensors.
+
+    ``tensors``: list of (verify_state, state_cache) pairs, verify_state [L, B, k+1, ...] and state_cache
+    [L, num_slots, ...] (contiguous, one dtype per pair; copied bit for bit).  state_slot and accept_len
+    are int32 [B]; seq_len (int32 [B], updated in place) and status (int32 [B] out) may be None.  For a
+    call without tensors, pass ``k``.  The caches of committed rows are updated in place; returns status."""
+    import torch
+    B = state_slot.shape[0]
+    descs = (StateTensor * max(1, len(tensors)))()
+    num_slots = None
+    for i, (vs, cache) in enumerate(tensors):
+        if not (vs.is_contiguous() and cache.is_contiguous()):
+            raise ValueError("state tensors must be contiguous")
+        if vs.dtype != cache.dtype or vs.shape[3:] != cache.shape[2:] or vs.shape[0] != cache.shape[0] \
+                or vs.shape[1] != B:
+            raise ValueError("verify_state [L, B, k+1, ...] and state_cache [L, num_slots, ...] do not match")
+        if k is None:
+            k = vs.shape[2] - 1
+        if vs.shape[2] != k + 1 or (num_slots is not None and cache.shape[1] != num_slots):
+            raise ValueError("all tensors must share k and num_slots")
+        num_slots = cache.shape[1]
+        descs[i] = StateTensor(vs.data_ptr(), cache.data_ptr(), vs[0, 0, 0].numel() * vs.element_size(), vs.shape[0])
+    if k is None:
+        raise ValueError("k is needed when no tensors are given")
+    if num_slots is None:
+        num_slots = 1 << 30
+    for t in (state_slot, accept_len, seq_len, status):
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous() or t.shape != (B,)):
+            raise ValueError("state_slot, accept_len, seq_len and status must be contiguous int32 [B]")
+    if status is None:
+        status = torch.empty(B, dtype=torch.int32, device=state_slot.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(state_slot.device)
+    st = lib().spec_commit(descs, len(tensors), state_slot.data_ptr(), accept_len.data_ptr(),
+                           seq_len.data_ptr() if seq_len is not None else None, status.data_ptr(), B, k,
+                           num_slots, ctypes.c_void_p(stream.cuda_stream))
+    if st != 0:
+        raise SpecVerifyError(st, "spec_commit")
+    return status
 
 
 def set_kernel_events(events):

@@ -6,7 +6,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "specverify.hip")
+SRCS = [os.path.join(HERE, "csrc", f) for f in ("specverify.hip", "commit.hip")]
 OUT = os.path.join(HERE, "libspecverify.so")
 
 HIPCC_FLAGS = [
@@ -18,7 +18,7 @@ HIPCC_FLAGS = [
 
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", OUT + ".tmp", SRC]
+    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", OUT + ".tmp", *SRCS]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stderr}")

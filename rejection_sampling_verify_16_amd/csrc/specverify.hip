@@ -2048,7 +2048,7 @@ static DevInfo g_dev[MAXDEV];
 static std::mutex g_mu;
 static hipEvent_t g_prof[2 * NKERN];  // benchmark hook: events around each kernel (all null: off)
 
-static bool device_ok(int dev, int& cus) {
+bool device_ok(int dev, int& cus) {
   if (dev < 0 || dev >= MAXDEV) return false;
   std::lock_guard<std::mutex> lk(g_mu);
   if (g_dev[dev].state == 0) {

@@ -6,6 +6,9 @@
 
 namespace sv {
 
+// Host: whether device `dev` is a gfx950 (cached per device); `cus` receives its compute-unit count.
+bool device_ok(int dev, int& cus);
+
 constexpr int NT = 256;          // threads per workgroup (4 wave64s)
 constexpr int NWAVE = NT / 64;
 constexpr int MAXK = 8;          // largest number of drafts per batch row

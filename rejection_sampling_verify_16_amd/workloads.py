@@ -205,3 +205,84 @@ def config5(n_calls: int = 100) -> Workload:
 
 CONFIGS = {"1": config1, "2": config2, "3": config3, "4a": lambda: config4(1), "4b": lambda: config4(2),
            "5": config5}
+
+
+# ---- commit step ------------------------------------------------------------------------------
+#
+# The pages give no state sizes, so these are stand-ins shaped like a hybrid linear-attention model's
+# stacked caches: per layer a recurrent state of H heads x d_k x d_v fp32 values and a conv window of
+# (W - 1) positions x C channels in bf16, one verify-state entry per fed position.  State bytes are
+# random (the copy is bit for bit, so their values do not matter); slots are a random injection of the
+# batch rows into a larger pool; accept lengths follow a steady per-draft acceptance rate.
+
+@dataclass
+class CommitTensor:
+    name: str
+    verify_state: np.ndarray   # [L, B, k+1, ...]
+    state_cache: np.ndarray    # [L, num_slots, ...] (the cache before the commit)
+
+
+@dataclass
+class CommitWorkload:
+    name: str
+    B: int
+    k: int
+    num_slots: int
+    tensors: list              # of CommitTensor
+    state_slot: np.ndarray     # int32 [B]
+    accept_len: np.ndarray     # int32 [B]
+    seq_len: np.ndarray        # int32 [B] (before the commit)
+
+    @property
+    def moved_bytes(self) -> int:
+        """Bytes read plus bytes written by a commit of the rows that are committed."""
+        ok = (self.accept_len >= 1) & (self.accept_len <= self.k + 1) & (self.state_slot >= 0) & \
+             (self.state_slot < self.num_slots)
+        per_row = sum(t.verify_state[:, 0, 0].nbytes for t in self.tensors)
+        return 2 * int(ok.sum()) * per_row
+
+
+def _random_bytes(rng: np.random.Generator, shape, dtype) -> np.ndarray:
+    """Pseudo-random contents (the bytes of uniform doubles; fast to draw at GB sizes)."""
+    n = int(np.prod(shape)) * np.dtype(dtype).itemsize
+    return rng.random((n + 7) // 8).view(np.uint8)[:n].view(dtype).reshape(shape)
+
+
+def accept_lengths(rng: np.random.Generator, B: int, k: int, rate: float) -> np.ndarray:
+    """accept_len = 1 + number of leading accepted drafts, each accepted with probability `rate`."""
+    acc = np.ones(B, dtype=np.int32)
+    alive = np.ones(B, dtype=bool)
+    for _ in range(k):
+        alive &= rng.random(B) < rate
+        acc += alive
+    return acc
+
+
+def make_commit(B: int, k: int, num_slots: int, shapes, *, seed: int, rate: float = 0.75, sentinels: int = 0,
+                bad_slots: int = 0, name: str = "commit") -> CommitWorkload:
+    """``shapes``: list of (name, layers, per-row state shape, numpy dtype)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    tensors = [CommitTensor(n, _random_bytes(rng, (L, B, k + 1) + tuple(s), dt),
+                            _random_bytes(rng, (L, num_slots) + tuple(s), dt)) for n, L, s, dt in shapes]
+    slot = rng.permutation(num_slots)[:B].astype(np.int32)
+    acc = accept_lengths(rng, B, k, rate)
+    if sentinels:
+        acc[rng.choice(B, size=sentinels, replace=False)] = 0
+    if bad_slots:
+        rows = rng.choice(B, size=bad_slots, replace=False)
+        slot[rows] = np.where(np.arange(bad_slots) % 2 == 0, num_slots + rows, -1 - rows).astype(np.int32)
+    seq = rng.integers(1, 4096, size=B).astype(np.int32)
+    return CommitWorkload(name, B, k, num_slots, tensors, slot, acc, seq)
+
+
+def commit_hybrid(B: int = 64, k: int = 2, layers: int = 12, heads: int = 16, dk: int = 128, dv: int = 128,
+                  conv_w: int = 4, conv_c: int = 6144, num_slots: int = 128, seed: int = 2001) -> CommitWorkload:
+    """Hybrid linear-attention stand-in: `layers` layers, each with an fp32 recurrent state
+    [heads, dk, dv] (1 MiB at the defaults) and a bf16 conv window [conv_w - 1, conv_c] (36 KiB)."""
+    shapes = [("recurrent", layers, (heads, dk, dv), np.float32),
+              ("conv", layers, (conv_w - 1, conv_c), np.uint16)]
+    return make_commit(B, k, num_slots, shapes, seed=seed,
+                       name=f"commit_B{B}_k{k}_L{layers}_rec{heads}x{dk}x{dv}f32_conv{conv_w - 1}x{conv_c}bf16")
+
+
+COMMIT_CONFIGS = {"hybrid": commit_hybrid}

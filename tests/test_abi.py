@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 @pytest.fixture(scope="module")
 def L():
-    if not os.path.exists(sv.LIB_PATH) or os.path.getmtime(sv.LIB_PATH) < os.path.getmtime(hip_build.SRC):
+    if not os.path.exists(sv.LIB_PATH) or os.path.getmtime(sv.LIB_PATH) < max(map(os.path.getmtime, hip_build.SRCS)):
         hip_build.build()
     return sv.lib()
 
@@ -82,3 +82,37 @@ def test_raw_variant_rejects_missing_output(L):
     assert st == 1
     st = L.spec_verify_raw(P, P, 0, P, P, P, P, 0, 2, 1024, 0, 0, P, P, P, P, P, P, 1 << 30, None)
     assert st == 1
+
+
+def test_commit_rejects_bad_arguments_before_launch(L):
+    """spec_commit's host checks: sizes, tensor count, null pointers, overlapping buffers and aliased
+    per-row arrays are rejected before any device call (a valid call then fails only for want of a GPU)."""
+    def T(vs, cache, rb=64, layers=2):
+        return sv.StateTensor(vs, cache, rb, layers)
+    P = lambda a: ctypes.c_void_p(a)
+    slot, acc, seq, stat = P(0x10000), P(0x20000), P(0x30000), P(0x40000)
+    B, k, ns = 4, 2, 8
+    ok = (sv.StateTensor * 2)(T(0x1000000, 0x2000000), T(0x3000000, 0x4000000, 36, 1))
+
+    def call(descs=ok, n=2, s=slot, a=acc, q=seq, st=stat, B=B, k=k, ns=ns):
+        return L.spec_commit(descs, n, s, a, q, st, B, k, ns, None)
+
+    for kw in [dict(B=0), dict(B=(1 << 20) + 1), dict(k=-1), dict(k=256), dict(ns=0), dict(n=9), dict(n=-1),
+               dict(s=None), dict(a=None), dict(q=acc), dict(st=slot), dict(q=stat)]:
+        assert call(**kw) == 1, kw
+    assert call(descs=None, n=1) == 1
+    bad = [T(0, 0x2000000), T(0x1000000, 0), T(0x1000000, 0x2000000, rb=0), T(0x1000000, 0x2000000, layers=0),
+           T(0x1000000, 0x1000000 + 64 * 2 * 4 * 3 - 64),   # cache starts inside the verify buffer
+           T(0x1000000, 0x2000000, layers=(1 << 31) // 4)]   # layers * B >= 2^31
+    for d in bad:
+        assert call(descs=(sv.StateTensor * 1)(d), n=1) == 1, (d.verify_state, d.state_cache, d.row_bytes, d.layers)
+    two_caches = (sv.StateTensor * 2)(T(0x1000000, 0x2000000), T(0x3000000, 0x2000000 + 64))
+    assert call(descs=two_caches) == 1
+    cross = (sv.StateTensor * 2)(T(0x1000000, 0x2000000), T(0x3000000, 0x1000000 + 128, 36, 1))
+    assert call(descs=cross) == 1
+    # valid arguments: only the device check remains, which fails where no GPU is visible (never run with
+    # a GPU present: the pointers above are not device memory)
+    import torch
+    if torch.cuda.device_count() == 0:
+        assert call() == 3
+        assert call(n=0, descs=None) == 3
