@@ -30,26 +30,34 @@ sys.path.insert(0, ROOT)
 METRIC = "verified rows/s + logits HBM GB/s (% peak), B=64 k=2 V=157184 bf16"
 HBM_PEAK_GBPS = 8000.0
 ROTATE_BYTES = 1 << 30
-KERNEL_SRC = [os.path.join(ROOT, "rejection_sampling_verify_16_amd", "csrc", f)
-              for f in ("specverify.hip", "sv_common.h")]
+_CSRC = os.path.join(ROOT, "rejection_sampling_verify_16_amd", "csrc")
+KERNEL_SRC = [os.path.join(_CSRC, f) for f in ("specverify.hip", "sv_common.h")]
+COMMIT_SRC = [os.path.join(_CSRC, "commit.hip")]
 
 
-def kernel_digest() -> str:
+def kernel_digest(files=None) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SRC:
+    for f in files or KERNEL_SRC:
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
+def _traffic_target(config: str):
+    """(summary file, kernel name fragment, sources) of the dominant kernel of a workload."""
+    if config == "commit":
+        return os.path.join(ROOT, "profiles", "traffic_commit.json"), "k_commit", COMMIT_SRC
+    return os.path.join(ROOT, "profiles", f"traffic_config{config}.json"), "k1_stats", KERNEL_SRC
+
+
 def load_traffic(config: str):
     """HBM traffic per launch from the committed PMC summary, if it was taken on this kernel."""
-    path = os.path.join(ROOT, "profiles", f"traffic_config{config}.json")
+    path, _, files = _traffic_target(config)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_digest") != kernel_digest():
+    if t.get("kernel_digest") != kernel_digest(files):
         return None
     return t.get("bytes_per_launch")
 
@@ -59,7 +67,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--config", default="3", help="workload: 1, 2, 3, 4a, 4b, 5")
+    ap.add_argument("--config", default="3", help="workload: 1, 2, 3, 4a, 4b, 5 (with --pmc-summary also: commit)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--raw-logprobs", action="store_true",
                     help="time spec_verify_raw (also the raw logprobs of the committed tokens)")
@@ -258,7 +266,7 @@ def bench_commit(args, dev):
                                         "row_bytes": int(t.verify_state[0, 0, 0].nbytes)} for t in w.tensors},
                    "committed_rows": int(((w.accept_len >= 1) & (w.accept_len <= w.k + 1)).sum())},
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None, "kernel": "k_commit",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": load_traffic("commit"), "kernel": "k_commit",
                      "kernel_ms_mean": ms_kernel, "algorithmic_bytes": moved},
     }
     if not args.no_cpu_baseline:
@@ -312,7 +320,8 @@ def pmc_summary(args):
     w_scale = copy_bytes / (cw_kib * 1024.0)
     fetch = _pmc_per_kernel(fetch_dir, "FETCH_SIZE")
     write = _pmc_per_kernel(write_dir, "WRITE_SIZE")
-    out = {"config": args.config, "kernel_digest": kernel_digest(), "copy_probe_bytes": copy_bytes,
+    path, main_kernel, files = _traffic_target(args.config)
+    out = {"config": args.config, "kernel_digest": kernel_digest(files), "copy_probe_bytes": copy_bytes,
            "copy_kernel": cf_name, "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
     for name, (kib, n) in fetch.items():
         if "sv::" not in name:
@@ -320,9 +329,9 @@ def pmc_summary(args):
         wk = write.get(name, (0.0, 0))[0]
         out["kernels"][name] = {"fetch_kib_raw": kib, "write_kib_raw": wk, "dispatches": n,
                                 "fetch_bytes": kib * 1024.0 * f_scale, "write_bytes": wk * 1024.0 * w_scale}
-    k1 = [v for k, v in out["kernels"].items() if "k1_stats" in k]
+    k1 = [v for k, v in out["kernels"].items() if main_kernel in k]
+    out["kernel"] = main_kernel
     out["bytes_per_launch"] = (k1[0]["fetch_bytes"] + k1[0]["write_bytes"]) if k1 else None
-    path = os.path.join(ROOT, "profiles", f"traffic_config{args.config}.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
