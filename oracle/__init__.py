@@ -107,6 +107,8 @@ class Oracle:
         L.oracle_raw_logprobs.restype = ctypes.c_int
         L.oracle_commit.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, ctypes.c_int64]
         L.oracle_commit.restype = ctypes.c_int
+        L.oracle_commit_slots.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32]
+        L.oracle_commit_slots.restype = ctypes.c_int
 
     # -- random streams ---------------------------------------------------------------
     def philox(self, ctr, key) -> np.ndarray:
@@ -219,6 +221,23 @@ class Oracle:
                                         int(cache.shape[1]), int(row_bytes))
             if rc != 0:
                 raise ValueError("oracle_commit rejected its arguments")
+        return status
+
+    def commit_slots(self, state_slot, pos_slot, accept_len, num_slots, seq_len=None):
+        """Commit by slot numbers: state_slot int32 [B] and pos_slot int32 [B, k+1] are swapped in place at
+        (b, accept_len[b] - 1) for rows with a valid accept length and slots in 0..num_slots-1; seq_len
+        (int32 [B], may be None) gains accept_len there.  Returns status int32 [B]."""
+        B, k1 = pos_slot.shape
+        for a, shape in ((state_slot, (B,)), (pos_slot, (B, k1))):
+            assert a.dtype == np.int32 and a.flags.c_contiguous and a.shape == shape
+        if seq_len is not None:
+            assert seq_len.dtype == np.int32 and seq_len.flags.c_contiguous and seq_len.shape == (B,)
+        acc = np.ascontiguousarray(np.asarray(accept_len, dtype=np.int32).reshape(B))
+        status = np.zeros(B, dtype=np.int32)
+        rc = self.lib.oracle_commit_slots(_ptr(state_slot), _ptr(pos_slot), _ptr(acc), _ptr(seq_len), _ptr(status),
+                                          B, k1 - 1, int(num_slots))
+        if rc != 0:
+            raise ValueError("oracle_commit_slots rejected its arguments")
         return status
 
     # -- plain sampler ---------------------------------------------------------------------

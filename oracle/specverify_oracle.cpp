@@ -607,6 +607,41 @@ int oracle_commit(const void* verify_state, void* state_cache, const int32_t* st
   return 0;
 }
 
+// The commit step by slot numbers (InfiniLM pull request "add mtp draft models for speculative decoding",
+// the state-consistency row of its mechanism table: verify writes to a scratch slot and a full accept
+// swaps slot numbers instead of copying).  Here the verify forward writes the state after fed position j
+// of row b into pool slot pos_slot[b][j], so any accept length is a swap: the row's committed slot
+// becomes pos_slot[b][accept_len - 1], and the slot it held takes that place among the row's scratch
+// slots.  seq_len and status as in oracle_commit.  No state byte moves.
+int oracle_commit_slots(int32_t* state_slot, int32_t* pos_slot, const int32_t* accept_len, int32_t* seq_len,
+                        int32_t* status, int32_t B, int32_t k, int32_t num_slots) {
+  if (B < 1 || k < 0 || num_slots < 1) return 1;
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t a = accept_len[b];
+    int32_t st = 0;
+    if (a < 1 || a > k + 1) st = 1;
+    else {
+      const int32_t cur = state_slot[b];
+      const int32_t nxt = pos_slot[(size_t)b * (size_t)(k + 1) + (size_t)(a - 1)];
+      if (cur < 0 || cur >= num_slots || nxt < 0 || nxt >= num_slots) st = 2;
+    }
+    if (status) status[b] = st;
+    if (st != 0) continue;
+#if ORACLE_MUTANT == 20
+    const size_t j = (size_t)b * (size_t)(k + 1) + (size_t)(a < k + 1 ? a : k);  // MUTANT 20: one position late
+#else
+    const size_t j = (size_t)b * (size_t)(k + 1) + (size_t)(a - 1);
+#endif
+    const int32_t held = state_slot[b];
+    state_slot[b] = pos_slot[j];
+#if ORACLE_MUTANT != 21
+    pos_slot[j] = held;  // MUTANT 21 leaves the old slot out of the scratch set
+#endif
+    if (seq_len) seq_len[b] += a;
+  }
+  return 0;
+}
+
 int oracle_sample(const void* logits, int32_t dtype, const float* temperature, const int32_t* top_k,
                   const float* top_p, const int32_t* row_b, const int32_t* row_pos, int32_t R, int32_t V,
                   uint64_t seed, uint64_t offset, int32_t* tokens, double* logprobs, double* gap,

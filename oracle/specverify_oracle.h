@@ -113,6 +113,17 @@ int oracle_commit(const void* verify_state, void* state_cache, const int32_t* st
                   const int32_t* accept_len, int32_t* seq_len, int32_t* status, int32_t L, int32_t B, int32_t k,
                   int32_t num_slots, int64_t row_bytes);
 
+/*
+ * Commit step by slot numbers: for every row b with 1 <= accept_len[b] <= k+1 whose current slot
+ * state_slot[b] and accepted-position slot pos_slot[b][accept_len[b]-1] both lie in 0..num_slots-1,
+ *   swap(state_slot[b], pos_slot[b][accept_len[b]-1]);  seq_len[b] += accept_len[b]  (seq_len may be NULL)
+ *   state_slot [B] in/out, pos_slot [B, k+1] in/out; status [B] out (may be NULL): 0 committed,
+ *   1 accept_len out of range, 2 a slot out of range.  Other rows are left as they are.
+ * Returns 0, or 1 for bad scalar arguments (nothing written).
+ */
+int oracle_commit_slots(int32_t* state_slot, int32_t* pos_slot, const int32_t* accept_len, int32_t* seq_len,
+                        int32_t* status, int32_t B, int32_t k, int32_t num_slots);
+
 #ifdef __cplusplus
 }
 #endif

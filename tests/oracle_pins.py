@@ -592,4 +592,60 @@ def pin_commit_matches_sequential_decode(o):
     _commit_rounds(o, L=4, D=17, rdtype=np.uint32, W=4, C=5, B=7, k=4, rounds=4, seed=72)
 
 
+def _commit_slot_rounds(o, L, D, rdtype, W, C, B, k, rounds, seed):
+    rng = np.random.default_rng(seed)
+    toy = _ToyHybrid(rng, L, D, rdtype, W, C)
+    P = B * (k + 2) + 5                                   # pool: a committed slot and k+1 scratch slots per row
+    perm = rng.permutation(P).astype(np.int32)
+    state_slot = perm[:B].copy()
+    pos_slot = perm[B:B * (k + 2)].reshape(B, k + 1).copy()
+    spare = perm[B * (k + 2):]
+    pool_rec = rng.integers(0, 250, size=(L, P, D)).astype(rdtype)
+    pool_conv = rng.integers(0, 60000, size=(L, P, W - 1, C)).astype(np.uint16)
+    spare_rec, spare_conv = pool_rec[:, spare].copy(), pool_conv[:, spare].copy()
+    seq = [(pool_rec[:, state_slot[b]].copy(), pool_conv[:, state_slot[b]].copy(), []) for b in range(B)]
+    seq_len = np.zeros(B, np.int32)
+    last = rng.integers(0, 1000, size=B)
+    for r in range(rounds):
+        fed = np.concatenate([last[:, None], rng.integers(0, 1000, size=(B, k))], axis=1)
+        for b in range(B):                                # verify: read the committed slot, write scratch slots
+            vr, vc = toy.verify(pool_rec[:, state_slot[b]], pool_conv[:, state_slot[b]], fed[b])
+            pool_rec[:, pos_slot[b]] = vr
+            pool_conv[:, pos_slot[b]] = vc
+        acc = rng.integers(1, k + 2, size=B).astype(np.int32)
+        acc[0] = k + 1
+        acc[1 % B] = 1
+        if r == 1:
+            acc[2 % B] = 0
+        before = np.sort(np.concatenate([state_slot, pos_slot.ravel()]))
+        status = o.commit_slots(state_slot, pos_slot, acc, P, seq_len)
+        np.testing.assert_array_equal(np.sort(np.concatenate([state_slot, pos_slot.ravel()])), before)
+        for b in range(B):
+            assert status[b] == (0 if 1 <= acc[b] <= k + 1 else 1)
+            if status[b] == 0:
+                st = seq[b]
+                for x in fed[b, :acc[b]]:
+                    st = toy.step(*st, x)
+                seq[b] = st
+                last[b] = rng.integers(0, 1000)
+            np.testing.assert_array_equal(pool_rec[:, state_slot[b]], seq[b][0])
+            np.testing.assert_array_equal(pool_conv[:, state_slot[b]], seq[b][1])
+            assert seq_len[b] == len(seq[b][2])
+        np.testing.assert_array_equal(pool_rec[:, spare], spare_rec)
+        np.testing.assert_array_equal(pool_conv[:, spare], spare_conv)
+
+
+def pin_commit_slots_matches_sequential_decode(o):
+    """Commit by slot numbers over a pool where verify writes each position's state to a scratch slot of
+    its row: after full and partial commits the state in each row's committed slot equals one-token-at-a-
+    time decoding, the committed and scratch slots stay a permutation of the pool (no slot lost, none
+    shared), rows with an unusable accept length keep their slots, and a slot outside the pool is refused."""
+    _commit_slot_rounds(o, L=3, D=1, rdtype=np.uint8, W=4, C=1, B=6, k=2, rounds=4, seed=80)
+    _commit_slot_rounds(o, L=2, D=9, rdtype=np.uint32, W=3, C=4, B=5, k=4, rounds=4, seed=81)
+    ss = np.array([0, 7], np.int32)
+    ps = np.array([[1, 2], [3, 4]], np.int32)
+    st = o.commit_slots(ss, ps, [2, 2], 7)
+    assert list(st) == [0, 2] and list(ss) == [2, 7] and ps.tolist() == [[1, 0], [3, 4]]
+
+
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_") and callable(v)]

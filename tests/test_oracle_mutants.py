@@ -7,14 +7,14 @@ the extra token, wrong alpha, wrong Gumbel sign, temperature multiplying, top-k 
 one, Philox one round short, bonus at the wrong position, residual without the clamp, raw logprobs
 in base 2, raw logprobs with the temperature applied, commit of the state after the drawn token's
 position, commit with layers and rows swapped, sequence length grown by the accepted drafts only,
-commit ignoring the slot map).
+commit ignoring the slot map, slot commit one position late, slot commit that drops the old slot).
 """
 import pytest
 
 import oracle
 import oracle_pins
 
-MUTANTS = list(range(1, 20))
+MUTANTS = list(range(1, 22))
 
 
 @pytest.mark.parametrize("mutant", MUTANTS)
