@@ -180,6 +180,34 @@ spec_status_t spec_commit(const spec_state_tensor_t* tensors, int32_t n_tensors,
                           const int32_t* accept_len, int32_t* seq_len, int32_t* status, int32_t B, int32_t k,
                           int32_t num_slots, void* stream);
 
+/*
+ * Commit step by slot numbers: the same commit without moving state bytes, for callers whose verify
+ * forward writes each fed position's state into a slot of a shared pool (InfiniLM pull request above, the
+ * state-consistency row of its mechanism table: verify writes a scratch slot and a full accept swaps slot
+ * numbers; keeping one scratch slot per fed position makes every accept length a swap, so a partial
+ * accept needs no replay).  Row b's committed state lives in pool slot state_slot[b] and the verify
+ * forward wrote the state after fed position j into pool slot pos_slot[b][j].  For every row with
+ * 1 <= accept_len[b] <= k+1 whose state_slot[b] and pos_slot[b][accept_len[b]-1] both lie in
+ * 0..num_slots-1:
+ *
+ *   swap(state_slot[b], pos_slot[b][accept_len[b] - 1]);   seq_len[b] += accept_len[b]
+ *
+ * so the accepted position's slot becomes the committed one and the previous committed slot joins the
+ * row's scratch slots for the next verify.  The pool itself is not touched (the caller owns it).
+ *
+ *   state_slot  device int32 [B] in/out
+ *   pos_slot    device int32 [B, k+1] in/out
+ *   accept_len  device int32 [B]   spec_verify's accept_len
+ *   seq_len     device int32 [B] in/out, may be NULL
+ *   status      device int32 [B] out, may be NULL: 0 committed, 1 accept_len outside 1..k+1,
+ *               2 a slot outside 0..num_slots-1 (the row is then left as it is)
+ *   B           1 .. 2^20;  k  0 .. 255;  num_slots >= 1
+ * None of the five arrays may overlap another (SPEC_ERR_INVALID_ARGUMENT).  Enqueues one kernel on
+ * `stream` and returns without synchronising; needs no workspace.
+ */
+spec_status_t spec_commit_slots(int32_t* state_slot, int32_t* pos_slot, const int32_t* accept_len, int32_t* seq_len,
+                                int32_t* status, int32_t B, int32_t k, int32_t num_slots, void* stream);
+
 /* A static, human-readable name of a status code. */
 const char* spec_verify_status_string(spec_status_t status);
 

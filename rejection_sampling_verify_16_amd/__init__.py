@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
         L.spec_verify_status_string.restype = ctypes.c_char_p
         L.spec_commit.argtypes = [ctypes.POINTER(StateTensor), I32, P, P, P, P, I32, I32, I32, P]
         L.spec_commit.restype = ctypes.c_int
+        L.spec_commit_slots.argtypes = [P, P, P, P, P, I32, I32, I32, P]
+        L.spec_commit_slots.restype = ctypes.c_int
         L.spec_set_kernel_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), I32]
         L.spec_set_kernel_events.restype = ctypes.c_int
         _lib = L
@@ -205,6 +207,27 @@ def spec_commit(tensors, state_slot, accept_len, seq_len=None, status=None, stre
                            num_slots, ctypes.c_void_p(stream.cuda_stream))
     if st != 0:
         raise SpecVerifyError(st, "spec_commit")
+    return status
+
+
+def spec_commit_slots(state_slot, pos_slot, accept_len, num_slots: int, seq_len=None, status=None, stream=None):
+    """Commit by slot numbers on device tensors: state_slot int32 [B] and pos_slot int32 [B, k+1] are
+    updated in place (see spec_commit_slots in the C header); seq_len (int32 [B]) too when given.
+    Returns status int32 [B]."""
+    import torch
+    B, k1 = pos_slot.shape
+    for t, shape in ((state_slot, (B,)), (pos_slot, (B, k1)), (accept_len, (B,)), (seq_len, (B,)), (status, (B,))):
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous() or tuple(t.shape) != shape):
+            raise ValueError("state_slot, accept_len, seq_len, status: contiguous int32 [B]; pos_slot [B, k+1]")
+    if status is None:
+        status = torch.empty(B, dtype=torch.int32, device=state_slot.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(state_slot.device)
+    st = lib().spec_commit_slots(state_slot.data_ptr(), pos_slot.data_ptr(), accept_len.data_ptr(),
+                                 seq_len.data_ptr() if seq_len is not None else None, status.data_ptr(), B, k1 - 1,
+                                 int(num_slots), ctypes.c_void_p(stream.cuda_stream))
+    if st != 0:
+        raise SpecVerifyError(st, "spec_commit_slots")
     return status
 
 

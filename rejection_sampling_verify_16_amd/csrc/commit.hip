@@ -148,6 +148,30 @@ __global__ __launch_bounds__(CT) void k_commit(const CommitParams p) {
   }
 }
 
+// Commit by slot numbers: one lane per row swaps the row's committed slot with the slot that holds the
+// state after its accepted position.
+__global__ __launch_bounds__(256) void k_commit_slots(int32_t* __restrict__ state_slot, int32_t* __restrict__ pos_slot,
+                                                      const int32_t* __restrict__ acc, int32_t* __restrict__ seq_len,
+                                                      int32_t* __restrict__ status, int32_t B, int32_t k,
+                                                      int32_t num_slots) {
+  const uint32_t b = blockIdx.x * 256u + threadIdx.x;
+  if (b >= (uint32_t)B) return;
+  const int32_t a = acc[b];
+  int32_t st = 1;
+  if (a >= 1 && a <= k + 1) {
+    const size_t j = (size_t)b * (size_t)(k + 1) + (size_t)(a - 1);
+    const int32_t cur = state_slot[b];
+    const int32_t nxt = pos_slot[j];
+    st = (cur < 0 || cur >= num_slots || nxt < 0 || nxt >= num_slots) ? 2 : 0;
+    if (st == 0) {
+      state_slot[b] = nxt;
+      pos_slot[j] = cur;
+      if (seq_len) seq_len[b] += a;
+    }
+  }
+  if (status) status[b] = st;
+}
+
 static bool overlap(uintptr_t a, uint64_t na, uintptr_t b, uint64_t nb) { return a < b + nb && b < a + na; }
 
 }  // namespace commit
@@ -232,6 +256,27 @@ extern "C" spec_status_t spec_commit(const spec_state_tensor_t* tensors, int32_t
   uint64_t grid = tiles > status_wgs ? tiles : status_wgs;
   if (grid > MAXGRID) grid = MAXGRID;
   hipLaunchKernelGGL(k_commit, dim3((unsigned)grid), dim3(CT), 0, (hipStream_t)stream, p);
+  if (hipGetLastError() != hipSuccess) return SPEC_ERR_LAUNCH;
+  return SPEC_OK;
+}
+
+extern "C" spec_status_t spec_commit_slots(int32_t* state_slot, int32_t* pos_slot, const int32_t* accept_len,
+                                           int32_t* seq_len, int32_t* status, int32_t B, int32_t k, int32_t num_slots,
+                                           void* stream) {
+  if (B < 1 || B > (1 << 20) || k < 0 || k > 255 || num_slots < 1) return SPEC_ERR_INVALID_ARGUMENT;
+  if (!state_slot || !pos_slot || !accept_len) return SPEC_ERR_INVALID_ARGUMENT;
+  // no two of the per-row arrays may overlap
+  const uintptr_t p[5] = {(uintptr_t)state_slot, (uintptr_t)pos_slot, (uintptr_t)accept_len, (uintptr_t)seq_len,
+                          (uintptr_t)status};
+  const uint64_t n[5] = {(uint64_t)B * 4, (uint64_t)B * (uint64_t)(k + 1) * 4, (uint64_t)B * 4, (uint64_t)B * 4,
+                         (uint64_t)B * 4};
+  for (int i = 0; i < 5; ++i)
+    for (int j = i + 1; j < 5; ++j)
+      if (p[i] && p[j] && overlap(p[i], n[i], p[j], n[j])) return SPEC_ERR_INVALID_ARGUMENT;
+  int dev = -1, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || !sv::device_ok(dev, cus)) return SPEC_ERR_UNSUPPORTED_DEVICE;
+  hipLaunchKernelGGL(k_commit_slots, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, (hipStream_t)stream, state_slot,
+                     pos_slot, accept_len, seq_len, status, B, k, num_slots);
   if (hipGetLastError() != hipSuccess) return SPEC_ERR_LAUNCH;
   return SPEC_OK;
 }

@@ -116,3 +116,22 @@ def test_commit_rejects_bad_arguments_before_launch(L):
     if torch.cuda.device_count() == 0:
         assert call() == 3
         assert call(n=0, descs=None) == 3
+
+
+def test_commit_slots_rejects_bad_arguments_before_launch(L):
+    """spec_commit_slots' host checks: sizes, null pointers, overlapping per-row arrays."""
+    P = lambda a: ctypes.c_void_p(a)
+    ss, ps, acc, seq, st = P(0x10000), P(0x20000), P(0x30000), P(0x40000), P(0x50000)
+    B, k, ns = 4, 2, 100
+
+    def call(ss=ss, ps=ps, acc=acc, seq=seq, st=st, B=B, k=k, ns=ns):
+        return L.spec_commit_slots(ss, ps, acc, seq, st, B, k, ns, None)
+
+    for kw in [dict(B=0), dict(B=(1 << 20) + 1), dict(k=-1), dict(k=256), dict(ns=0), dict(ss=None), dict(ps=None),
+               dict(acc=None), dict(ps=P(0x10000 + 8)), dict(seq=P(0x20000 + 4 * 4 * 3 - 4)), dict(st=acc),
+               dict(seq=st)]:
+        assert call(**kw) == 1, kw
+    import torch
+    if torch.cuda.device_count() == 0:
+        assert call() == 3
+        assert call(seq=None, st=None) == 3

@@ -144,3 +144,34 @@ def test_commit_hybrid_full_size(o):
 def test_commit_hybrid_k4(o):
     """k = 4 drafts, 32 rows, 6 layers."""
     run_case(o, W.commit_hybrid(B=32, k=4, layers=6, num_slots=40, seed=2002))
+
+
+@pytest.mark.parametrize("B,k", [(1, 0), (7, 1), (64, 2), (300, 4), (5000, 8), (1 << 20, 2)])
+def test_commit_slots_parity(o, B, k):
+    """spec_commit_slots against the oracle, two calls in a row: slot arrays, sequence lengths and status
+    exactly, including rows with unusable accept lengths and slots outside the pool."""
+    import torch
+    import rejection_sampling_verify_16_amd as sv
+    print(f"commit_slots case B={B} k={k}", flush=True)
+    rng = np.random.default_rng(B * 31 + k)
+    P = B * (k + 2) + 7
+    perm = rng.permutation(P).astype(np.int32)
+    ss = perm[:B].copy()
+    ps = perm[B:B * (k + 2)].reshape(B, k + 1).copy()
+    if B >= 7:
+        bad = rng.choice(B, size=max(2, B // 100), replace=False)
+        ss[bad[0::2]] = P + bad[0::2].astype(np.int32)
+        ps[bad[1::2], rng.integers(0, k + 1, size=len(bad[1::2]))] = -1
+    seq = rng.integers(0, 1000, size=B).astype(np.int32)
+    d = {n: torch.from_numpy(a.copy()).to("cuda:0") for n, a in (("ss", ss), ("ps", ps), ("seq", seq))}
+    for r in range(2):
+        acc = W.accept_lengths(rng, B, k, 0.7)
+        if B >= 7:
+            acc[rng.choice(B, size=3, replace=False)] = [0, -2, k + 2]
+        st_h = o.commit_slots(ss, ps, acc, P, seq)
+        st_d = sv.spec_commit_slots(d["ss"], d["ps"], torch.from_numpy(acc).to("cuda:0"), P, seq_len=d["seq"])
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(st_d.cpu().numpy(), st_h)
+        np.testing.assert_array_equal(d["ss"].cpu().numpy(), ss)
+        np.testing.assert_array_equal(d["ps"].cpu().numpy(), ps)
+        np.testing.assert_array_equal(d["seq"].cpu().numpy(), seq)
