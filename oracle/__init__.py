@@ -80,6 +80,25 @@ class VerifyResult:
                 | (self.topp_margin <= tol_topp) | self.fallback)
 
 
+@dataclass
+class TreeResult:
+    tokens: np.ndarray       # int32 [B, N]
+    path: np.ndarray         # int32 [B, N]
+    accept_len: np.ndarray   # int32 [B]
+    logprobs: np.ndarray     # float64 [B, N]
+    accept_margin: np.ndarray  # float64 [B]
+    gumbel_gap: np.ndarray     # float64 [B]
+    topp_margin: np.ndarray    # float64 [B]
+    stop_node: np.ndarray      # int32 [B]
+
+    @property
+    def sentinel(self) -> np.ndarray:
+        return self.accept_len == 0
+
+    def margin_rows(self, tol_accept: float = 1e-5, tol_gap: float = 1e-5, tol_topp: float = 1e-5) -> np.ndarray:
+        return (self.accept_margin <= tol_accept) | (self.gumbel_gap <= tol_gap) | (self.topp_margin <= tol_topp)
+
+
 class Oracle:
     """Loaded oracle library (optionally a negative-control mutant)."""
 
@@ -107,6 +126,9 @@ class Oracle:
         L.oracle_raw_logprobs.restype = ctypes.c_int
         L.oracle_commit.argtypes = [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, ctypes.c_int64]
         L.oracle_commit.restype = ctypes.c_int
+        L.oracle_tree_verify.argtypes = [_P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _U64, _U64, _P, _P, _P, _P,
+                                         _P, _I32]
+        L.oracle_tree_verify.restype = ctypes.c_int
         L.oracle_commit_slots.argtypes = [_P, _P, _P, _P, _P, _I32, _I32, _I32]
         L.oracle_commit_slots.restype = ctypes.c_int
 
@@ -170,6 +192,37 @@ class Oracle:
             raise ValueError("oracle_spec_verify rejected its scalar arguments")
         return VerifyResult(tokens, acc, lp, al, diag[:, 0].copy(), diag[:, 1].copy(), diag[:, 2].copy(),
                             diag[:, 3].copy(), (fl & 1) != 0, (fl & 2) != 0, (fl >> 8).astype(np.int32))
+
+    # -- tree verification ---------------------------------------------------------------
+    def tree_verify(self, target, parent, node_tokens, temperature, top_k, top_p, seed: int = 0, offset: int = 0,
+                    num_threads: int = 0) -> TreeResult:
+        """Recursive rejection over a draft tree per batch row: target [B, N, V] (uint16 bf16 bits or
+        float32), parent and node_tokens int32 [B, N] (entry 0, the root, ignored), parameters [B]."""
+        target = np.ascontiguousarray(target)
+        if target.dtype == np.uint16:
+            dtype = DTYPE_BF16
+        elif target.dtype == np.float32:
+            dtype = DTYPE_F32
+        else:
+            raise TypeError("logits must be uint16 (bf16 bits) or float32")
+        B, N, V = target.shape
+        par = np.ascontiguousarray(np.asarray(parent, dtype=np.int32).reshape(B, N))
+        tok = np.ascontiguousarray(np.asarray(node_tokens, dtype=np.int32).reshape(B, N))
+        T = np.ascontiguousarray(np.asarray(temperature, dtype=np.float32).reshape(B))
+        K = np.ascontiguousarray(np.asarray(top_k, dtype=np.int32).reshape(B))
+        P = np.ascontiguousarray(np.asarray(top_p, dtype=np.float32).reshape(B))
+        tokens = np.zeros((B, N), dtype=np.int32)
+        path = np.zeros((B, N), dtype=np.int32)
+        acc = np.zeros(B, dtype=np.int32)
+        lp = np.zeros((B, N), dtype=np.float64)
+        diag = np.zeros((B, 4), dtype=np.float64)
+        rc = self.lib.oracle_tree_verify(_ptr(target), dtype, _ptr(par), _ptr(tok), _ptr(T), _ptr(K), _ptr(P), B, N, V,
+                                         int(seed), int(offset), _ptr(tokens), _ptr(path), _ptr(acc), _ptr(lp),
+                                         _ptr(diag), int(num_threads))
+        if rc != 0:
+            raise ValueError("oracle_tree_verify rejected its scalar arguments")
+        stop = np.where(acc > 0, diag[:, 3], -1).astype(np.int32)
+        return TreeResult(tokens, path, acc, lp, diag[:, 0].copy(), diag[:, 1].copy(), diag[:, 2].copy(), stop)
 
     # -- raw logprobs of the committed tokens --------------------------------------------
     def raw_logprobs(self, target, tokens, accept_len, temperature=None, num_threads: int = 0) -> np.ndarray:

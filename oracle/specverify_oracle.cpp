@@ -448,6 +448,164 @@ void verify_row(const VerifyArgs& a, int32_t b) {
   if (a.dflags) a.dflags[b] = flags | (n << 8);
 }
 
+// ---------------------------------------------------------------------------------------
+// One batch row of tree verification.  The pages name only the draft-tree parameters (EAGLE top-k
+// through SGLang's NEXTN passthrough, AReaL pull request "MTP training with speculative decoding
+// rollout", its key-changes list); the rule below is the published recursive rejection for drafts
+// that are distinct tokens chosen deterministically (top-k children), taken from outside the pages:
+// at a node u with target distribution p_u and children c_1..c_m (node-index order), one uniform U
+// (the accept stream at position = depth) accepts the first child j with U < p_u(t_1) + ... +
+// p_u(t_j); if none is accepted the token is drawn from p_u with the children's tokens removed
+// (renormalised), and at a leaf from p_u itself.  Every emitted token is then distributed exactly as
+// p_u, so the committed sequence follows the target sampler.  A tree whose nodes each have one child
+// is chain verification with one-hot draft distributions.
+// ---------------------------------------------------------------------------------------
+struct TreeArgs {
+  const void* target;
+  int32_t dtype;
+  const int32_t* parent;
+  const int32_t* node_tokens;
+  const float* temperature;
+  const int32_t* top_k;
+  const float* top_p;
+  int32_t B, N, V;
+  uint64_t seed;
+  uint32_t offset;
+  int32_t* tokens;
+  int32_t* path;
+  int32_t* accept_len;
+  double* logprobs;
+  double* diag;
+};
+
+void tree_sentinel(const TreeArgs& a, int32_t b) {
+  for (int32_t i = 0; i < a.N; ++i) {
+    a.tokens[(size_t)b * a.N + i] = -1;
+    a.path[(size_t)b * a.N + i] = -1;
+    a.logprobs[(size_t)b * a.N + i] = kNaN;
+  }
+  a.accept_len[b] = 0;
+  if (a.diag)
+    for (int j = 0; j < 4; ++j) a.diag[(size_t)b * 4 + j] = kInf;
+}
+
+void tree_row(const TreeArgs& a, int32_t b) {
+  const int32_t N = a.N, V = a.V;
+  const int32_t* par = a.parent + (size_t)b * N;
+  const int32_t* tok = a.node_tokens + (size_t)b * N;
+  const float Tf = a.temperature[b];
+  const int32_t K = a.top_k[b];
+  const float Pf = a.top_p[b];
+  if (!params_valid(Tf, K, Pf)) return tree_sentinel(a, b);
+  // the tree: every node but the root has an earlier parent and a token in range; siblings differ
+  std::vector<std::vector<int32_t>> children((size_t)N);
+  for (int32_t i = 1; i < N; ++i) {
+    if (par[i] < 0 || par[i] >= i || tok[i] < 0 || tok[i] >= V) return tree_sentinel(a, b);
+    for (int32_t c : children[(size_t)par[i]])
+      if (tok[c] == tok[i]) return tree_sentinel(a, b);
+    children[(size_t)par[i]].push_back(i);
+  }
+  const double T = (double)Tf, P = (double)Pf;
+  std::vector<RowDist> p((size_t)N);
+  std::vector<double> l;
+  double topp_margin = kInf;
+  for (int32_t i = 0; i < N; ++i) {
+    load_row(a.target, a.dtype, (size_t)b * N + i, V, l);
+    if (row_has_nan_or_posinf(l) || !row_dist(l, T, K, P, p[(size_t)i])) return tree_sentinel(a, b);
+    topp_margin = std::min(topp_margin, p[(size_t)i].topp_margin);
+  }
+
+  // walk from the root
+  std::vector<int32_t> path;
+  int32_t u = 0;
+  bool leaf = false;
+  double accept_margin = kInf;
+  for (;;) {
+    const std::vector<int32_t>& ch = children[(size_t)u];
+    if (ch.empty()) {
+      leaf = true;
+      break;
+    }
+    const int32_t d = (int32_t)path.size();
+#if ORACLE_MUTANT == 24
+    const RowDist& pu = p[(size_t)(d == 0 ? 0 : par[u])];  // MUTANT 24: the parent's distribution
+#else
+    const RowDist& pu = p[(size_t)u];
+#endif
+    int32_t acc = -1;
+    if (T == 0.0) {
+      for (int32_t c : ch)
+        if (tok[c] == pu.argmax) acc = c;
+    } else {
+      const double U = accept_uniform(a.seed, (uint32_t)b, (uint32_t)d, a.offset);
+      double S = 0.0;
+      for (int32_t c : ch) {
+#if ORACLE_MUTANT == 23
+        S = pu.p[(size_t)tok[c]];  // MUTANT 23: each child tested against its own mass alone
+#else
+        S += pu.p[(size_t)tok[c]];
+#endif
+        if (S > 0.0) accept_margin = std::min(accept_margin, std::fabs(U - S));
+        if (U < S) {
+          acc = c;
+          break;
+        }
+      }
+    }
+    if (acc < 0) break;
+    path.push_back(acc);
+    u = acc;
+  }
+  const int32_t d = (int32_t)path.size();
+
+  // the committed extra token at the stopping node u
+  int32_t y;
+  double gap = kInf;
+  if (T == 0.0) {
+    y = p[(size_t)u].argmax;
+  } else {
+    std::vector<double> w = p[(size_t)u].p;
+    if (!leaf) {
+      double mass = 0.0;
+#if ORACLE_MUTANT != 22
+      for (int32_t c : children[(size_t)u]) w[(size_t)tok[c]] = 0.0;  // MUTANT 22 keeps the rejected children
+#endif
+      for (double v : w) mass += v;
+      if (!(mass > 0.0)) w = p[(size_t)u].p;  // reachable only through rounding (as R7)
+    }
+#if ORACLE_MUTANT == 25
+    y = gumbel_argmax(w, a.seed, 1u, (uint32_t)b, (uint32_t)d + 1u, a.offset, &gap);  // MUTANT 25: one depth late
+#else
+    y = gumbel_argmax(w, a.seed, 1u, (uint32_t)b, (uint32_t)d, a.offset, &gap);
+#endif
+  }
+
+  for (int32_t i = 0; i < N; ++i) {
+    const size_t o = (size_t)b * N + i;
+    if (i < d) {
+      const int32_t row = i == 0 ? 0 : path[(size_t)i - 1];
+      a.tokens[o] = tok[path[(size_t)i]];
+      a.path[o] = path[(size_t)i];
+      a.logprobs[o] = std::log(p[(size_t)row].p[(size_t)tok[path[(size_t)i]]]);
+    } else if (i == d) {
+      a.tokens[o] = y;
+      a.path[o] = -1;
+      a.logprobs[o] = std::log(p[(size_t)u].p[(size_t)y]);
+    } else {
+      a.tokens[o] = -1;
+      a.path[o] = -1;
+      a.logprobs[o] = 0.0;
+    }
+  }
+  a.accept_len[b] = d + 1;
+  if (a.diag) {
+    a.diag[(size_t)b * 4 + 0] = accept_margin;
+    a.diag[(size_t)b * 4 + 1] = gap;
+    a.diag[(size_t)b * 4 + 2] = topp_margin;
+    a.diag[(size_t)b * 4 + 3] = (double)u;
+  }
+}
+
 template <class F>
 void parallel_rows(int32_t n_rows, int32_t num_threads, F f) {
   int32_t nt = num_threads > 0 ? num_threads : (int32_t)std::thread::hardware_concurrency();
@@ -639,6 +797,18 @@ int oracle_commit_slots(int32_t* state_slot, int32_t* pos_slot, const int32_t* a
 #endif
     if (seq_len) seq_len[b] += a;
   }
+  return 0;
+}
+
+int oracle_tree_verify(const void* target_logits, int32_t dtype, const int32_t* parent, const int32_t* node_tokens,
+                       const float* temperature, const int32_t* top_k, const float* top_p, int32_t B, int32_t N,
+                       int32_t V, uint64_t seed, uint64_t offset, int32_t* tokens, int32_t* path, int32_t* accept_len,
+                       double* logprobs, double* diag, int32_t num_threads) {
+  if (B < 1 || N < 1 || V < 1 || offset >= (1ull << 32)) return 1;
+  if (dtype != ORACLE_DTYPE_BF16 && dtype != ORACLE_DTYPE_F32) return 1;
+  TreeArgs a{target_logits, dtype, parent, node_tokens, temperature, top_k, top_p, B, N, V, seed, (uint32_t)offset,
+             tokens, path, accept_len, logprobs, diag};
+  parallel_rows(B, num_threads, [&](int32_t b) { tree_row(a, b); });
   return 0;
 }
 

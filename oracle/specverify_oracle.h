@@ -124,6 +124,25 @@ int oracle_commit(const void* verify_state, void* state_cache, const int32_t* st
 int oracle_commit_slots(int32_t* state_slot, int32_t* pos_slot, const int32_t* accept_len, int32_t* seq_len,
                         int32_t* status, int32_t B, int32_t k, int32_t num_slots);
 
+/*
+ * Tree verification (recursive rejection for deterministic, distinct draft children):
+ *   target_logits [B, N, V] (row i: the target distribution after node i; node 0 is the root, the last
+ *   committed token); parent [B, N] (parent[b][i] < i for i >= 1; entry 0 ignored); node_tokens [B, N]
+ *   (the draft token of node i >= 1; siblings must differ); temperature/top_k/top_p [B].
+ *   tokens [B, N] out: the accepted nodes' tokens, then the drawn token, then -1
+ *   path [B, N] out: the accepted node indices (root excluded), then -1
+ *   accept_len [B] out: accepted nodes + 1 (0 = unusable row)
+ *   logprobs [B, N] out: ln p of each committed token under the distribution it was drawn from, 0 after
+ *   diag [B, 4] (may be NULL): [0] min |U - S_j| over evaluated children with S_j > 0, [1] Gumbel top-2
+ *   gap of the final draw, [2] top-p margin over the N rows, [3] the stopping node.
+ * Unusable rows (bad parameters, a bad tree, NaN/+inf or all -inf in any of the N rows) get
+ * accept_len 0, tokens and path -1, logprobs NaN.  Returns 0, or 1 for bad scalar arguments.
+ */
+int oracle_tree_verify(const void* target_logits, int32_t dtype, const int32_t* parent, const int32_t* node_tokens,
+                       const float* temperature, const int32_t* top_k, const float* top_p, int32_t B, int32_t N,
+                       int32_t V, uint64_t seed, uint64_t offset, int32_t* tokens, int32_t* path, int32_t* accept_len,
+                       double* logprobs, double* diag, int32_t num_threads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -648,4 +648,145 @@ def pin_commit_slots_matches_sequential_decode(o):
     assert list(st) == [0, 2] and list(ss) == [2, 7] and ps.tolist() == [[1, 0], [3, 4]]
 
 
+# ---------------------------------------------------------------------------------------
+# tree verification
+# ---------------------------------------------------------------------------------------
+
+def _one_hot_drafts(B, k, V, drafts):
+    """Draft logit rows whose sampler distribution is one-hot at the draft token: 0 there, -inf elsewhere."""
+    d = np.full((B, k, V), -np.inf, dtype=np.float32)
+    for b in range(B):
+        for i in range(k):
+            d[b, i, drafts[b, i]] = 0.0
+    return d
+
+
+def pin_tree_chain_equals_chain_verify(o):
+    """A tree in which every node has one child is chain verification whose draft distributions are one-hot
+    at the draft tokens: same committed tokens, accept lengths and logprobs, row for row, across greedy,
+    untruncated, top-k and top-p rows; the path is nodes 1..n."""
+    rng = np.random.default_rng(90)
+    B, k, V = 600, 3, 24
+    t = rng.normal(0.0, 1.3, size=(B, k + 1, V)).astype(np.float32)
+    drafts = np.zeros((B, k), np.int32)
+    for b in range(B):   # mostly likely tokens, so that some rows accept deep
+        for i in range(k):
+            drafts[b, i] = int(np.argmax(t[b, i])) if rng.random() < 0.7 else int(rng.integers(0, V))
+    T = f32(rng.choice([0.0, 0.7, 1.0, 1.4], size=B))
+    K = rng.choice([0, 3, 8], size=B).astype(np.int32)
+    P = f32(rng.choice([1.0, 0.9, 0.6], size=B))
+    c = o.spec_verify(t, _one_hot_drafts(B, k, V, drafts), drafts, T, K, P, seed=11, offset=2)
+    par = np.tile(np.arange(-1, k, dtype=np.int32), (B, 1))
+    par[:, 0] = 0
+    ntok = np.concatenate([np.zeros((B, 1), np.int32), drafts], axis=1)
+    r = o.tree_verify(t, par, ntok, T, K, P, seed=11, offset=2)
+    np.testing.assert_array_equal(r.accept_len, c.accept_len)
+    np.testing.assert_array_equal(r.tokens, c.tokens)
+    np.testing.assert_allclose(r.logprobs, c.logprobs, rtol=0, atol=1e-12)
+    for b in range(B):
+        n = c.accept_len[b] - 1
+        assert list(r.path[b, :n]) == list(range(1, n + 1)) and np.all(r.path[b, n:] == -1)
+    assert (c.accept_len == k + 1).sum() > 20 and (c.accept_len == 1).sum() > 20
+
+
+def _tree_law(p_rows, parent, tok, V):
+    """Exact law of the committed sequence for one tree: {token tuple: probability}.  p_rows[i] is the
+    sampler distribution after node i; a drawn token that matches a child moves the walk to that child."""
+    N = len(parent)
+    children = {u: [c for c in range(1, N) if parent[c] == u] for u in range(N)}
+    law = {}
+
+    def walk(u, prefix, prob):
+        for y in range(V):
+            py = p_rows[u][y]
+            if py == 0.0:
+                continue
+            nxt = [c for c in children[u] if tok[c] == y]
+            if nxt and children[u]:
+                walk(nxt[0], prefix + (y,), prob * py)
+            else:
+                law[prefix + (y,)] = law.get(prefix + (y,), 0.0) + prob * py
+    walk(0, (), 1.0)
+    return law
+
+
+def pin_tree_joint_law(o):
+    """The committed sequence of tree verification follows the target sampler exactly: chi-square of the
+    whole sequence law over 1e5 independent rows of one tree (with a top-k that removes tokens, so some
+    children have probability 0), against the law enumerated from textbook sampler distributions; the mean
+    accept length matches its closed form 1 + sum over non-root nodes of the product of p along the edges."""
+    rng = np.random.default_rng(91)
+    V, R = 6, 100_000
+    parent = [0, 0, 0, 0, 1, 4, 0]
+    tok = [0, 2, 0, 5, 3, 1, 4]
+    N = len(parent)
+    parent[6] = 2
+    l = rng.normal(0.0, 1.2, size=(N, V)).astype(np.float32)
+    l[0, 2] += 1.5
+    l[1, 3] += 1.5
+    T, K, P = 0.8, 5, 1.0
+    p_rows = [textbook_topk_topp(l[i].astype(np.float64), T, K, P) for i in range(N)]
+    law = _tree_law(p_rows, parent, tok, V)
+    r = o.tree_verify(np.broadcast_to(l, (R, N, V)).copy(), np.tile(parent, (R, 1)), np.tile(tok, (R, 1)),
+                      *_params(R, T, K, P), seed=21, offset=5)
+    keys = sorted(law)
+    index = {kk: i for i, kk in enumerate(keys)}
+    counts = np.zeros(len(keys))
+    for b in range(R):
+        seq = tuple(int(x) for x in r.tokens[b, :r.accept_len[b]])
+        assert seq in index, f"impossible sequence {seq}"
+        counts[index[seq]] += 1
+    probs = np.array([law[kk] for kk in keys])
+    big = probs * R >= 5
+    c2 = np.append(counts[big], counts[~big].sum())
+    p2 = np.append(probs[big], probs[~big].sum())
+    assert chi2_pvalue(c2, p2) > CHI2_P_MIN
+    # closed form of the expected accept length
+    def path_prob(v):
+        pr, u = 1.0, v
+        while u != 0:
+            pr *= p_rows[parent[u]][tok[u]]
+            u = parent[u]
+        return pr
+    expected = 1.0 + sum(path_prob(v) for v in range(1, N))
+    np.testing.assert_allclose(sum(len(kk) * law[kk] for kk in keys), expected, rtol=1e-12)
+    sd = np.std(r.accept_len)
+    assert abs(r.accept_len.mean() - expected) < 5 * sd / math.sqrt(R)
+
+
+def pin_tree_rules(o):
+    """Greedy walks follow the lowest-index argmax through the children (ties included) and end on the
+    argmax; a child outside the kept set is never accepted; unusable trees and rows become sentinels."""
+    V = 8
+    l = np.zeros((1, 4, V), np.float32)
+    l[0, 0, [3, 6]] = 2.0        # tie at the root: 3 is the lowest-index argmax
+    l[0, 1, 5] = 1.0
+    l[0, 3, 1] = 4.0
+    par = np.array([[0, 0, 0, 1]], np.int32)
+    tok = np.array([[0, 6, 3, 5]], np.int32)
+    r = o.tree_verify(l, par, tok, *_params(1, 0.0))
+    assert r.accept_len[0] == 2 and list(r.path[0, :2]) == [2, -1] and list(r.tokens[0, :3]) == [3, 0, -1]
+    # node 2 is a leaf: its row's argmax is token 0 (all zeros): the bonus is the argmax
+    r = o.tree_verify(l, par, np.array([[0, 3, 6, 5]], np.int32), *_params(1, 0.0))
+    assert list(r.tokens[0, :3]) == [3, 5, 1] and list(r.path[0, :2]) == [1, 3]
+    # top-k 1 at T > 0 is one-hot too: a child that is not the argmax is never accepted
+    l1 = l.copy()
+    l1[0, 0, 6] = 1.9             # no tie now: top-k 1 keeps token 3 alone
+    rr = o.tree_verify(np.broadcast_to(l1, (200, 4, V)).copy(), np.tile([0, 0, 0, 1], (200, 1)),
+                       np.tile([0, 6, 2, 5], (200, 1)), *_params(200, 1.0, 1))
+    assert np.all(rr.accept_len == 1) and np.all(rr.tokens[:, 0] == 3)
+    # unusable: parent not earlier, token out of range, siblings with one token, NaN in an unvisited row
+    bad = [(np.array([[0, 0, 2, 1]]), tok), (par, np.array([[0, 6, 3, V]])), (par, np.array([[0, 6, 6, 5]]))]
+    for pa, tk in bad:
+        rb = o.tree_verify(l, pa, tk, *_params(1, 1.0))
+        assert rb.accept_len[0] == 0 and np.all(rb.tokens == -1) and np.all(np.isnan(rb.logprobs))
+    ln = l.copy()
+    ln[0, 3, 7] = np.nan
+    rb = o.tree_verify(ln, par, tok, *_params(1, 1.0))
+    assert rb.accept_len[0] == 0
+    # a single node: the token is drawn from the root's distribution
+    r1 = o.tree_verify(l[:, :1].copy(), np.zeros((1, 1), np.int32), np.zeros((1, 1), np.int32), *_params(1, 0.0))
+    assert r1.accept_len[0] == 1 and r1.tokens[0, 0] == 3
+
+
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_") and callable(v)]

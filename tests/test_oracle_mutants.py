@@ -7,14 +7,16 @@ the extra token, wrong alpha, wrong Gumbel sign, temperature multiplying, top-k 
 one, Philox one round short, bonus at the wrong position, residual without the clamp, raw logprobs
 in base 2, raw logprobs with the temperature applied, commit of the state after the drawn token's
 position, commit with layers and rows swapped, sequence length grown by the accepted drafts only,
-commit ignoring the slot map, slot commit one position late, slot commit that drops the old slot).
+commit ignoring the slot map, slot commit one position late, slot commit that drops the old slot, tree draws that keep the rejected children, tree
+children tested against their own mass alone, the parent's distribution after an accepted child, the
+tree's final draw one depth late).
 """
 import pytest
 
 import oracle
 import oracle_pins
 
-MUTANTS = list(range(1, 22))
+MUTANTS = list(range(1, 26))
 
 
 @pytest.mark.parametrize("mutant", MUTANTS)
