@@ -129,6 +129,46 @@ spec_status_t spec_sample(const void* logits, spec_dtype_t dtype, const float* t
                           size_t workspace_bytes, void* stream);
 
 /*
+ * Tree verification: verify a draft tree per batch row instead of a chain.  The pages name only the
+ * draft-tree parameters (EAGLE top-k, passed through to SGLang's NEXTN speculative decoding: AReaL pull
+ * request "MTP training with speculative decoding rollout", its key-changes list); the rule is the
+ * published recursive rejection for draft children that are distinct tokens chosen deterministically
+ * (top-k of the draft), which keeps the committed sequence distributed exactly as target sampling:
+ *
+ *   Start at the root (node 0: the last committed token).  At a node u with children c_1..c_m (in node
+ *   index order) and sampler distribution p_u (temperature, top-k, top-p as in spec_verify), draw one
+ *   uniform U (the accept stream of spec_verify at position = depth) and accept the first child j with
+ *   U < p_u(t_{c_1}) + ... + p_u(t_{c_j}); continue at that child.  If no child is accepted, draw the
+ *   committed extra token from p_u with the children's tokens removed; at a leaf, draw it from p_u.
+ *   Draws are Gumbel-max on spec_verify's draw stream at position = depth.  Greedy rows (T = 0) follow
+ *   the child whose token is the row's lowest-index argmax and end on the argmax.
+ *
+ * A tree whose nodes each have one child gives exactly spec_verify's outputs for draft rows that are
+ * one-hot at the draft tokens (0 there, -inf elsewhere).
+ *
+ *   target_logits  [B, N, V] contiguous, dtype, 16-byte aligned: row i is the target's logits after node i
+ *   parent         int32 [B, N]  parent[b][i] in 0..i-1 for i >= 1 (entry 0 ignored)
+ *   node_tokens    int32 [B, N]  draft token of node i >= 1 (entry 0 ignored); siblings must differ
+ *   temperature, top_k, top_p   [B] as in spec_verify
+ *   B, N, V        1 <= B <= 2^20, 1 <= N <= 64, B * N <= 2^24, V as in spec_verify
+ *   tokens         out int32 [B, N]  the accepted nodes' tokens, then the drawn token, then -1
+ *   path           out int32 [B, N]  the accepted node indices (root excluded), then -1
+ *   accept_len     out int32 [B]     accepted nodes + 1 (committed tokens); 0 for an unusable row
+ *   logprobs       out float [B, N]  ln p of each committed token under the distribution it was drawn from
+ *                                    (0 for greedy rows), 0 after
+ *   workspace      at least spec_tree_verify_workspace_size(B, N, V, dtype) bytes, same rules as spec_verify
+ * A row is unusable (accept_len 0, tokens and path -1, logprobs NaN) if its parameters are invalid, its
+ * tree breaks the rules above, or any of its N logit rows holds NaN or +inf or is entirely -inf.
+ */
+size_t spec_tree_verify_workspace_size(int32_t B, int32_t N, int32_t V, spec_dtype_t dtype);
+
+spec_status_t spec_tree_verify(const void* target_logits, spec_dtype_t dtype, const int32_t* parent,
+                               const int32_t* node_tokens, const float* temperature, const int32_t* top_k,
+                               const float* top_p, int32_t B, int32_t N, int32_t V, uint64_t seed, uint64_t offset,
+                               int32_t* tokens, int32_t* path, int32_t* accept_len, float* logprobs, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
  * Commit step: after verify, make each batch row's cached model state the state after its last consumed
  * token (AReno pull request above, section "What does this PR do?": the Phase-2 paragraph keeps the
  * recurrent and conv caches stacked across layers with one verify-state buffer, and its per-step table
@@ -212,9 +252,9 @@ spec_status_t spec_commit_slots(int32_t* state_slot, int32_t* pos_slot, const in
 const char* spec_verify_status_string(spec_status_t status);
 
 /*
- * Benchmark hook: per-kernel timing of later calls.  Each spec_verify / spec_sample call enqueues
- * SPEC_NUM_KERNELS kernels: 0 = row statistics and kept thresholds (reads every logit once),
- * 1 = accept chain, alpha and draws (re-reads the draft-position rows).
+ * Benchmark hook: per-kernel timing of later calls.  Each spec_verify / spec_sample / spec_tree_verify
+ * call enqueues SPEC_NUM_KERNELS kernels: 0 = row statistics and kept thresholds (reads every logit once),
+ * 1 = accept chain (or tree walk), alpha and draws (re-reads the rows it draws from).
  *
  *   events  NULL (turns the hook off; count ignored) or 2 * SPEC_NUM_KERNELS hipEvent_t handles,
  *           created by the caller with timing enabled and owned by the caller

@@ -57,6 +57,10 @@ def lib() -> ctypes.CDLL:
         L.spec_sample.restype = ctypes.c_int
         L.spec_verify_status_string.argtypes = [ctypes.c_int]
         L.spec_verify_status_string.restype = ctypes.c_char_p
+        L.spec_tree_verify_workspace_size.argtypes = [I32, I32, I32, ctypes.c_int]
+        L.spec_tree_verify_workspace_size.restype = SZ
+        L.spec_tree_verify.argtypes = [P, ctypes.c_int, P, P, P, P, P, I32, I32, I32, U64, U64, P, P, P, P, P, SZ, P]
+        L.spec_tree_verify.restype = ctypes.c_int
         L.spec_commit.argtypes = [ctypes.POINTER(StateTensor), I32, P, P, P, P, I32, I32, I32, P]
         L.spec_commit.restype = ctypes.c_int
         L.spec_commit_slots.argtypes = [P, P, P, P, P, I32, I32, I32, P]
@@ -165,6 +169,44 @@ def spec_sample(logits, temperature, top_k, top_p, row_b=None, row_pos=None, see
                            ctypes.c_void_p(stream.cuda_stream))
     if st != 0:
         raise SpecVerifyError(st, "spec_sample")
+    return out
+
+
+def tree_workspace_size(B: int, N: int, V: int, dtype: int = SPEC_DTYPE_BF16) -> int:
+    return int(lib().spec_tree_verify_workspace_size(B, N, V, dtype))
+
+
+def spec_tree_verify(target_logits, parent, node_tokens, temperature, top_k, top_p, seed: int = 0, offset: int = 0,
+                     out=None, workspace=None, stream=None):
+    """Tree verification on device tensors: target_logits [B, N, V] (bf16 or fp32), parent and node_tokens
+    int32 [B, N], temperature float32 [B], top_k int32 [B], top_p float32 [B].  Returns a dict with
+    tokens [B, N], path [B, N], accept_len [B] (int32) and logprobs [B, N] (float32)."""
+    import torch
+    B, N, V = target_logits.shape
+    dt = _dtype_code(target_logits)
+    for t in (target_logits, parent, node_tokens, temperature, top_k, top_p):
+        if not t.is_contiguous():
+            raise ValueError("all inputs must be contiguous")
+    dev = target_logits.device
+    if out is None:
+        out = dict(tokens=torch.empty((B, N), dtype=torch.int32, device=dev),
+                   path=torch.empty((B, N), dtype=torch.int32, device=dev),
+                   accept_len=torch.empty((B,), dtype=torch.int32, device=dev),
+                   logprobs=torch.empty((B, N), dtype=torch.float32, device=dev))
+    if workspace is None:
+        n = tree_workspace_size(B, N, V, dt)
+        if n == 0:
+            raise ValueError("invalid sizes for spec_tree_verify")
+        workspace = torch.zeros(n, dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    st = lib().spec_tree_verify(target_logits.data_ptr(), dt, parent.data_ptr(), node_tokens.data_ptr(),
+                                temperature.data_ptr(), top_k.data_ptr(), top_p.data_ptr(), B, N, V, int(seed),
+                                int(offset), out["tokens"].data_ptr(), out["path"].data_ptr(),
+                                out["accept_len"].data_ptr(), out["logprobs"].data_ptr(), workspace.data_ptr(),
+                                workspace.numel(), ctypes.c_void_p(stream.cuda_stream))
+    if st != 0:
+        raise SpecVerifyError(st, "spec_tree_verify")
     return out
 
 

@@ -47,6 +47,8 @@ namespace sv {
 
 constexpr int MODE_VERIFY = 0;
 constexpr int MODE_SAMPLE = 1;  // plain sampler: k = 0, one logit row per batch row, stream tag 2
+constexpr int MODE_TREE = 2;    // tree verification: N = rows = k + 1 target rows per batch row, no draft rows
+constexpr int MAXN = 64;        // nodes per draft tree
 constexpr int MAXDEV = 64;
 constexpr int VPT1 = 8;         // K1: 16-byte vectors per thread per slice
 constexpr int VPT5 = 2;         // K5
@@ -114,6 +116,8 @@ struct Params {
   const int32_t* row_b;      // plain sampler: stream coordinate b of each row (NULL = row index)
   const int32_t* row_pos;    // plain sampler: stream coordinate i of each row (NULL = 0)
   uint32_t key0, key1, offset;
+  const int32_t* parent;     // tree mode: [B][N] parent of each node (the draft tokens are the nodes' tokens)
+  int32_t* path;             // tree mode: [B][N] accepted node indices
   int32_t* tokens;
   int32_t* accept_len;
   float* logprobs;
@@ -1995,6 +1999,225 @@ __global__ __launch_bounds__(NT) void k5_verify(Params p) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Tree verification: one workgroup per (batch row, K5-sized slice).  Every workgroup checks the tree,
+// gathers each node's token logit from its parent's row and walks the tree from the root out of LDS
+// (one uniform per depth on the accept stream: the first child whose cumulative target mass exceeds it
+// is accepted); then all slices race over the stopping node's row -- with its children's tokens removed
+// after a rejection (weights p, as the chain's residual with a one-hot draft), or the plain bonus
+// weights at a leaf -- and the last slice to arrive writes the outputs.  A chain of single children is
+// therefore the chain verify step with one-hot draft rows, bit for bit.
+// ---------------------------------------------------------------------------------------------
+struct TreeSmem {
+  RedSmem rs;
+  float m[MAXN], Z[MAXN], lz[MAXN], fthr[MAXN], gl[MAXN], u[MAXN];
+  int32_t arg[MAXN], par[MAXN], tok[MAXN], path[MAXN], ex[MAXN];
+  uint32_t state[MAXN];
+  int32_t nex, d, stop, leaf;
+};
+
+// Race over one slice of the stopping node's row after a rejection: weights kept_p on the kept entries,
+// except the node's children's tokens (stream tag 1, position = depth).
+template <class E, int VPT>
+__device__ __forceinline__ void tree_resid_slice(const Params& p, const TreeSmem& sm, const uint4 (&va)[VPT], int x0, int nv,
+                                                 float c, float mt, float lt, float tt, uint32_t sb, uint32_t sj,
+                                                 float& best, int& bidx, float& bval) {
+  constexpr int EPV = E::EPV;
+  const int tid = threadIdx.x, nex = sm.nex;
+#pragma unroll 1
+  for (int u = 0; u < VPT; ++u) {
+    const int j = tid + u * NT;
+    if (j >= nv) continue;
+    const uint4 a = pick_vec<VPT>(va, u);
+    bool kept = false;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) kept = kept || E::get(a, e) >= tt;
+    if (!kept) continue;
+#pragma unroll 1
+    for (int g = 0; g < EPV; g += 4) {
+      const int x = x0 + j * EPV + g;
+      float w[4];
+      bool any = false;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w[e] = kept_p(E::get(a, g + e), mt, c, lt, tt);
+        if (w[e] > 0.0f)
+          for (int t = 0; t < nex; ++t)
+            if (sm.ex[t] == x + e) w[e] = 0.0f;
+        any = any || w[e] > 0.0f;
+      }
+      if (!any) continue;
+      const uint4 w4 = philox10(make_uint4((uint32_t)x >> 2, sb, (1u << 24) | sj, p.offset), p.key0, p.key1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (w[e] > 0.0f) {
+          const uint32_t word = e == 0 ? w4.x : e == 1 ? w4.y : e == 2 ? w4.z : w4.w;
+          race_take(best, bidx, bval, race_key(w[e], word), x + e, E::get(a, g + e));
+        }
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void tree_sentinel(const Params& p, int b) {
+  const int N = p.rows, tid = threadIdx.x;
+  if (tid < N) {
+    p.tokens[(size_t)b * N + tid] = -1;
+    p.path[(size_t)b * N + tid] = -1;
+    p.logprobs[(size_t)b * N + tid] = __builtin_nanf("");
+  }
+  if (tid == 0) p.accept_len[b] = 0;
+}
+
+// Outputs of a batch row whose walk ended at depth d on node u with drawn token y (logit yv).
+__device__ __forceinline__ void tree_emit(const Params& p, const TreeSmem& sm, int b, const RowParams& q, int y, float yv) {
+  const int N = p.rows, tid = threadIdx.x, d = sm.d, u = sm.stop;
+  if (tid < N) {
+    int t = -1, pth = -1;
+    float lp = 0.0f;
+    if (tid < d) {
+      const int node = sm.path[tid], row = tid == 0 ? 0 : sm.path[tid - 1];
+      t = sm.tok[node];
+      pth = node;
+      if (!q.greedy) lp = (sm.gl[node] - sm.m[row]) / q.T - logf(sm.Z[row]);
+    } else if (tid == d) {
+      t = y;
+      if (!q.greedy) lp = (yv - sm.m[u]) / q.T - logf(sm.Z[u]);
+    }
+    p.tokens[(size_t)b * N + tid] = t;
+    p.path[(size_t)b * N + tid] = pth;
+    p.logprobs[(size_t)b * N + tid] = lp;
+  }
+  if (tid == 0) p.accept_len[b] = d + 1;
+}
+
+template <class E, int VPT>
+__global__ __launch_bounds__(NT) void k_tree(Params p) {
+  __shared__ TreeSmem sm;
+  constexpr int EPV = E::EPV;
+  constexpr int esize = 16 / EPV;
+  const int b = blockIdx.x / p.S5, s = blockIdx.x - b * p.S5;
+  const int N = p.rows, tid = threadIdx.x;
+  const RowParams q = row_params(p, b);
+  if (tid < N) {
+    const RowInfo* ri = p.rinfo + (size_t)b * N + tid;
+    sm.m[tid] = ri->m;
+    sm.arg[tid] = ri->arg;
+    sm.Z[tid] = ri->Z;
+    sm.lz[tid] = ri->lz;
+    sm.fthr[tid] = ri->fthr;
+    sm.state[tid] = ri->state;
+    sm.par[tid] = p.parent[(size_t)b * N + tid];
+    sm.tok[tid] = p.draft_tokens[(size_t)b * N + tid];
+    const uint4 w4 = philox10(make_uint4((uint32_t)tid >> 2, (uint32_t)b, 0u, p.offset), p.key0, p.key1);
+    const int qq = tid & 3;
+    sm.u[tid] = u24(qq == 0 ? w4.x : qq == 1 ? w4.y : qq == 2 ? w4.z : w4.w);
+  }
+  __syncthreads();
+  // the tree: every node but the root has an earlier parent and a token in range; siblings differ
+  bool bad = false;
+  if (tid < N) {
+    bad = (sm.state[tid] & ST_BAD) != 0;
+    if (tid >= 1) {
+      const int pa = sm.par[tid], tk = sm.tok[tid];
+      bad = bad || pa < 0 || pa >= tid || tk < 0 || tk >= p.V;
+      for (int j = 1; j < tid; ++j) bad = bad || (sm.par[j] == pa && sm.tok[j] == tk);
+    }
+  }
+  const bool ok = q.ok && !__syncthreads_or(bad);
+  if (!ok) {
+    if (s == 0) tree_sentinel(p, b);
+    return;
+  }
+  if (tid >= 1 && tid < N) sm.gl[tid] = E::load1(row_ptr(p, b, sm.par[tid], esize), sm.tok[tid]);
+  __syncthreads();
+  if (tid == 0) {
+    int u = 0, d = 0, leaf = 0;
+    for (;;) {
+      int acc = -1;
+      bool any = false;
+      float S = 0.0f;
+      for (int c = u + 1; c < N; ++c) {  // children have larger indices than their parent
+        if (sm.par[c] != u) continue;
+        any = true;
+        if (q.greedy) {
+          if (sm.tok[c] == sm.arg[u]) {
+            acc = c;
+            break;
+          }
+        } else {
+          S += kept_p(sm.gl[c], sm.m[u], q.c, sm.lz[u], sm.fthr[u]);
+          if (sm.u[d] < S) {
+            acc = c;
+            break;
+          }
+        }
+      }
+      if (!any) {
+        leaf = 1;
+        break;
+      }
+      if (acc < 0) break;
+      sm.path[d++] = acc;
+      u = acc;
+    }
+    int ne = 0;
+    if (!leaf)
+      for (int c = u + 1; c < N; ++c)
+        if (sm.par[c] == u) sm.ex[ne++] = sm.tok[c];
+    sm.nex = ne;
+    sm.d = d;
+    sm.stop = u;
+    sm.leaf = leaf;
+  }
+  __syncthreads();
+  const int u = sm.stop, d = sm.d;
+  if (q.greedy) {
+    if (s == 0) tree_emit(p, sm, b, q, sm.arg[u], sm.m[u]);
+    return;
+  }
+  const int x0 = s * p.L5;
+  const int nv = min(p.L5, p.V - x0) / EPV;
+  uint4 v[VPT];
+  load_slice<E, VPT>(row_ptr(p, b, u, esize), x0, nv, v);
+  float best = 0.0f, bval = 0.0f;
+  int bidx = INT_MAX;
+  if (sm.leaf)
+    race_slice<E, VPT, false>(p, v, v, x0, nv, q.c, sm.m[u], 0.0f, sm.fthr[u], 0.0f, 0.0f, 0.0f, 1u, (uint32_t)b,
+                              (uint32_t)d, best, bidx, bval);
+  else
+    tree_resid_slice<E, VPT>(p, sm, v, x0, nv, q.c, sm.m[u], sm.lz[u], sm.fthr[u], (uint32_t)b, (uint32_t)d, best,
+                             bidx, bval);
+  block_race(sm.rs, best, bidx, bval);
+  FinalPart* fp = p.fin5 + (size_t)b * p.S5 + s;
+  if (tid == 0) {
+    stf(&fp->key, best);
+    st32(&fp->idx, (uint32_t)bidx);
+    stf(&fp->val, bval);
+  }
+  if (!arrive_last(&p.cnt5[b], (uint32_t)p.S5, &sm.rs.flag)) return;
+  best = 0.0f;
+  bval = 0.0f;
+  bidx = INT_MAX;
+  for (int sl = tid; sl < p.S5; sl += NT) {
+    const FinalPart* f = p.fin5 + (size_t)b * p.S5 + sl;
+    race_take(best, bidx, bval, ldf(&f->key), (int)ld32(&f->idx), ldf(&f->val));
+  }
+  block_race(sm.rs, best, bidx, bval);
+  if (bidx == INT_MAX) {
+    // nothing left after removing the children (rounding only): draw from p_u over the whole row
+    const uint4* row = (const uint4*)row_ptr(p, b, u, esize);
+    for (int j = tid; j < p.V / EPV; j += NT)
+      gumbel_vec<E>(row[j], j * EPV, sm.m[u], q.c, sm.fthr[u], 1u, (uint32_t)b, (uint32_t)d, p, best, bidx, bval);
+    block_race(sm.rs, best, bidx, bval);
+  }
+  if (bidx < 0 || bidx >= p.V)
+    tree_sentinel(p, b);  // no candidate: not reachable for a valid row
+  else
+    tree_emit(p, sm, b, q, bidx, bval);
+  if (tid == 0) atomicExch(&p.cnt5[b], 0u);
+}
+
+// ---------------------------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------------------------
 struct Geo {
@@ -2005,13 +2228,18 @@ struct Geo {
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-static bool make_geo(int32_t B, int32_t k, int32_t V, spec_dtype_t dtype, Geo& g) {
+// tree_nodes > 0: tree verification with that many nodes (target rows) per batch row; k is ignored.
+static bool make_geo(int32_t B, int32_t k, int32_t V, spec_dtype_t dtype, Geo& g, int32_t tree_nodes = 0) {
+  if (tree_nodes > 0) {
+    if (tree_nodes > MAXN) return false;
+    k = 0;
+  }
   if (B < 1 || B > (1 << 20) || k < 0 || k > MAXK || V < 8 || V > (1 << 20)) return false;
   if (dtype != SPEC_DTYPE_BF16 && dtype != SPEC_DTYPE_F32) return false;
   g.esize = dtype == SPEC_DTYPE_BF16 ? 2 : 4;
   g.EPV = 16 / g.esize;
   if (V % g.EPV != 0) return false;
-  g.rows = 2 * k + 1;
+  g.rows = tree_nodes > 0 ? tree_nodes : 2 * k + 1;
   if ((long long)B * g.rows > (1 << 24)) return false;  // item counts stay below 2^31
   g.R = B * g.rows;
   g.L1 = NT * g.EPV * VPT1;
@@ -2070,6 +2298,14 @@ static void enqueue(const Params& p, int cus, hipStream_t st) {
   static_assert(WTOP / 2 == NT && NBC == NT, "K1 assumes one histogram word pair per thread");
   (void)cus;
   prof_mark(0, st);
+  if (p.mode == MODE_TREE) {
+    hipLaunchKernelGGL((k1_stats<E, VPT1, false>), dim3((unsigned)(p.R * p.S1)), dim3(NT), 0, st, p);
+    prof_mark(1, st);
+    prof_mark(2, st);
+    hipLaunchKernelGGL((k_tree<E, VPT5>), dim3((unsigned)(p.B * p.S5)), dim3(NT), 0, st, p);
+    prof_mark(3, st);
+    return;
+  }
   if (p.raw_logprobs)
     hipLaunchKernelGGL((k1_stats<E, VPT1, true>), dim3((unsigned)(p.R * p.S1)), dim3(NT), 0, st, p);
   else
@@ -2223,6 +2459,47 @@ extern "C" spec_status_t spec_sample(const void* logits, spec_dtype_t dtype, con
   p.key1 = (uint32_t)(seed >> 32);
   p.offset = (uint32_t)offset;
   p.tokens = tokens;
+  p.logprobs = logprobs;
+  return launch(p, g, dtype, workspace, workspace_bytes, stream);
+}
+
+extern "C" size_t spec_tree_verify_workspace_size(int32_t B, int32_t N, int32_t V, spec_dtype_t dtype) {
+  Geo g;
+  if (N < 1 || !make_geo(B, 0, V, dtype, g, N)) return 0;
+  return g.total;
+}
+
+extern "C" spec_status_t spec_tree_verify(const void* target_logits, spec_dtype_t dtype, const int32_t* parent,
+                                          const int32_t* node_tokens, const float* temperature, const int32_t* top_k,
+                                          const float* top_p, int32_t B, int32_t N, int32_t V, uint64_t seed,
+                                          uint64_t offset, int32_t* tokens, int32_t* path, int32_t* accept_len,
+                                          float* logprobs, void* workspace, size_t workspace_bytes, void* stream) {
+  Geo g;
+  if (N < 1 || !make_geo(B, 0, V, dtype, g, N)) return SPEC_ERR_INVALID_ARGUMENT;
+  if (offset >= (1ull << 32)) return SPEC_ERR_INVALID_ARGUMENT;
+  if (!target_logits || !parent || !node_tokens || !temperature || !top_k || !top_p || !tokens || !path ||
+      !accept_len || !logprobs)
+    return SPEC_ERR_INVALID_ARGUMENT;
+  if ((uintptr_t)target_logits & 15) return SPEC_ERR_INVALID_ARGUMENT;
+  Params p;
+  std::memset(&p, 0, sizeof p);
+  p.target = (const uint8_t*)target_logits;
+  p.draft = (const uint8_t*)target_logits;
+  p.draft_tokens = node_tokens;
+  p.parent = parent;
+  p.path = path;
+  p.temperature = temperature;
+  p.top_k = top_k;
+  p.top_p = top_p;
+  p.B = B;
+  p.k = N - 1;  // rows 0..N-1 of a batch row are all target rows
+  p.V = V;
+  p.mode = MODE_TREE;
+  p.key0 = (uint32_t)(seed & 0xffffffffu);
+  p.key1 = (uint32_t)(seed >> 32);
+  p.offset = (uint32_t)offset;
+  p.tokens = tokens;
+  p.accept_len = accept_len;
   p.logprobs = logprobs;
   return launch(p, g, dtype, workspace, workspace_bytes, stream);
 }

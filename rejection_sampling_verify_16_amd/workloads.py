@@ -286,3 +286,95 @@ def commit_hybrid(B: int = 64, k: int = 2, layers: int = 12, heads: int = 16, dk
 
 
 COMMIT_CONFIGS = {"hybrid": commit_hybrid}
+
+
+# ---- tree verification --------------------------------------------------------------------------
+#
+# Draft trees shaped like EAGLE top-k trees: the children of a node are the m most likely tokens of a
+# noisy copy of that node's target logits (a stand-in for the draft model), in decreasing order, so
+# siblings are distinct and the first child is the draft's favourite.  Target logits per node as in the
+# chain workloads.
+
+# parents of a 9-node tree: the root has 4 children, its first child 2, its second 1, and the first
+# grandchild 1 (depth 3, 8 draft tokens)
+EAGLE_TREE_9 = (0, 0, 0, 0, 0, 1, 1, 2, 5)
+
+
+@dataclass
+class TreeWorkload:
+    name: str
+    B: int
+    N: int
+    V: int
+    dtype: str
+    target: np.ndarray        # [B, N, V] (uint16 bf16 bits or float32)
+    parent: np.ndarray        # int32 [B, N]
+    node_tokens: np.ndarray   # int32 [B, N]
+    temperature: np.ndarray
+    top_k: np.ndarray
+    top_p: np.ndarray
+    seed: int = 0
+    offset: int = 0
+
+    @property
+    def logit_bytes(self) -> int:
+        return self.target.nbytes
+
+
+def random_tree(rng: np.random.Generator, N: int, max_children: int = 4) -> np.ndarray:
+    """A random recursive tree: node i >= 1 takes a uniformly chosen earlier node with room as its parent."""
+    par = np.zeros(N, dtype=np.int32)
+    nch = np.zeros(N, dtype=np.int32)
+    for i in range(1, N):
+        room = np.flatnonzero(nch[:i] < max_children)
+        par[i] = int(rng.choice(room))
+        nch[par[i]] += 1
+    return par
+
+
+def make_tree(B: int, V: int, parents=EAGLE_TREE_9, *, N: int = 0, dtype: str = "bf16", seed: int = 3000,
+              target_sigma: float = 2.5, noise_sigma: float = 0.8, boost: float = 8.0, temperature=1.0, top_k=0,
+              top_p=1.0, mixed_params: bool = False, name: str = "tree", offset: int = 0) -> TreeWorkload:
+    """``parents`` fixes one topology for every row; ``parents=None`` draws a random tree of N nodes per row."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if parents is not None:
+        N = len(parents)
+    is_bf16 = dtype == "bf16"
+    tgt = np.empty((B, N, V), dtype=np.uint16 if is_bf16 else np.float32)
+    par = np.zeros((B, N), dtype=np.int32)
+    tok = np.zeros((B, N), dtype=np.int32)
+    for b in range(B):
+        pr = np.asarray(parents, dtype=np.int32) if parents is not None else random_tree(rng, N)
+        t = _normal(rng, (N, V), target_sigma)
+        if boost:
+            t[np.arange(N), rng.integers(0, V, size=N)] += np.float32(boost)
+        tgt[b] = bf16_rne(t) if is_bf16 else t
+        tv = bf16_to_f32(tgt[b]) if is_bf16 else tgt[b]
+        par[b] = pr
+        for u in range(N):
+            kids = [c for c in range(1, N) if pr[c] == u]
+            if kids:
+                noisy = tv[u] + _normal(rng, (V,), noise_sigma)
+                m = len(kids)
+                cand = np.argpartition(-noisy, m - 1)[:m] if m < V else np.arange(V)
+                tok[b, kids] = cand[np.argsort(-noisy[cand], kind="stable")]
+    if mixed_params:
+        T = rng.uniform(0.6, 1.2, size=B).astype(np.float32)
+        K = np.where(rng.random(B) < 0.5, 0, 50).astype(np.int32)
+        P = np.where(rng.random(B) < 0.5, 1.0, 0.95).astype(np.float32)
+    else:
+        T = np.full(B, temperature, dtype=np.float32)
+        K = np.full(B, top_k, dtype=np.int32)
+        P = np.full(B, top_p, dtype=np.float32)
+    return TreeWorkload(name, B, N, V, dtype, tgt, par, tok, T, K, P, seed=seed, offset=offset)
+
+
+def tree_eagle9() -> TreeWorkload:
+    """B=64, 9-node EAGLE-style tree (8 drafts, depth 3), V=157184, bf16, mixed T / top-k / top-p; target rows
+    N(0, 2.5^2) + 15 at one index, so the top token holds about half the mass at T = 1 (a next-token
+    distribution as peaked as a language model's, which is what makes target-only acceptance likely)."""
+    return make_tree(64, 157184, EAGLE_TREE_9, seed=3001, boost=15.0, mixed_params=True,
+                     name="tree_B64_N9_V157184_bf16_mixed")
+
+
+TREE_CONFIGS = {"eagle9": tree_eagle9}

@@ -135,3 +135,23 @@ def test_commit_slots_rejects_bad_arguments_before_launch(L):
     if torch.cuda.device_count() == 0:
         assert call() == 3
         assert call(seq=None, st=None) == 3
+
+
+def test_tree_verify_sizes_and_rejects(L):
+    """Tree workspace sizes and host-side argument checks (no device call)."""
+    assert sv.tree_workspace_size(64, 9, 157184) > 0
+    assert sv.tree_workspace_size(1, 1, 1024, sv.SPEC_DTYPE_F32) > 0
+    assert sv.tree_workspace_size(4, 64, 4096) > 0
+    assert sv.tree_workspace_size(4, 65, 4096) == 0      # more than 64 nodes
+    assert sv.tree_workspace_size(4, 0, 4096) == 0
+    assert sv.tree_workspace_size(1 << 20, 17, 1024) == 0  # B * N > 2^24
+    P = ctypes.c_void_p(16)
+    ok = (P, 0, P, P, P, P, P, 4, 9, 1024, 0, 0, P, P, P, P, P, 1 << 30, None)
+    for i, bad in [(7, 0), (8, 0), (8, 65), (9, 1001), (11, 1 << 32), (0, None), (2, None), (13, None),
+                   (0, ctypes.c_void_p(18))]:
+        args = list(ok)
+        args[i] = bad
+        assert L.spec_tree_verify(*args) == 1, (i, bad)
+    args = list(ok)
+    args[16] = None                                       # no workspace
+    assert L.spec_tree_verify(*args) == 2
