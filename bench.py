@@ -75,6 +75,8 @@ def main():
     ap.add_argument("--no-commit", action="store_true", help="skip the commit-step measurement")
     ap.add_argument("--commit-only", action="store_true", help="only the commit-step measurement")
     ap.add_argument("--commit-steps", type=int, default=100)
+    ap.add_argument("--no-tree", action="store_true", help="skip the tree-verification measurement")
+    ap.add_argument("--tree-only", action="store_true", help="only the tree-verification measurement")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, 5 times (PMC calibration)")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
@@ -106,6 +108,9 @@ def main():
         return
     if args.commit_only:
         print(json.dumps({"commit": bench_commit(args, dev)}), flush=True)
+        return
+    if args.tree_only:
+        print(json.dumps({"tree": bench_tree(args, dev)}), flush=True)
         return
     w = W.CONFIGS[args.config]()
     B, k, V = w.B, w.k, w.V
@@ -207,11 +212,83 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, drafts.cpu().numpy(), args.cpu_seconds)
+    del sets, out, ws
+    torch.cuda.empty_cache()
+    if not args.no_tree:
+        result["tree"] = bench_tree(args, dev)
     if not args.no_commit:
-        del sets, out, ws
-        torch.cuda.empty_cache()
         result["commit"] = bench_commit(args, dev)
     print(json.dumps(result), flush=True)
+
+
+def bench_tree(args, dev):
+    """Tree verification (spec_tree_verify) on an EAGLE-style 9-node tree per batch row (B=64, V=157184,
+    bf16, mixed parameters): verified rows/s, per-kernel durations from the library's event hook, and the
+    row-statistics kernel against the HBM roofline with the tree's logit bytes (every node row read once)."""
+    import torch
+    import rejection_sampling_verify_16_amd as sv
+    from rejection_sampling_verify_16_amd import workloads as W
+    w = W.tree_eagle9()
+    d = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).to(dev)
+    tgt0 = torch.from_numpy(w.target.view(np.int16)).view(torch.bfloat16).to(dev)
+    n_sets = max(2, math.ceil(ROTATE_BYTES / w.logit_bytes))
+    sets = [tgt0] + [tgt0.clone() for _ in range(n_sets - 1)]
+    par, tok = d(w.parent, np.int32), d(w.node_tokens, np.int32)
+    T, K, P = d(w.temperature, np.float32), d(w.top_k, np.int32), d(w.top_p, np.float32)
+    ws = torch.zeros(sv.tree_workspace_size(w.B, w.N, w.V, sv.SPEC_DTYPE_BF16), dtype=torch.uint8, device=dev)
+    out = None
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        nonlocal out
+        out = sv.spec_tree_verify(sets[i % n_sets], par, tok, T, K, P, seed=w.seed, offset=i, out=out, workspace=ws,
+                                  stream=stream)
+
+    n = max(50, args.steps // 2)
+    for i in range(10):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    k1_ms, kt_ms = kernel_durations(sv, step, n, stream)
+    gbps = w.logit_bytes / (k1_ms * 1e-3) / 1e9
+    acc = out["accept_len"].cpu().numpy()
+    res = {
+        "metric": "verified rows/s (draft trees)",
+        "value": w.B / (ms * 1e-3),
+        "unit": "verified rows/s",
+        "steps": n,
+        "ms_per_step": ms,
+        "dtype": "bf16",
+        "config": {"workload": w.name, "B": w.B, "N": w.N, "V": w.V, "parents": list(W.EAGLE_TREE_9),
+                   "logit_bytes_per_step": w.logit_bytes, "rotating_input_sets": n_sets},
+        "mean_accept_len": float(acc.mean()),
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None, "kernel": "k1_stats (tree rows)",
+                     "kernel_ms_mean": k1_ms, "algorithmic_bytes": w.logit_bytes},
+        "kernels": {"k1_stats": {"ms_mean": k1_ms}, "k_tree": {"ms_mean": kt_ms}},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        o = oracle.get()
+        threads = min(os.cpu_count() or 1, 16)
+        calls, t0 = 0, time.perf_counter()
+        while True:
+            o.tree_verify(w.target, w.parent, w.node_tokens, w.temperature, w.top_k, w.top_p, seed=w.seed,
+                          offset=calls, num_threads=threads)
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= min(args.cpu_seconds, 5.0) or calls >= 200:
+                break
+        res["cpu_baseline"] = {"value": w.B * calls / el, "unit": "verified rows/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"{calls} full calls of the tree workload ({w.B} rows each), {el:.1f} s"}
+    return res
 
 
 def bench_commit(args, dev):
