@@ -165,7 +165,7 @@ def main():
 
     # ---- per-kernel durations: HIP events recorded by the library around each of its kernels,
     # on the stream the kernels run on, over a second pass of the same `steps` calls ----
-    k1_ms, k5_ms = kernel_durations(sv, step, args.steps, stream)
+    k1_ms, km_ms, k5_ms = kernel_durations(sv, step, args.steps, stream)
     logit_bytes = w.logit_bytes
     draft_pos_bytes = w.B * 2 * w.k * w.V * (2 if bf16 else 4)  # rows K5 re-reads (bonus row aside)
     k1_gbps = logit_bytes / (k1_ms * 1e-3) / 1e9
@@ -204,6 +204,9 @@ def main():
         },
         "kernels": {
             "k1_stats": {"ms_mean": k1_ms, "bytes": logit_bytes, "GBps": k1_gbps},
+            # per-row merges of K1's slice partials and the kept thresholds (re-reads only rows whose
+            # threshold needs a count over the whole row)
+            "k1_rows": {"ms_mean": km_ms},
             # K5 streams the draft-position rows of batch rows it cannot finish from recorded
             # candidates; this is its traffic when every row is streamed (an upper bound)
             "k5_verify": {"ms_mean": k5_ms, "bytes_all_rows_streamed": draft_pos_bytes},
@@ -255,7 +258,7 @@ def bench_tree(args, dev):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / n
-    k1_ms, kt_ms = kernel_durations(sv, step, n, stream)
+    k1_ms, km_ms, kt_ms = kernel_durations(sv, step, n, stream)
     gbps = w.logit_bytes / (k1_ms * 1e-3) / 1e9
     acc = out["accept_len"].cpu().numpy()
     res = {
@@ -271,7 +274,7 @@ def bench_tree(args, dev):
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": gbps / HBM_PEAK_GBPS, "traffic": None, "kernel": "k1_stats (tree rows)",
                      "kernel_ms_mean": k1_ms, "algorithmic_bytes": w.logit_bytes},
-        "kernels": {"k1_stats": {"ms_mean": k1_ms}, "k_tree": {"ms_mean": kt_ms}},
+        "kernels": {"k1_stats": {"ms_mean": k1_ms}, "k1_rows": {"ms_mean": km_ms}, "k_tree": {"ms_mean": kt_ms}},
     }
     if not args.no_cpu_baseline:
         import oracle

@@ -253,8 +253,9 @@ const char* spec_verify_status_string(spec_status_t status);
 
 /*
  * Benchmark hook: per-kernel timing of later calls.  Each spec_verify / spec_sample / spec_tree_verify
- * call enqueues SPEC_NUM_KERNELS kernels: 0 = row statistics and kept thresholds (reads every logit once),
- * 1 = accept chain (or tree walk), alpha and draws (re-reads the rows it draws from).
+ * call enqueues SPEC_NUM_KERNELS kernels: 0 = per-slice row statistics (reads every logit once),
+ * 1 = per-row merges and kept thresholds, 2 = accept chain (or tree walk), alpha and draws (re-reads the
+ * rows it draws from).
  *
  *   events  NULL (turns the hook off; count ignored) or 2 * SPEC_NUM_KERNELS hipEvent_t handles,
  *           created by the caller with timing enabled and owned by the caller
@@ -265,7 +266,7 @@ const char* spec_verify_status_string(spec_status_t status);
  * that makes the calls, and turn it off (NULL) before the events are destroyed.
  * Returns SPEC_ERR_INVALID_ARGUMENT if count is wrong.
  */
-#define SPEC_NUM_KERNELS 2
+#define SPEC_NUM_KERNELS 3
 spec_status_t spec_set_kernel_events(void* const* events, int32_t count);
 
 #ifdef __cplusplus

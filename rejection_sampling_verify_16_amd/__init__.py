@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 
 SPEC_DTYPE_BF16 = 0
 SPEC_DTYPE_F32 = 1
-SPEC_NUM_KERNELS = 2  # kernels per call: 0 = row statistics / thresholds, 1 = accept chain / alpha / draws
+SPEC_NUM_KERNELS = 3  # kernels per call: 0 = slice statistics, 1 = row merges / thresholds, 2 = accept chain / draws
 STATUS = {0: "SPEC_OK", 1: "SPEC_ERR_INVALID_ARGUMENT", 2: "SPEC_ERR_WORKSPACE",
           3: "SPEC_ERR_UNSUPPORTED_DEVICE", 4: "SPEC_ERR_LAUNCH"}
 

@@ -61,7 +61,7 @@ constexpr int WF = 2048;        // widest exact code window of the whole-row pas
 constexpr int MAXS1 = 64;       // slices per bf16 row at the largest V
 constexpr int MB = 8;           // merge: slices whose histogram words are loaded in one round trip
 constexpr int HCW = NBC / 2 + 1;  // words per slice of packed bin counts + the slice's base bin
-constexpr int NKERN = 2;        // kernels per call
+constexpr int NKERN = 3;        // kernels per call
 
 constexpr int WC = 64;          // K1: candidate window (codes below the slice max) of truncated rows
 constexpr int NC = 192;         // K1: candidates recorded per slice at most
@@ -123,7 +123,6 @@ struct Params {
   float* logprobs;
   float* alpha;
   float* raw_logprobs;  // NULL, or [B][k+1] raw logprobs of the committed tokens
-  uint32_t* cnt1;     // [R] K1 arrivals
   uint32_t* cnt5;     // [B] K5 arrivals
   StatPart* st1;      // [R][S1]
   uint32_t* hw1;      // [R][S1][WTOP/2] packed 16-bit code counts
@@ -954,7 +953,6 @@ __device__ __forceinline__ void k1_merge(const Params& p, K1Smem& sm, int r, int
     ri->state = bad ? ST_BAD : (sparse ? ST_SPARSE : 0u);
     ri->rlz = rlz;
     ri->gath = sg >= 0 ? __uint_as_float(sm.win[1]) : 0.0f;
-    atomicExch(&p.cnt1[r], 0u);
   }
 }
 
@@ -1351,11 +1349,6 @@ __device__ __forceinline__ void k1_item(const Params& p, K1Smem& sm, int item, i
     if (BF && q.cand) st32(&p.ncand1[(size_t)r * p.S1 + s], sm.u.st.over ? (uint32_t)NC + 1u : sm.u.st.ncand);
   }
   SV_TRACE_AT(p, item, 2);
-  if (arrive_last(&p.cnt1[r], (uint32_t)p.S1, &sm.rs.flag)) {
-    SV_TRACE_AT(p, item, 3);
-    k1_merge<E, RAW>(p, sm, r, b, i, q);
-    SV_TRACE_AT(p, item, 7);
-  }
 }
 
 template <class E, int VPT, bool RAW>
@@ -1364,6 +1357,21 @@ __global__ __launch_bounds__(NT, OCC1) void k1_stats(Params p) {
   int r, s;
   item_rs(blockIdx.x, p.R, p.S1, r, s);
   k1_item<E, VPT, RAW>(p, sm, blockIdx.x, r, s);
+}
+
+// Row merges: one workgroup per logit row, launched after every slice has written its partials.  Kept
+// apart from the slices so that long merges (top-p rows that count a code window over the whole row)
+// neither hold slice slots nor pile up on one XCD: workgroups are handed to the XCDs in order, so one
+// XCD full of long merges stalls the hand-out to all of them.
+template <class E, bool RAW>
+__global__ __launch_bounds__(NT) void k1_rows(Params p) {
+  __shared__ K1Smem sm;
+  const int r = blockIdx.x;
+  const int b = r / p.rows, i = r - b * p.rows;
+  const RowParams q = row_params(p, b);
+  SV_TRACE_AT(p, (size_t)r * p.S1, 3);
+  k1_merge<E, RAW>(p, sm, r, b, i, q);
+  SV_TRACE_AT(p, (size_t)r * p.S1, 7);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -2222,7 +2230,7 @@ __global__ __launch_bounds__(NT) void k_tree(Params p) {
 // ---------------------------------------------------------------------------------------------
 struct Geo {
   int rows, R, S1, S5, L1, L5, esize, EPV;
-  size_t off_cnt1, off_cnt5, off_st1, off_hw1, off_hc1, off_cand1, off_ncand1, off_rinfo, off_fin5, off_trace, off_trace5,
+  size_t off_cnt5, off_st1, off_hw1, off_hc1, off_cand1, off_ncand1, off_rinfo, off_fin5, off_trace, off_trace5,
       total;
 };
 
@@ -2252,7 +2260,6 @@ static bool make_geo(int32_t B, int32_t k, int32_t V, spec_dtype_t dtype, Geo& g
     o = off;
     off = align_up(off + bytes, 256);
   };
-  take(g.off_cnt1, R * 4);
   take(g.off_cnt5, (size_t)B * 4);
   take(g.off_st1, R * g.S1 * sizeof(StatPart));
   const bool bf = dtype == SPEC_DTYPE_BF16;  // per-code and weight-bin partials: bf16 rows only
@@ -2297,26 +2304,28 @@ template <class E>
 static void enqueue(const Params& p, int cus, hipStream_t st) {
   static_assert(WTOP / 2 == NT && NBC == NT, "K1 assumes one histogram word pair per thread");
   (void)cus;
+  const dim3 g1((unsigned)(p.R * p.S1)), gr((unsigned)p.R), g5((unsigned)(p.B * p.S5));
+  const bool raw = p.raw_logprobs != nullptr;
   prof_mark(0, st);
-  if (p.mode == MODE_TREE) {
-    hipLaunchKernelGGL((k1_stats<E, VPT1, false>), dim3((unsigned)(p.R * p.S1)), dim3(NT), 0, st, p);
-    prof_mark(1, st);
-    prof_mark(2, st);
-    hipLaunchKernelGGL((k_tree<E, VPT5>), dim3((unsigned)(p.B * p.S5)), dim3(NT), 0, st, p);
-    prof_mark(3, st);
-    return;
-  }
-  if (p.raw_logprobs)
-    hipLaunchKernelGGL((k1_stats<E, VPT1, true>), dim3((unsigned)(p.R * p.S1)), dim3(NT), 0, st, p);
+  if (raw)
+    hipLaunchKernelGGL((k1_stats<E, VPT1, true>), g1, dim3(NT), 0, st, p);
   else
-    hipLaunchKernelGGL((k1_stats<E, VPT1, false>), dim3((unsigned)(p.R * p.S1)), dim3(NT), 0, st, p);
+    hipLaunchKernelGGL((k1_stats<E, VPT1, false>), g1, dim3(NT), 0, st, p);
   prof_mark(1, st);
   prof_mark(2, st);
-  if (p.raw_logprobs)
-    hipLaunchKernelGGL((k5_verify<E, VPT5, true>), dim3((unsigned)(p.B * p.S5)), dim3(NT), 0, st, p);
+  if (raw)
+    hipLaunchKernelGGL((k1_rows<E, true>), gr, dim3(NT), 0, st, p);
   else
-    hipLaunchKernelGGL((k5_verify<E, VPT5, false>), dim3((unsigned)(p.B * p.S5)), dim3(NT), 0, st, p);
+    hipLaunchKernelGGL((k1_rows<E, false>), gr, dim3(NT), 0, st, p);
   prof_mark(3, st);
+  prof_mark(4, st);
+  if (p.mode == MODE_TREE)
+    hipLaunchKernelGGL((k_tree<E, VPT5>), g5, dim3(NT), 0, st, p);
+  else if (raw)
+    hipLaunchKernelGGL((k5_verify<E, VPT5, true>), g5, dim3(NT), 0, st, p);
+  else
+    hipLaunchKernelGGL((k5_verify<E, VPT5, false>), g5, dim3(NT), 0, st, p);
+  prof_mark(5, st);
 }
 
 static spec_status_t launch(Params& p, const Geo& g, spec_dtype_t dtype, void* workspace, size_t workspace_bytes,
@@ -2331,7 +2340,6 @@ static spec_status_t launch(Params& p, const Geo& g, spec_dtype_t dtype, void* w
   p.L1 = g.L1;
   p.L5 = g.L5;
   uint8_t* ws = (uint8_t*)workspace;
-  p.cnt1 = (uint32_t*)(ws + g.off_cnt1);
   p.cnt5 = (uint32_t*)(ws + g.off_cnt5);
   p.st1 = (StatPart*)(ws + g.off_st1);
   p.hw1 = (uint32_t*)(ws + g.off_hw1);
