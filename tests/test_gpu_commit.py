@@ -175,3 +175,51 @@ def test_commit_slots_parity(o, B, k):
         np.testing.assert_array_equal(d["ss"].cpu().numpy(), ss)
         np.testing.assert_array_equal(d["ps"].cpu().numpy(), ps)
         np.testing.assert_array_equal(d["seq"].cpu().numpy(), seq)
+
+
+def test_commit_graph_replay(o):
+    """A captured HIP graph of a gather commit followed by a slot commit replays exactly: each replay, from the
+    same starting caches, slots and lengths, matches the oracle."""
+    import torch
+    import rejection_sampling_verify_16_amd as sv
+    w = _case("graph", 24, 2, 40, [("rec", 3, (40, 128), np.float32), ("conv", 3, (3, 96), np.uint16)], 31,
+              sentinels=2, bad_slots=1)
+    host = [(_bytes4(t.verify_state), _bytes3(t.state_cache).copy()) for t in w.tensors]
+    init = [c.copy() for _, c in host]
+    seq_h, st_h = w.seq_len.copy(), None
+    st_h = o.commit(host, w.state_slot, w.accept_len, seq_h)
+    rng = np.random.default_rng(32)
+    P = w.B * (w.k + 2)
+    perm = rng.permutation(P).astype(np.int32)
+    ss0, ps0 = perm[:w.B].copy(), perm[w.B:].reshape(w.B, w.k + 1).copy()
+    ss_h, ps_h, seq2_h = ss0.copy(), ps0.copy(), seq_h.copy()
+    st2_h = o.commit_slots(ss_h, ps_h, w.accept_len, P, seq2_h)
+    dev = [(_to_dev(v), _to_dev(c)) for v, c in host]
+    slot = torch.from_numpy(w.state_slot).to("cuda:0")
+    acc = torch.from_numpy(w.accept_len).to("cuda:0")
+    seq = torch.from_numpy(w.seq_len.copy()).to("cuda:0")
+    ss, ps = torch.from_numpy(ss0).to("cuda:0"), torch.from_numpy(ps0).to("cuda:0")
+    st1 = torch.empty(w.B, dtype=torch.int32, device="cuda:0")
+    st2 = torch.empty(w.B, dtype=torch.int32, device="cuda:0")
+    sv.spec_commit(dev, slot, acc, seq_len=seq, status=st1)   # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sv.spec_commit(dev, slot, acc, seq_len=seq, status=st1)
+        sv.spec_commit_slots(ss, ps, acc, P, seq_len=seq, status=st2)
+    for rep in range(3):
+        for (_, c_d), c0 in zip(dev, init):   # reset the state from the host between replays
+            c_d.copy_(torch.from_numpy(c0))
+        seq.copy_(torch.from_numpy(w.seq_len))
+        ss.copy_(torch.from_numpy(ss0))
+        ps.copy_(torch.from_numpy(ps0))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for (_, c_h), (_, c_d) in zip(host, dev):
+            np.testing.assert_array_equal(c_d.cpu().numpy(), c_h, err_msg=f"replay {rep}")
+        np.testing.assert_array_equal(st1.cpu().numpy(), st_h)
+        np.testing.assert_array_equal(st2.cpu().numpy(), st2_h)
+        np.testing.assert_array_equal(ss.cpu().numpy(), ss_h)
+        np.testing.assert_array_equal(ps.cpu().numpy(), ps_h)
+        np.testing.assert_array_equal(seq.cpu().numpy(), seq2_h)

@@ -158,3 +158,33 @@ def test_tree_chain_equals_chain_verify():
             n = c["accept_len"][b] - 1
             assert list(t["path"][b]) == list(range(1, n + 1)) + [-1] * (k + 1 - n)
         assert len(set(c["accept_len"].tolist())) > 1
+
+
+def test_tree_determinism_and_graph_replay():
+    """Repeated calls give identical outputs; a captured HIP graph of the call replays them exactly, with
+    unrelated eager calls between replays."""
+    import torch
+    import rejection_sampling_verify_16_amd as sv
+    w = W.make_tree(32, 65536, W.EAGLE_TREE_9, seed=3030, boost=12.0, mixed_params=True, name="graph")
+    d = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).to("cuda:0")
+    args = (_dev_logits(w.target), d(w.parent, np.int32), d(w.node_tokens, np.int32), d(w.temperature, np.float32),
+            d(w.top_k, np.int32), d(w.top_p, np.float32))
+    eager = {k_: v.cpu().numpy() for k_, v in sv.spec_tree_verify(*args, seed=4, offset=7).items()}
+    again = {k_: v.cpu().numpy() for k_, v in sv.spec_tree_verify(*args, seed=4, offset=7).items()}
+    for key in eager:
+        np.testing.assert_array_equal(eager[key], again[key])
+    gws = torch.zeros(sv.tree_workspace_size(w.B, w.N, w.V), dtype=torch.uint8, device="cuda:0")
+    gout = sv.spec_tree_verify(*args, seed=4, offset=7, workspace=gws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sv.spec_tree_verify(*args, seed=4, offset=7, out=gout, workspace=gws)
+    for rep in range(3):
+        for key in gout:
+            gout[key].fill_(7)
+        graph.replay()
+        torch.cuda.synchronize()
+        for key in eager:
+            np.testing.assert_array_equal(gout[key].cpu().numpy(), eager[key], err_msg=f"replay {rep} {key}")
+        sv.spec_tree_verify(*args, seed=5, offset=1)   # unrelated eager work between replays
+        torch.cuda.synchronize()
