@@ -82,7 +82,13 @@ def main():
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="summarise rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of this benchmark and of the copy "
                          "probe into profiles/traffic_config<C>.json (no GPU needed)")
+    ap.add_argument("--pmc-report", nargs="+", metavar="DIR",
+                    help="print the mean of every counter per kernel (per dispatch) over rocprofv3 --pmc CSV runs "
+                         "(no GPU needed)")
     args = ap.parse_args()
+    if args.pmc_report:
+        pmc_report(args.pmc_report)
+        return
     if args.pmc_summary:
         pmc_summary(args)
         return
@@ -404,6 +410,29 @@ def _pmc_per_kernel(run_dir, counter):
         name = r.get("Kernel_Name", "").split("(")[0]
         vals.setdefault(name, []).append(float(r["Counter_Value"]))
     return {k: (float(np.mean(v)), len(v)) for k, v in vals.items()}
+
+
+def pmc_report(dirs):
+    """Markdown table: kernel x counter, mean value per dispatch, over the library's kernels."""
+    import csv
+    import glob
+    vals = {}
+    for d in dirs:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        for r in csv.DictReader(open(files[0])):
+            name = r.get("Kernel_Name", "").split("(")[0]
+            if "sv::" not in name:
+                continue
+            vals.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    counters = sorted({c for k in vals.values() for c in k})
+    print("| kernel | dispatches | " + " | ".join(counters) + " |")
+    print("|---|---|" + "---|" * len(counters))
+    for name in sorted(vals):
+        n = max(len(v) for v in vals[name].values())
+        cells = [f"{np.mean(vals[name][c]):.4g}" if c in vals[name] else "" for c in counters]
+        print(f"| {name} | {n} | " + " | ".join(cells) + " |")
 
 
 def pmc_summary(args):
