@@ -488,9 +488,10 @@ __device__ inline unsigned long long code_mass(uint32_t cnt, uint32_t code, floa
   return cnt ? (unsigned long long)cnt * fixmass(fexp2((key16_value(code) - m) * c)) : 0ull;
 }
 
+// Entry i is code ktop - i, or codes[i] when a list of (descending) codes is given.
 __device__ __forceinline__ bool select_run(const uint32_t* cnt, int n, uint32_t ktop, float m, float c, SelState& ss, RedSmem& rs,
                            uint32_t base_cnt, unsigned long long base_mass, double ztot_fixed, bool useK, int K,
-                           bool useP, float P, int& sel, unsigned long long& zsel) {
+                           bool useP, float P, int& sel, unsigned long long& zsel, const uint32_t* codes = nullptr) {
   const int tid = threadIdx.x;
   if (tid == 0) {
     ss.sel_k = -1;
@@ -506,7 +507,8 @@ __device__ __forceinline__ bool select_run(const uint32_t* cnt, int n, uint32_t 
     for (int c0 = 0; c0 < n; c0 += 2 * NT) {
       const int i0 = c0 + 2 * tid, i1 = i0 + 1;
       const uint32_t a0 = i0 < n ? cnt[i0] : 0u, a1 = i1 < n ? cnt[i1] : 0u;
-      const unsigned long long b0 = code_mass(a0, ktop - i0, m, c), b1 = code_mass(a1, ktop - i1, m, c);
+      const uint32_t k0 = codes ? (i0 < n ? codes[i0] : 0u) : ktop - i0, k1 = codes ? (i1 < n ? codes[i1] : 0u) : ktop - i1;
+      const unsigned long long b0 = code_mass(a0, k0, m, c), b1 = code_mass(a1, k1, m, c);
       const uint32_t ic = block_inclusive_scan<uint32_t>(a0 + a1, rs.scan32) + ccarry;
       const unsigned long long im = block_inclusive_scan<unsigned long long>(b0 + b1, rs.scan64) + mcarry;
       const uint32_t e0 = ic - a0 - a1;
@@ -544,7 +546,9 @@ __device__ __forceinline__ bool select_run(const uint32_t* cnt, int n, uint32_t 
     for (int c0 = 0; c0 <= last; c0 += 2 * NT) {
       const int i0 = c0 + 2 * tid, i1 = i0 + 1;
       const uint32_t a0 = i0 <= last ? cnt[i0] : 0u, a1 = i1 <= last ? cnt[i1] : 0u;
-      const unsigned long long b0 = code_mass(a0, ktop - i0, m, c), b1 = code_mass(a1, ktop - i1, m, c);
+      const uint32_t k0 = codes ? (i0 <= last ? codes[i0] : 0u) : ktop - i0;
+      const uint32_t k1 = codes ? (i1 <= last ? codes[i1] : 0u) : ktop - i1;
+      const unsigned long long b0 = code_mass(a0, k0, m, c), b1 = code_mass(a1, k1, m, c);
       const unsigned long long im = block_inclusive_scan<unsigned long long>(b0 + b1, rs.scan64) + mcarry;
       const unsigned long long f0 = im - b0 - b1;
       if (i0 <= last && (double)f0 < target && (double)(f0 + b0) >= target) {
@@ -675,7 +679,7 @@ __device__ __forceinline__ bool coarse_window(K1Smem& sm, float m, float c, floa
   const uint32_t kh = key32(vhi) >> 16, kl = key32(vlo) >> 16;  // within one code of key16 of those values
   khi = min(kh + 2u, keym);
   klo = kl > 2u ? kl - 2u : 0u;
-  return khi >= klo && khi - klo + 1u <= (uint32_t)WF;
+  return khi >= klo;
 }
 
 // Exact per-code counts of [klo, khi] over the whole row by this workgroup (entry i counts code khi - i),
@@ -731,6 +735,101 @@ __device__ __forceinline__ bool window_pass(K1Smem& sm, const uint8_t* row, int 
   if (!select_run(h, width, khi, m, c, sm.ss, sm.rs, above_c, above_m, ztot_fixed, useK, K, useP, P, sel, zsel))
     return false;
   thr = khi - (uint32_t)sel;
+  Z = (float)((double)zsel * 0x1p-40);
+  return true;
+}
+
+// The same search for a window too wide to count per code: a window that straddles logit 0 is narrow in
+// value but spans thousands of order-preserving codes (they are logarithmic in magnitude), while holding few
+// entries.  Those entries (up to LCAP) are listed in LDS; their distinct codes, ranked in descending order,
+// with their counts form the histogram the search runs on.  Codes without entries add no count and no mass,
+// so the result equals counting every code.  More than LCAP entries: false (the caller takes the radix select).
+constexpr int LCAP = 512;
+__device__ __forceinline__ bool window_list_pass(K1Smem& sm, const uint8_t* row, int V, float m, float c, uint32_t klo,
+                                 uint32_t khi, bool useK, int K, bool useP, float P, double ztot_fixed, uint32_t& thr,
+                                 float& Z) {
+  static_assert(4 * LCAP <= WF, "list, codes, counts and first-occurrence counts share the count array");
+  const int tid = threadIdx.x;
+  uint32_t* list = sm.u.mg.cnt;              // entry keys, in arrival order
+  uint32_t* ucode = sm.u.mg.cnt + LCAP;      // distinct keys, descending
+  uint32_t* ucnt = sm.u.mg.cnt + 2 * LCAP;   // their counts
+  uint32_t* fcnt = sm.u.mg.cnt + 3 * LCAP;   // per entry: its key's count at the key's first occurrence, else 0
+  if (tid == 0) sm.win[3] = 0;
+  __syncthreads();
+  const uint4* src = (const uint4*)row;
+  const int nvec = V / BF16::EPV;
+  uint32_t acnt = 0;
+  unsigned long long amass = 0;
+  for (int j0 = 0; j0 < nvec; j0 += NT * FVPT) {
+    uint4 v[FVPT];
+#pragma unroll
+    for (int u = 0; u < FVPT; ++u) {
+      const int j = j0 + tid + u * NT;
+      if (j < nvec) v[u] = src[j];
+    }
+#pragma unroll
+    for (int u = 0; u < FVPT; ++u) {
+      const int j = j0 + tid + u * NT;
+      if (j < nvec) {
+#pragma unroll
+        for (int e = 0; e < BF16::EPV; ++e) {
+          const float f = BF16::get(v[u], e);
+          const uint32_t key = key16f(f);
+          if (key > khi) {
+            ++acnt;
+            amass += fixmass(fexp2((f - m) * c));
+          } else if (key >= klo) {
+            const uint32_t at = atomicAdd(&sm.win[3], 1u);
+            if (at < (uint32_t)LCAP) list[at] = key;
+          }
+        }
+      }
+    }
+  }
+  const uint32_t tc = block_inclusive_scan<uint32_t>(acnt, sm.rs.scan32);
+  const unsigned long long tm = block_inclusive_scan<unsigned long long>(amass, sm.rs.scan64);
+  if (tid == NT - 1) {
+    sm.win[0] = tc;
+    sm.rs.scan64[0] = tm;
+  }
+  __syncthreads();
+  const uint32_t above_c = sm.win[0];
+  const unsigned long long above_m = sm.rs.scan64[0];
+  const uint32_t nl = sm.win[3];
+  __syncthreads();
+  if (nl > (uint32_t)LCAP) return false;
+  // first occurrences of each key with the key's count; then each one's rank among the distinct keys
+  for (int e = tid; e < (int)nl; e += NT) {
+    const uint32_t k = list[e];
+    uint32_t count = 0;
+    bool first = true;
+    for (int o = 0; o < (int)nl; ++o) {
+      count += list[o] == k ? 1u : 0u;
+      first = first && !(list[o] == k && o < e);
+    }
+    fcnt[e] = first ? count : 0u;
+  }
+  __syncthreads();
+  uint32_t nd = 0;
+  for (int e = tid; e < (int)nl; e += NT) {
+    if (fcnt[e] == 0u) continue;
+    const uint32_t k = list[e];
+    uint32_t rank = 0;
+    for (int o = 0; o < (int)nl; ++o) rank += (fcnt[o] != 0u && list[o] > k) ? 1u : 0u;
+    ucode[rank] = k;
+    ucnt[rank] = fcnt[e];
+    ++nd;
+  }
+  const uint32_t ndist = block_inclusive_scan<uint32_t>(nd, sm.rs.scan32);
+  if (tid == NT - 1) sm.win[2] = ndist;
+  __syncthreads();
+  const int n = (int)sm.win[2];
+  __syncthreads();
+  int sel = -1;
+  unsigned long long zsel = 0;
+  if (!select_run(ucnt, n, khi, m, c, sm.ss, sm.rs, above_c, above_m, ztot_fixed, useK, K, useP, P, sel, zsel, ucode))
+    return false;
+  thr = ucode[sel];
   Z = (float)((double)zsel * 0x1p-40);
   return true;
 }
@@ -933,9 +1032,14 @@ __device__ __forceinline__ void k1_merge(const Params& p, K1Smem& sm, int r, int
         }
         __syncthreads();
         uint32_t klo = 0, khi = 0;
-        if (coarse_window(sm, m, q.c, q.P, sum, p.V, keym, klo, khi))
-          done = window_pass(sm, row_ptr(p, b, i, esize), p.V, m, q.c, klo, khi, q.useK, q.K, q.useP, q.P, ztot,
-                             thr, Z);
+        if (coarse_window(sm, m, q.c, q.P, sum, p.V, keym, klo, khi)) {
+          if (khi - klo + 1u <= (uint32_t)WF)
+            done = window_pass(sm, row_ptr(p, b, i, esize), p.V, m, q.c, klo, khi, q.useK, q.K, q.useP, q.P, ztot,
+                               thr, Z);
+          else
+            done = window_list_pass(sm, row_ptr(p, b, i, esize), p.V, m, q.c, klo, khi, q.useK, q.K, q.useP, q.P,
+                                    ztot, thr, Z);
+        }
       }
     }
     if (!done) {
