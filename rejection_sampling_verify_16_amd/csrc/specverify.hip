@@ -6,32 +6,34 @@
 // rejection sampling, unchanged logprobs), its accept-probability table (alpha = sum min(p, q)), and
 // its per-step optimisation table (Gumbel-max draws, no host synchronisation).
 //
-// One call enqueues two kernels on the caller's stream; no workgroup ever waits for another.
-// A merge across workgroups is done by the last one to arrive at a per-row counter (agent-scope
-// atomics; partials travel through agent-scope atomic stores and loads, coherent across the XCDs' L2s
-// without cache-wide write-back or invalidation).  Workgroup ids map to (row, slice) so that all
-// slices of one row run on one XCD and consecutive rows' merges run on different XCDs.
+// One call enqueues three kernels on the caller's stream; no workgroup ever waits for another.  Where
+// workgroups of one kernel combine partials (K5, the tree kernel), the last one to arrive at a per-row
+// counter does it (agent-scope atomics; partials travel through agent-scope atomic stores and loads,
+// coherent across the XCDs' L2s without cache-wide write-back or invalidation).
 //
-//   K1 stats   items (logit row, slice).  Streams every logit once with 16-byte loads and keeps only
-//              what the row needs: NaN-propagating max (lowest argmax for greedy rows); the sum of
-//              exp2((l - max) * log2(e) / T) for rows whose normaliser is the whole row; for bf16 rows
-//              with top-k / top-p, exact per-code counts of the 512 order-preserving codes below the
-//              slice max (keys of two logits at a time, packed 16-bit operations), and for top-p-only
-//              rows also counts in 1/8-log2-unit weight bins.  The last slice of a row merges (one round
-//              trip for all its partials): row max / argmax / normaliser and, for truncated rows, the
-//              kept threshold.  Among the row's top 512 codes the threshold is exact (merged per-code
-//              counts, masses = count x 2^40 fixed-point weight, integer sums).  Otherwise the weight
-//              bins bound the cumulative mass, which gives a code window that must hold the threshold;
-//              the merging workgroup counts that window exactly over the whole row.  Anything this
-//              cannot settle (fp32 keys, a window too wide, a failed self-check) takes an exact MSD
-//              radix select.
+//   K1 stats   items (logit row, slice), all slices of a row on one XCD.  Streams every logit once with
+//              16-byte loads and keeps only what the row needs: NaN-propagating max (lowest argmax for
+//              greedy rows); the sum of exp2((l - max) * log2(e) / T) for rows whose normaliser is the
+//              whole row; for bf16 rows with top-k <= 64, a record of the slice's candidate logits; for
+//              other truncated bf16 rows, exact per-code counts of the 512 order-preserving codes below
+//              the slice max (keys of two logits at a time, packed 16-bit operations) and, for top-p-only
+//              rows, counts in 1/8-log2-unit weight bins.
+//   K1 rows    one workgroup per logit row, after every slice is done: row max / argmax / normaliser and,
+//              for truncated rows, the kept threshold (one round trip for all partials).  From recorded
+//              candidates or among the row's top 512 codes the threshold is exact (merged per-code counts,
+//              masses = count x 2^40 fixed-point weight, integer sums).  Otherwise the weight bins bound
+//              the cumulative mass, which gives a code window that must hold the threshold; the workgroup
+//              counts that window exactly over the whole row (or lists its entries when the window
+//              straddles logit 0).  Anything this cannot settle (fp32 keys, a failed self-check) takes an
+//              exact MSD radix select.
 //   K5 verify  items (batch row, slice).  Each evaluates the accept chain (p_i(x_i), q_i(x_i) from the
 //              row statistics and two gathered logits, Philox accept uniforms), then re-reads its slice
-//              of the draft-position rows (the next position's loads in flight while one is computed):
-//              alpha partial sums for every position and the Gumbel-max race candidate at the first
-//              rejected position (residual max(p - q, 0)) or at position k (bonus from p_k).  Logits
-//              below a row's kept threshold are skipped a wave at a time.  The last slice of a batch row
-//              writes the outputs.
+//              of the draft-position rows, one position at a time: alpha partial sums for every position
+//              and the Gumbel-max race candidate at the first rejected position (residual max(p - q, 0))
+//              or at position k (bonus from p_k).  Logits below a row's kept threshold are skipped a wave
+//              at a time.  Batch rows whose kept sets K1 recorded whole are finished from the records.
+//              The last slice of a batch row writes the outputs.
+//   k_tree     tree verification in place of K5 (see its comment).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -834,7 +836,7 @@ __device__ __forceinline__ bool window_list_pass(K1Smem& sm, const uint8_t* row,
   return true;
 }
 
-// Merge of one row by the last of its slices to arrive.  The slice statistics and, for histogram rows,
+// Merge of one row (the row-merge kernel, after all its slices are done).  The slice statistics and, for histogram rows,
 // thread t's word of each slice's packed code counts are all loaded before any is used, so they cost
 // one round trip for up to MB slices; the weight-bin counts are loaded only when the top codes do not
 // hold the threshold.
