@@ -36,10 +36,16 @@ COMMIT_SRC = [os.path.join(_CSRC, "commit.hip")]
 
 
 def kernel_digest(files=None) -> str:
+    """Digest of the kernel sources' code (comments and whitespace removed), so that a traffic figure stays
+    attached to the code it was measured on."""
+    import re
     h = hashlib.sha256()
     for f in files or KERNEL_SRC:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
