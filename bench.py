@@ -83,6 +83,9 @@ def main():
     ap.add_argument("--commit-steps", type=int, default=100)
     ap.add_argument("--no-tree", action="store_true", help="skip the tree-verification measurement")
     ap.add_argument("--tree-only", action="store_true", help="only the tree-verification measurement")
+    ap.add_argument("--configs", default="1,2,4a,4b,5",
+                    help="other workloads timed after the headline one (comma list; empty: none)")
+    ap.add_argument("--configs-only", action="store_true", help="only the other workloads")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, 5 times (PMC calibration)")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
@@ -124,27 +127,13 @@ def main():
     if args.tree_only:
         print(json.dumps({"tree": bench_tree(args, dev)}), flush=True)
         return
+    if args.configs_only:
+        print(json.dumps({"configs": bench_configs(args, dev)}), flush=True)
+        return
     w = W.CONFIGS[args.config]()
     B, k, V = w.B, w.k, w.V
     bf16 = w.dtype == "bf16"
-
-    def to_dev(a):
-        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if bf16 else torch.from_numpy(a)
-        return t.to(dev)
-
-    tgt0, drf0 = to_dev(w.target), to_dev(w.draft)
-    T = torch.from_numpy(w.temperature).to(dev)
-    K = torch.from_numpy(w.top_k).to(dev)
-    P = torch.from_numpy(w.top_p).to(dev)
-
-    # drafts sampled from the processed q by the library's plain sampler
-    rows, Tr, Kr, Pr, rb, rp = w.draft_sampling_inputs()
-    tt = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).to(dev)
-    dtok, _ = sv.spec_sample(drf0.reshape(B * k, V), tt(Tr, np.float32), tt(Kr, np.int32), tt(Pr, np.float32),
-                             tt(rb, np.int32), tt(rp, np.int32), seed=w.draft_seed, offset=w.draft_offset)
-    drafts = dtok.reshape(B, k).contiguous()
-    for b, i, t in w.draft_overrides:
-        drafts[b, i] = t
+    tgt0, drf0, drafts, T, K, P = verify_inputs(w, dev)
 
     n_sets = max(2, math.ceil(ROTATE_BYTES / w.logit_bytes))
     sets = [(tgt0, drf0)] + [(tgt0.clone(), drf0.clone()) for _ in range(n_sets - 1)]
@@ -229,11 +218,86 @@ def main():
         result["cpu_baseline"] = cpu_baseline(w, drafts.cpu().numpy(), args.cpu_seconds)
     del sets, out, ws
     torch.cuda.empty_cache()
+    if args.configs:
+        result["configs"] = bench_configs(args, dev)
     if not args.no_tree:
         result["tree"] = bench_tree(args, dev)
     if not args.no_commit:
         result["commit"] = bench_commit(args, dev)
     print(json.dumps(result), flush=True)
+
+
+def verify_inputs(w, dev):
+    """Device inputs of a verify workload: logits, parameters and the drafts drawn from q by the library's
+    plain sampler (plus the workload's overrides)."""
+    import torch
+    import rejection_sampling_verify_16_amd as sv
+    bf16 = w.dtype == "bf16"
+
+    def to_dev(a):
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if bf16 else torch.from_numpy(a)
+        return t.to(dev)
+
+    tt = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).to(dev)
+    tgt, drf = to_dev(w.target), to_dev(w.draft)
+    rows, Tr, Kr, Pr, rb, rp = w.draft_sampling_inputs()
+    dtok, _ = sv.spec_sample(drf.reshape(w.B * w.k, w.V), tt(Tr, np.float32), tt(Kr, np.int32), tt(Pr, np.float32),
+                             tt(rb, np.int32), tt(rp, np.int32), seed=w.draft_seed, offset=w.draft_offset)
+    drafts = dtok.reshape(w.B, w.k).contiguous()
+    for b, i, t in w.draft_overrides:
+        drafts[b, i] = t
+    return tgt, drf, drafts, tt(w.temperature, np.float32), tt(w.top_k, np.int32), tt(w.top_p, np.float32)
+
+
+def bench_configs(args, dev):
+    """The other named workloads, one after another: per-call time over back-to-back calls on rotating input
+    sets (inputs resident in HBM), verified rows/s, logit GB/s against the HBM peak, and each kernel's mean
+    duration from the library's event hook.  Config 5 runs its 100 offsets (0..99) on the same inputs."""
+    import torch
+    import rejection_sampling_verify_16_amd as sv
+    from rejection_sampling_verify_16_amd import workloads as W
+    res = {}
+    stream = torch.cuda.current_stream(dev)
+    for name in [c for c in args.configs.split(",") if c]:
+        w = W.CONFIGS[name]()
+        tgt0, drf0, drafts, T, K, P = verify_inputs(w, dev)
+        n_sets = max(2, math.ceil(ROTATE_BYTES / w.logit_bytes))
+        sets = [(tgt0, drf0)] + [(tgt0.clone(), drf0.clone()) for _ in range(n_sets - 1)]
+        out = sv.alloc_outputs(w.B, w.k, dev)
+        ws = sv.make_workspace(w.B, w.k, w.V, sv.SPEC_DTYPE_BF16 if w.dtype == "bf16" else sv.SPEC_DTYPE_F32, dev)
+        offs = w.offsets
+        n = len(offs) if len(offs) > 1 else 200
+
+        def step(i):
+            t_, d_ = sets[i % n_sets]
+            sv.spec_verify(t_, d_, drafts, T, K, P, seed=w.seed, offset=offs[i % len(offs)], out=out, workspace=ws,
+                           stream=stream)
+
+        for i in range(10):
+            step(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        k1_ms, km_ms, k5_ms = kernel_durations(sv, step, n, stream)
+        acc = out["accept_len"].float().mean().item()
+        gbps = w.logit_bytes / (ms * 1e-3) / 1e9
+        k1_gbps = w.logit_bytes / (k1_ms * 1e-3) / 1e9
+        res[name] = {
+            "workload": w.name, "B": w.B, "k": w.k, "V": w.V, "dtype": w.dtype, "calls": n,
+            "us_per_call": ms * 1e3, "verified_rows_per_s": w.B / (ms * 1e-3), "logit_bytes_per_call": w.logit_bytes,
+            "logits_GBps": gbps, "pct_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS,
+            "kernels_us": {"k1_stats": k1_ms * 1e3, "k1_rows": km_ms * 1e3, "k5_verify": k5_ms * 1e3},
+            "k1_stats_roofline_frac": k1_gbps / HBM_PEAK_GBPS, "mean_accept_len": acc,
+        }
+        print(f"[bench] config {name}: {ms * 1e3:.1f} us/call", file=sys.stderr, flush=True)
+        del sets, out, ws, tgt0, drf0
+        torch.cuda.empty_cache()
+    return res
 
 
 def bench_tree(args, dev):

@@ -1115,6 +1115,7 @@ __device__ __forceinline__ void k1_hist(K1Smem& sm, const uint4 (&v)[VPT], int n
   const uint32_t spare2 = (WTOP + lane) * 0x10001u;
   const uint32_t spare_c = NBC + lane;
   const float cb = c * BRC;
+  const float nmc = -ms * c;
   uint32_t cmask = 0;  // bit u: vector u holds a candidate (an entry within WC codes of the slice max)
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
@@ -1130,8 +1131,8 @@ __device__ __forceinline__ void k1_hist(K1Smem& sm, const uint4 (&v)[VPT], int n
         dmin = min16x2(dmin, d2);
         if (TOPP_ONLY) {
           const float f0 = __uint_as_float(wv[q] << 16), f1 = __uint_as_float(wv[q] & 0xffff0000u);
-          sum += fexp2((f0 - ms) * c);
-          sum += fexp2((f1 - ms) * c);
+          sum += fexp2(fmaf(f0, c, nmc));
+          sum += fexp2(fmaf(f1, c, nmc));
           const uint32_t j0 = min(__float2uint_rz(fmaf(f0, -cb, -cbase)), spare_c);
           const uint32_t j1 = min(__float2uint_rz(fmaf(f1, -cb, -cbase)), spare_c);
           atomicAdd(&sm.u.st.hc[j0], 1u);
@@ -1367,12 +1368,13 @@ __device__ __forceinline__ void k1_item(const Params& p, K1Smem& sm, int item, i
     if (!(BF && q.trunc)) {
       // the whole-row normaliser, unless top-k fixes the kept set (fp32 truncated rows: radix select)
       if (!q.useK && m > -INFINITY) {
+        const float nmc = -m * q.c;  // exp2(l c - m c): one fma per logit
 #pragma unroll
         for (int u = 0; u < VPT; ++u) {
           const int j = tid + u * NT;
           if (j < nv) {
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) sum += fexp2((E::get(v[u], e) - m) * q.c);
+            for (int e = 0; e < EPV; ++e) sum += fexp2(fmaf(E::get(v[u], e), q.c, nmc));
           }
         }
       }
@@ -1796,9 +1798,6 @@ __device__ __forceinline__ void k5_position(const Params& p, K5Smem& sm, int b, 
   if (lane == 0) sm.wacc[i][wave] = acc;
 }
 
-// Every draft position of this slice, one position's slices at a time: (a0, b0) hold position 0 on
-// entry, and position i + 1 is loaded once position i is done.  A second pair in flight would need 16
-// more VGPRs and cost a workgroup per CU (4 instead of 5), which loses more than the overlap gains.
 template <class E, int VPT, bool TRUNC>
 __device__ __forceinline__ void k5_positions(const Params& p, K5Smem& sm, int b, int n, int x0, int nv, float c,
                                              uint4 (&a0)[VPT], uint4 (&b0)[VPT], float& best, int& bidx, float& bval) {
@@ -1991,7 +1990,8 @@ __device__ __forceinline__ void k5_item(const Params& p, K5Smem& sm, int item, i
   const RowParams q = row_params(p, b);
   // Everything else independent is issued at once: the first position's slices, the rows'
   // statistics (with the logits at the draft tokens), the draft tokens and the accept uniforms.
-  // Truncated rows wait for their statistics: they may take the candidate path instead.
+  // Truncated rows wait for their statistics: they may take the candidate path instead.  (Issuing
+  // the slices of rows unlikely to take it at once as well measured no faster.)
   uint4 a0[VPT], b0[VPT];
   if (!q.greedy && !q.trunc && k > 0) {
     load_slice<E, VPT>(row_ptr(p, b, 0, esize), x0, nv, a0);
@@ -2014,6 +2014,10 @@ __device__ __forceinline__ void k5_item(const Params& p, K5Smem& sm, int item, i
     const int qq = tid & 3;
     sm.u[tid] = u24(qq == 0 ? w4.x : qq == 1 ? w4.y : qq == 2 ? w4.z : w4.w);
   }
+  // Greedy rows need nothing but the row statistics: workgroup 0 of the batch row writes every output,
+  // the others leave.  (Tested only after the loads above are issued, so that other rows do not wait
+  // for the temperature before issuing them.)
+  if (q.greedy && s != 0) return;
   __syncthreads();
   SV_TRACE5_AT(p, item, 1);
   bool ok = q.ok;
@@ -2022,6 +2026,11 @@ __device__ __forceinline__ void k5_item(const Params& p, K5Smem& sm, int item, i
   for (int r = 0; r < rows; ++r) {
     ok = ok && (sm.state[r] & ST_BAD) == 0;
     sparse = sparse && (sm.state[r] & ST_SPARSE) != 0;
+  }
+  if (q.greedy) {  // workgroup 0 only (see above): no slice partials, no arrivals
+    k5_finalize<E>(p, sm, b, ok, q);
+    SV_TRACE5_AT(p, item, 7);
+    return;
   }
   if (ok && sparse && s > k) {  // candidate-path row: this workgroup has no position to finish
     SV_TRACE5_AT(p, item, 7);
