@@ -59,6 +59,7 @@ constexpr int FVPT = 2;         // whole-row passes of one workgroup: vectors pe
 constexpr int WTOP = 512;       // K1: exact per-code window below the slice max
 constexpr int NBC = 256;        // K1: weight bins of top-p-only rows
 constexpr float BRC = 8.0f;     // weight bins per log2 unit
+constexpr int NCOPY = 4;        // K1: interleaved copies of each weight bin (lane & 3 picks one)
 constexpr int WF = 2048;        // widest exact code window of the whole-row pass
 constexpr int MAXS1 = 64;       // slices per bf16 row at the largest V
 constexpr int MB = 8;           // merge: slices whose histogram words are loaded in one round trip
@@ -623,7 +624,8 @@ struct K1Smem {
   union {
     struct {                    // streaming phase; entries past WTOP / NBC absorb out-of-range
       uint32_t hw[WTOP + 64];   // logits, one per lane, so the atomics need no branch
-      uint32_t hc[NBC + 64];
+      uint32_t hc[(NBC + 64) * NCOPY];  // bin j, copy q at j NCOPY + q: lanes that hit one bin
+                                        // mostly hit different words (fewer same-address atomics)
       unsigned long long cand[NC];  // logits within WC codes of the slice max: index << 16 | bits
       uint32_t ncand;
       uint4 fvec[NWAVE * NFW];  // staged vectors that hold a candidate, and their vector indices
@@ -1114,6 +1116,8 @@ __device__ __forceinline__ void k1_hist(K1Smem& sm, const uint4 (&v)[VPT], int n
   const uint32_t keyms2 = keyms * 0x10001u;
   const uint32_t spare2 = (WTOP + lane) * 0x10001u;
   const uint32_t spare_c = NBC + lane;
+  const uint32_t copy4 = (lane & (NCOPY - 1)) << 2;  // byte offset of this lane's copy of a bin
+  uint8_t* const hcb = (uint8_t*)sm.u.st.hc;
   const float cb = c * BRC;
   const float nmc = -ms * c;
   uint32_t cmask = 0;  // bit u: vector u holds a candidate (an entry within WC codes of the slice max)
@@ -1135,8 +1139,8 @@ __device__ __forceinline__ void k1_hist(K1Smem& sm, const uint4 (&v)[VPT], int n
           sum += fexp2(fmaf(f1, c, nmc));
           const uint32_t j0 = min(__float2uint_rz(fmaf(f0, -cb, -cbase)), spare_c);
           const uint32_t j1 = min(__float2uint_rz(fmaf(f1, -cb, -cbase)), spare_c);
-          atomicAdd(&sm.u.st.hc[j0], 1u);
-          atomicAdd(&sm.u.st.hc[j1], 1u);
+          atomicAdd((uint32_t*)(hcb + ((j0 * (NCOPY * 4)) | copy4)), 1u);
+          atomicAdd((uint32_t*)(hcb + ((j1 * (NCOPY * 4)) | copy4)), 1u);
         }
       }
       if (min(dmin & 0xffffu, dmin >> 16) < (uint32_t)WC) cmask |= 1u << u;
@@ -1383,7 +1387,10 @@ __device__ __forceinline__ void k1_item(const Params& p, K1Smem& sm, int item, i
       const bool topp_only = !q.useK;
       sm.u.st.hw[tid] = 0;
       sm.u.st.hw[tid + NT] = 0;
-      if (topp_only) sm.u.st.hc[tid] = 0;
+      if (topp_only) {
+#pragma unroll
+        for (int q = 0; q < NCOPY; ++q) sm.u.st.hc[tid + q * NT] = 0;  // the bins, not the spares
+      }
       if (tid == 0) {
         sm.u.st.ncand = 0;
         sm.u.st.nflag = 0;
@@ -1408,7 +1415,15 @@ __device__ __forceinline__ void k1_item(const Params& p, K1Smem& sm, int item, i
       if (tid == 0) st32(&p.ncand1[(size_t)r * p.S1 + s], nc);
       if (topp_only) {
         uint32_t* hc = p.hc1 + ((size_t)r * p.S1 + s) * HCW;
-        if (tid < NBC / 2) st32(&hc[tid], sm.u.st.hc[2 * tid] | (sm.u.st.hc[2 * tid + 1] << 16));
+        if (tid < NBC / 2) {
+          uint32_t c0 = 0, c1 = 0;
+#pragma unroll
+          for (int q = 0; q < NCOPY; ++q) {
+            c0 += sm.u.st.hc[2 * tid * NCOPY + q];
+            c1 += sm.u.st.hc[(2 * tid + 1) * NCOPY + q];
+          }
+          st32(&hc[tid], c0 | (c1 << 16));
+        }
         if (tid == 0) stf(&hc[NBC / 2], cbase);
       }
     }
@@ -2418,6 +2433,7 @@ static void prof_mark(int idx, hipStream_t st) {
 template <class E>
 static void enqueue(const Params& p, int cus, hipStream_t st) {
   static_assert(WTOP / 2 == NT && NBC == NT, "K1 assumes one histogram word pair per thread");
+  static_assert((NCOPY & (NCOPY - 1)) == 0 && NCOPY <= 64, "weight-bin copies: a power of two");
   (void)cus;
   const dim3 g1((unsigned)(p.R * p.S1)), gr((unsigned)p.R), g5((unsigned)(p.B * p.S5));
   const bool raw = p.raw_logprobs != nullptr;
