@@ -2002,32 +2002,36 @@ __device__ __forceinline__ void k5_item(const Params& p, K5Smem& sm, int item, i
   const int k = p.k, rows = p.rows;
   const int x0 = s * p.L5;
   const int nv = min(p.L5, p.V - x0) / EPV;
+  // Everything independent is issued at once: the rows' statistics (with the logits at the draft
+  // tokens) and the draft tokens into registers, then the first position's slices; the accept
+  // uniforms are computed while they are in flight.  Truncated rows wait for their
+  // statistics before loading slices: they may take the candidate path instead.  (Issuing the slices
+  // of rows unlikely to take it at once as well measured no faster.)
   const RowParams q = row_params(p, b);
-  // Everything else independent is issued at once: the first position's slices, the rows'
-  // statistics (with the logits at the draft tokens), the draft tokens and the accept uniforms.
-  // Truncated rows wait for their statistics: they may take the candidate path instead.  (Issuing
-  // the slices of rows unlikely to take it at once as well measured no faster.)
+  RowInfo ri{};
+  if (tid < rows) ri = p.rinfo[(size_t)b * rows + tid];
+  int32_t tokv = 0;
+  if (tid < k) tokv = p.draft_tokens[(size_t)b * k + tid];
   uint4 a0[VPT], b0[VPT];
   if (!q.greedy && !q.trunc && k > 0) {
     load_slice<E, VPT>(row_ptr(p, b, 0, esize), x0, nv, a0);
     load_slice<E, VPT>(row_ptr(p, b, k + 1, esize), x0, nv, b0);
   }
-  if (tid < rows) {
-    const RowInfo* ri = p.rinfo + (size_t)b * rows + tid;
-    sm.m[tid] = ri->m;
-    sm.arg[tid] = ri->arg;
-    sm.Z[tid] = ri->Z;
-    sm.lz[tid] = ri->lz;
-    sm.fthr[tid] = ri->fthr;
-    sm.state[tid] = ri->state;
-    sm.gath[tid] = ri->gath;
-    if (p.raw_logprobs) sm.rlz[tid] = ri->rlz;
-  }
   if (tid < k) {
-    sm.tok[tid] = p.draft_tokens[(size_t)b * k + tid];
     const uint4 w4 = philox10(make_uint4((uint32_t)tid >> 2, (uint32_t)b, 0u, p.offset), p.key0, p.key1);
     const int qq = tid & 3;
     sm.u[tid] = u24(qq == 0 ? w4.x : qq == 1 ? w4.y : qq == 2 ? w4.z : w4.w);
+    sm.tok[tid] = tokv;
+  }
+  if (tid < rows) {
+    sm.m[tid] = ri.m;
+    sm.arg[tid] = ri.arg;
+    sm.Z[tid] = ri.Z;
+    sm.lz[tid] = ri.lz;
+    sm.fthr[tid] = ri.fthr;
+    sm.state[tid] = ri.state;
+    sm.gath[tid] = ri.gath;
+    if (p.raw_logprobs) sm.rlz[tid] = ri.rlz;
   }
   // Greedy rows need nothing but the row statistics: workgroup 0 of the batch row writes every output,
   // the others leave.  (Tested only after the loads above are issued, so that other rows do not wait

@@ -179,6 +179,24 @@ def test_special_values_and_sentinels(o):
     assert reps[0]["sentinel"] == 7
 
 
+def test_greedy_rows_among_sampled_rows_and_greedy_sentinels(o):
+    """Greedy batch rows (written by one workgroup from the row statistics) interleaved with sampled and
+    truncated rows, and greedy rows that must become sentinel rows."""
+    w = W.make(12, 2, 20000, seed=78, boost=8.0, tie_fraction=0.1, mixed_params=True, name="greedy_mix")
+    w.temperature[[0, 2, 3, 5, 6, 7, 8, 9, 11]] = 0.0   # rows 1, 4, 10 keep their sampled parameters
+    drafts = w.draft_tokens(parity.oracle_sampler(o)).copy()
+    a0 = np.argmax(W.bf16_to_f32(w.target[0, 0]))
+    drafts[0, 0] = a0                                    # greedy row accepting its first draft at least
+    w.target[5, 1, 7] = np.uint16(0x7FC0)                # NaN in a greedy row -> sentinel
+    w.draft[6, 0, 11] = np.uint16(0x7F80)                # +inf in a greedy row's draft -> sentinel
+    drafts[7, 1] = -1                                    # draft token out of range -> sentinel
+    w.top_k[8] = -2                                      # invalid top-k with temperature 0 -> sentinel
+    w.target[9, 0, :] = np.uint16(0xFF80)                # all -inf target row -> sentinel
+    w.target[11, :, ::2] = np.uint16(0xFF80)             # -inf entries are legal in greedy rows
+    reps = _check(o, w, [0, 4], "greedy_mix", drafts)
+    assert reps[0]["sentinel"] == 5
+
+
 def test_gpu_output_marginal_chi2(o):
     """The GPU path's committed first token follows p_0 (1e5 independent batch rows, V = 16)."""
     from scipy import special, stats
