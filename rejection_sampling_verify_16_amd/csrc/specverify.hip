@@ -926,33 +926,39 @@ __device__ __forceinline__ void k1_merge(const Params& p, K1Smem& sm, int r, int
   float m = -INFINITY, sum = 0.0f;
   int a = INT_MAX;
   uint32_t fl = 0, flo = 0;
-  // slice holding this row's draft token (-1: none or out of range)
-  int sg = -1;
-  if (p.mode == MODE_VERIFY && i != p.k) {
-    const int xg = p.draft_tokens[(size_t)b * p.k + (i < p.k ? i : i - p.k - 1)];
-    if (xg >= 0 && xg < p.V) sg = xg / p.L1;
-  }
+  // Every partial the merge needs is issued before any of them is used (one round trip): the logit at
+  // the draft token of every slice is loaded, the one of the slice holding the token is kept.
+  uint32_t gv = 0, ncv = 0;
+  float cbv = 0.0f;
   if (tid < S) {
     const StatPart* sp = p.st1 + (size_t)r * S + tid;
     m = ldf(&sp->m);
     a = (int)ld32(&sp->arg);
     sum = ldf(&sp->s);
     fl = ld32(&sp->flags);
-    if (tid == sg) sm.win[1] = ld32(&sp->g);
-    if (hist || cmode) sm.u.mg.ncs[tid] = ld32(&p.ncand1[(size_t)r * S + tid]);
+    gv = ld32(&sp->g);
+    if (hist || cmode) ncv = ld32(&p.ncand1[(size_t)r * S + tid]);
     if (cmode) flo = ld32(&sp->floor);
+    if (coarse) cbv = ldf(&p.hc1[((size_t)r * S + tid) * HCW + NBC / 2]);
   }
   uint32_t hwv[MB];
   if (hist) {
 #pragma unroll
     for (int t = 0; t < MB; ++t) hwv[t] = t < S ? ld32(&p.hw1[((size_t)r * S + t) * (WTOP / 2) + tid]) : 0u;
+  }
+  int32_t xg = -1;  // this row's draft token (draft-position rows), loaded after the partials are in flight
+  if (p.mode == MODE_VERIFY && i != p.k) xg = p.draft_tokens[(size_t)b * p.k + (i < p.k ? i : i - p.k - 1)];
+  const int sg = (xg >= 0 && xg < p.V) ? xg / p.L1 : -1;  // slice holding it (-1: none or out of range)
+  if (tid < S) {
+    if (tid == sg) sm.win[1] = gv;
+    if (hist || cmode) sm.u.mg.ncs[tid] = ncv;
+    if (coarse) sm.u.mg.cbs[tid] = cbv;
+  }
+  if (hist) {
     sm.u.mg.cnt[tid] = 0;
     sm.u.mg.cnt[tid + NT] = 0;
   }
-  if (coarse) {
-    if (tid < S) sm.u.mg.cbs[tid] = ldf(&p.hc1[((size_t)r * S + tid) * HCW + NBC / 2]);
-    sm.u.mg.bc[tid] = 0;
-  }
+  if (coarse) sm.u.mg.bc[tid] = 0;
   if (hist && tid < S) sm.u.mg.keyms[tid] = key16f(m);
   block_stats(sm.rs, m, a, sum, fl, q.c);  // its barriers publish keyms / cbs and the cleared counts
   const bool bad = fl != 0 || !(m > -INFINITY) || m == INFINITY;
