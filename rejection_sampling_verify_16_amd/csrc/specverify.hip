@@ -1277,18 +1277,19 @@ __device__ __forceinline__ void k1_item(const Params& p, K1Smem& sm, int item, i
   constexpr bool BF = E::KEYBITS == 16;
   const int tid = threadIdx.x;
   const int b = r / p.rows, i = r - b * p.rows;
-  const RowParams q = row_params(p, b);
   const int x0 = s * p.L1;
   const int nv = min(p.L1, p.V - x0) / EPV;
   const uint4* src = (const uint4*)(row_ptr(p, b, i, esize) + (size_t)x0 * esize);
   SV_TRACE_AT(p, item, 0);
 
+  // the slice's loads go out first: nothing in them waits for the sampling parameters
   uint4 v[VPT];
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
     const int j = tid + u * NT;
     if (j < nv) v[u] = src[j];
   }
+  const RowParams q = row_params(p, b);
   // draft-position rows also record their logit at the draft token (used by the accept chain)
   float gval = 0.0f;
   if (p.mode == MODE_VERIFY && i != p.k) {
