@@ -190,6 +190,9 @@ __device__ inline void st32(void* p, uint32_t v) {
   __hip_atomic_store((uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ inline void stf(void* p, float v) { st32(p, __float_as_uint(v)); }
+// Plain stores, for partials read only by a later kernel (the kernel boundary makes them visible).
+__device__ inline void pst32(void* p, uint32_t v) { *(uint32_t*)p = v; }
+__device__ inline void pstf(void* p, float v) { *(float*)p = v; }
 __device__ inline uint32_t ld32(const void* p) {
   return __hip_atomic_load((const uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1216,8 +1219,8 @@ __device__ inline uint32_t wave_kth_key(uint32_t key, int kth) {
   return t;
 }
 
-// Candidates of a top-k slice: every logit with key >= fe, written (index << 16 | bits) to the slice's
-// record in the workspace.  vm holds the vector maxima.  Each wave stages its own vectors whose maximum
+// Candidates of a top-k slice: every logit with key >= fe, collected (index << 16 | bits) in LDS; the
+// item writes them to the slice's record in one coalesced store.  vm holds the vector maxima.  Each wave stages its own vectors whose maximum
 // reaches fe in its LDS region, then one lane per staged vector appends that vector's candidates, with
 // one slot reservation per wave.  A wave with more than NFW such vectors sets `over`; more than NC
 // candidates leave ncand above NC.  Either way the slice has no usable record.
@@ -1255,15 +1258,12 @@ __device__ __forceinline__ void k1_capture(const Params& p, K1Smem& sm, const ui
   const uint32_t bits = mine ? cand_bits_ge(vv, fe) : 0u;
   const int xb = x0 + (mine ? (int)fi[lane] : 0) * BF16::EPV;
   uint32_t c = wave_reserve(&sm.u.st.ncand, (uint32_t)__popc(bits));
-  unsigned long long* dst = p.cand1 + ((size_t)r * p.S1 + s) * NC;
   const uint32_t wv[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
   for (int e = 0; e < BF16::EPV; ++e) {
     if (bits & (1u << e)) {
       const uint32_t h = (e & 1) ? (wv[e >> 1] >> 16) : (wv[e >> 1] & 0xffffu);
-      if (c < (uint32_t)NC)
-        __hip_atomic_store(dst + c, ((unsigned long long)(xb + e) << 16) | h, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+      if (c < (uint32_t)NC) sm.u.st.cand[c] = ((unsigned long long)(xb + e) << 16) | h;
       ++c;
     }
   }
@@ -1413,13 +1413,13 @@ __device__ __forceinline__ void k1_item(const Params& p, K1Smem& sm, int item, i
       m = ms;  // the sums above are relative to the slice max
       __syncthreads();
       uint32_t* hw = p.hw1 + ((size_t)r * p.S1 + s) * (WTOP / 2);
-      st32(&hw[tid], sm.u.st.hw[2 * tid] | (sm.u.st.hw[2 * tid + 1] << 16));  // WTOP / 2 == NT
+      pst32(&hw[tid], sm.u.st.hw[2 * tid] | (sm.u.st.hw[2 * tid + 1] << 16));  // WTOP / 2 == NT
       const uint32_t nc = sm.u.st.ncand;
       if (tid < (int)min(nc, (uint32_t)NC)) {
         unsigned long long* cd = p.cand1 + ((size_t)r * p.S1 + s) * NC + tid;
-        __hip_atomic_store(cd, sm.u.st.cand[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *cd = sm.u.st.cand[tid];
       }
-      if (tid == 0) st32(&p.ncand1[(size_t)r * p.S1 + s], nc);
+      if (tid == 0) pst32(&p.ncand1[(size_t)r * p.S1 + s], nc);
       if (topp_only) {
         uint32_t* hc = p.hc1 + ((size_t)r * p.S1 + s) * HCW;
         if (tid < NBC / 2) {
@@ -1429,9 +1429,9 @@ __device__ __forceinline__ void k1_item(const Params& p, K1Smem& sm, int item, i
             c0 += sm.u.st.hc[2 * tid * NCOPY + q];
             c1 += sm.u.st.hc[(2 * tid + 1) * NCOPY + q];
           }
-          st32(&hc[tid], c0 | (c1 << 16));
+          pst32(&hc[tid], c0 | (c1 << 16));
         }
-        if (tid == 0) stf(&hc[NBC / 2], cbase);
+        if (tid == 0) pstf(&hc[NBC / 2], cbase);
       }
     }
     if (!(m == m) || m == INFINITY) fl = 1u;
@@ -1467,16 +1467,20 @@ __device__ __forceinline__ void k1_item(const Params& p, K1Smem& sm, int item, i
   if (tid == 0) {
     StatPart* sp = p.st1 + (size_t)r * p.S1 + s;
     if (RAW) {
-      stf(&sp->rmax, rmax);
-      stf(&sp->rsum, rsum);
+      pstf(&sp->rmax, rmax);
+      pstf(&sp->rsum, rsum);
     }
-    stf(&sp->m, m);
-    st32(&sp->arg, (uint32_t)a);
-    stf(&sp->s, sum);
-    st32(&sp->flags, fl);
-    stf(&sp->g, gval);
-    st32(&sp->floor, flo);
-    if (BF && q.cand) st32(&p.ncand1[(size_t)r * p.S1 + s], sm.u.st.over ? (uint32_t)NC + 1u : sm.u.st.ncand);
+    pstf(&sp->m, m);
+    pst32(&sp->arg, (uint32_t)a);
+    pstf(&sp->s, sum);
+    pst32(&sp->flags, fl);
+    pstf(&sp->g, gval);
+    pst32(&sp->floor, flo);
+    if (BF && q.cand) pst32(&p.ncand1[(size_t)r * p.S1 + s], sm.u.st.over ? (uint32_t)NC + 1u : sm.u.st.ncand);
+  }
+  if (BF && q.cand) {  // the candidates collected in LDS (block_stats' barriers order them), coalesced
+    const uint32_t nc = sm.u.st.ncand;
+    if (tid < (int)min(nc, (uint32_t)NC)) p.cand1[((size_t)r * p.S1 + s) * NC + tid] = sm.u.st.cand[tid];
   }
   SV_TRACE_AT(p, item, 2);
 }
