@@ -1,0 +1,49 @@
+"""Randomised parity sweep: small ragged shapes, bf16 and fp32, k from 1 to 8, and per-row sampling parameters
+drawn from the values the kernels branch on (greedy; top-k 1, 5, 50, 64, 65, 1000, >= V; top-p 0.05 to 1;
+temperatures 0.3 to 2), several rows of each kind in one batch, compared with the oracle element by element."""
+import numpy as np
+import pytest
+
+import oracle
+import parity
+from rejection_sampling_verify_16_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 24
+
+
+@pytest.fixture(scope="module")
+def o():
+    return oracle.get()
+
+
+def _case(i):
+    rng = np.random.default_rng(9000 + i)
+    dtype = "f32" if i % 4 == 3 else "bf16"
+    epv = 4 if dtype == "f32" else 8
+    B = int(rng.integers(1, 9))
+    k = int(rng.integers(1, 9))
+    V = int(rng.integers(1, 5001)) * epv          # ragged against the 4096- and 16384-logit slices
+    w = W.make(B, k, V, dtype=dtype, seed=9100 + i, target_sigma=float(rng.uniform(1.0, 4.0)),
+               noise_sigma=float(rng.uniform(0.2, 1.5)), boost=float(rng.choice([0.0, 8.0])),
+               tie_fraction=float(rng.choice([0.0, 0.2])), name=f"sweep{i}")
+    T = rng.uniform(0.3, 2.0, size=B).astype(np.float32)
+    T[rng.random(B) < 0.2] = 0.0
+    K = rng.choice(np.array([0, 1, 5, 50, 64, 65, 1000, V], dtype=np.int32), size=B).astype(np.int32)
+    P = rng.choice(np.array([1.0, 0.99, 0.9, 0.5, 0.05], dtype=np.float32), size=B).astype(np.float32)
+    w.temperature, w.top_k, w.top_p = T, K, P
+    return w
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_case(o, i):
+    w = _case(i)
+    drafts = w.draft_tokens(parity.oracle_sampler(o))
+    dev = parity.device_inputs(w, drafts)
+    for off in (0, 7):
+        print(f"[sweep] case {i}: B={w.B} k={w.k} V={w.V} {w.dtype} offset={off}", flush=True)
+        g = parity.run_gpu(dev, 11 + i, off)
+        r = o.spec_verify(w.target, w.draft, drafts, w.temperature, w.top_k, w.top_p, seed=11 + i, offset=off)
+        rep = parity.compare(g, r, drafts, w.V, label=f"sweep{i}@{off}")
+        print(f"[sweep] case {i}@{off}: {rep}", flush=True)
