@@ -93,6 +93,9 @@ SMALL = [
     # the largest vocabulary: 64 slices per bf16 row (the candidate records' limit), 128 per fp32 row
     ("maxV_bf16_mixed", 4, 2, 1 << 20, "bf16", dict(boost=8.0, mixed_params=True)),
     ("maxV_f32_topk", 2, 1, 1 << 20, "f32", dict(temperature=0.8, top_k=40, top_p=0.9)),
+    # many batch rows of a small vocabulary: grids of 40k (statistics and merges) and 20k (verify) workgroups
+    ("many_rows", 20000, 1, 64, "bf16", dict(boost=4.0, mixed_params=True)),
+    ("many_rows_k8", 2000, 8, 256, "f32", dict(mixed_params=True)),
 ]
 
 
