@@ -629,7 +629,8 @@ struct K1Smem {
       uint32_t hw[WTOP + 64];   // logits, one per lane, so the atomics need no branch
       uint32_t hc[(NBC + 64) * NCOPY];  // bin j, copy q at j NCOPY + q: lanes that hit one bin
                                         // mostly hit different words (fewer same-address atomics)
-      unsigned long long cand[NC];  // logits within WC codes of the slice max: index << 16 | bits
+      unsigned long long cand[NC];  // the slice's recorded candidates (index << 16 | bits): logits within WC
+                                    // codes of the slice max, or at or above a top-k slice's floor
       uint32_t ncand;
       uint4 fvec[NWAVE * NFW];  // staged vectors that hold a candidate, and their vector indices
       uint32_t fidx[NWAVE * NFW];
