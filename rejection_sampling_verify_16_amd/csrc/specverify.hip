@@ -208,6 +208,7 @@ __device__ inline void drain() {
 __device__ inline bool arrive_last(uint32_t* counter, uint32_t total, int* flag) {
   drain();
   __syncthreads();
+  if (total == 1) return true;  // the only arrival: no round trip (the counter stays at 0)
   if (threadIdx.x == 0) *flag = (atomicAdd(counter, 1u) == total - 1) ? 1 : 0;
   __syncthreads();
   return *flag != 0;
