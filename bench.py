@@ -142,10 +142,10 @@ def main():
     stream = torch.cuda.current_stream(dev)
     offsets = w.offsets
 
-    def step(i):
+    def step(i, timing=None):
         t_, d_ = sets[i % n_sets]
         sv.spec_verify(t_, d_, drafts, T, K, P, seed=w.seed, offset=offsets[i % len(offsets)], out=out,
-                       workspace=ws, stream=stream, raw=args.raw_logprobs)
+                       workspace=ws, stream=stream, raw=args.raw_logprobs, timing=timing)
 
     for i in range(args.warmup):
         step(i)
@@ -268,10 +268,10 @@ def bench_configs(args, dev):
         offs = w.offsets
         n = len(offs) if len(offs) > 1 else 200
 
-        def step(i):
+        def step(i, timing=None):
             t_, d_ = sets[i % n_sets]
             sv.spec_verify(t_, d_, drafts, T, K, P, seed=w.seed, offset=offs[i % len(offs)], out=out, workspace=ws,
-                           stream=stream)
+                           stream=stream, timing=timing)
 
         for i in range(10):
             step(i)
@@ -318,10 +318,10 @@ def bench_tree(args, dev):
     out = None
     stream = torch.cuda.current_stream(dev)
 
-    def step(i):
+    def step(i, timing=None):
         nonlocal out
         out = sv.spec_tree_verify(sets[i % n_sets], par, tok, T, K, P, seed=w.seed, offset=i, out=out, workspace=ws,
-                                  stream=stream)
+                                  stream=stream, timing=timing)
 
     n = max(50, args.steps // 2)
     for i in range(10):
@@ -539,21 +539,25 @@ def pmc_summary(args):
 
 
 def kernel_durations(sv, step, n, stream):
-    """Mean duration (ms) of each of the library's kernels over n calls, from HIP events the library
-    records around its launches (spec_set_kernel_events)."""
+    """Mean duration (ms) of each of the library's kernels over n calls, from HIP events that the timed
+    entry points record around the launches of each call, on the stream the kernels run on.  step(i, timing)
+    makes call i with that KernelTiming.  Returns one mean per kernel the calls launched."""
     import torch
-    nk = sv.SPEC_NUM_KERNELS
+    nk = sv.SPEC_MAX_KERNELS
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nk)] for _ in range(n)]
     for row in evs:  # a first record creates the underlying hipEvent_t
         for e in row:
             e.record(stream)
     torch.cuda.synchronize()
+    used = set()
     for i in range(n):
-        sv.set_kernel_events([e.cuda_event for e in evs[i]])
-        step(i)
-    sv.set_kernel_events(None)
+        t = sv.KernelTiming([e.cuda_event for e in evs[i]])
+        step(i, t)
+        used.add(t.kernels)
     torch.cuda.synchronize()
-    per = [[evs[i][2 * j].elapsed_time(evs[i][2 * j + 1]) for i in range(n)] for j in range(nk)]
+    assert len(used) == 1, f"calls launched different kernel counts: {used}"
+    nk_used = used.pop()
+    per = [[evs[i][2 * j].elapsed_time(evs[i][2 * j + 1]) for i in range(n)] for j in range(nk_used)]
     return tuple(float(np.mean(x)) for x in per)
 
 

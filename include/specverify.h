@@ -56,8 +56,9 @@ typedef enum {
 
 /*
  * Bytes of device workspace spec_verify() needs for these sizes (0 if the sizes are invalid).
- * The workspace must be zero-filled once before its first use (e.g. hipMemset); every completed
- * call leaves the bytes the next call relies on at zero again, so it can be reused without clearing.
+ * The workspace needs no initialisation and may hold anything: every call writes each workspace byte it
+ * reads (partials, arrival counters, flags) before reading it, in stream order.  Calls that share one
+ * workspace must not overlap (order them on one stream).
  */
 size_t spec_verify_workspace_size(int32_t B, int32_t k, int32_t V, spec_dtype_t dtype);
 
@@ -71,7 +72,8 @@ size_t spec_verify_workspace_size(int32_t B, int32_t k, int32_t V, spec_dtype_t 
  *   temperature    float [B]   0 = greedy (top_k/top_p ignored)
  *   top_k          int32 [B]   0 or >= V = off
  *   top_p          float [B]   >= 1 (including +inf) = off
- *   B, k, V        1 <= B <= 2^20, 1 <= k <= 8, 8 <= V <= 2^20
+ *   B, k, V        1 <= B <= 2^20, 1 <= k <= 8, 1 <= V <= 2^20 (with V % 8 == 0 for bf16 and
+ *                  V % 4 == 0 for fp32, so V >= 8 for bf16 and V >= 4 for fp32)
  *   seed, offset   Philox key and counter word 3; offset < 2^32
  *   tokens         out int32 [B, k+1]  x_0..x_{n-1}, the drawn token, then -1
  *   accept_len     out int32 [B]       n + 1 (committed tokens, 1..k+1), 0 for a sentinel row
@@ -116,7 +118,7 @@ spec_status_t spec_verify_raw(const void* target_logits, const void* draft_logit
  *   logits        [R, V] row-major, contiguous, dtype; 16-byte aligned
  *   temperature   float [R]; top_k int32 [R]; top_p float [R] (meaning as in spec_verify)
  *   row_b, row_pos  int32 [R] stream coordinates (b, i) of each row; NULL = (row index, 0)
- *   R, V          1 <= R <= 2^20, 8 <= V <= 2^20 (V % 8 == 0 for bf16, V % 4 == 0 for fp32)
+ *   R, V          1 <= R <= 2^20, 1 <= V <= 2^20 (V % 8 == 0 for bf16, V % 4 == 0 for fp32)
  *   tokens        out int32 [R]   the drawn token (-1 for a row with unusable inputs)
  *   logprobs      out float [R]   ln of its sampler probability (0 for greedy rows, NaN if unusable)
  *   workspace     at least spec_sample_workspace_size(R, V, dtype) bytes, same rules as spec_verify
@@ -252,22 +254,40 @@ spec_status_t spec_commit_slots(int32_t* state_slot, int32_t* pos_slot, const in
 const char* spec_verify_status_string(spec_status_t status);
 
 /*
- * Benchmark hook: per-kernel timing of later calls.  Each spec_verify / spec_sample / spec_tree_verify
- * call enqueues SPEC_NUM_KERNELS kernels: 0 = per-slice row statistics (reads every logit once),
- * 1 = per-row merges and kept thresholds, 2 = accept chain (or tree walk), alpha and draws (re-reads the
- * rows it draws from).
+ * Per-kernel timing of one call, for benchmarks.  The timed entry points take the arguments of the call
+ * they time (spec_verify_timed: spec_verify's, plus raw_logprobs, which may be NULL for the plain verify
+ * step and otherwise makes it spec_verify_raw; spec_tree_verify_timed: spec_tree_verify's) and one
+ * spec_timing_t.  They enqueue exactly the same kernels, and in addition record, on `stream`,
+ * events[2j] just before kernel j and events[2j+1] just after it, for each of the kernels the call
+ * launches; `kernels` receives how many that is (1 .. SPEC_MAX_KERNELS; which kernels depends on the
+ * sizes and the device).  hipEventElapsedTime(events[2j], events[2j+1]) is then kernel j's duration.
  *
- *   events  NULL (turns the hook off; count ignored) or 2 * SPEC_NUM_KERNELS hipEvent_t handles,
- *           created by the caller with timing enabled and owned by the caller
- *   count   2 * SPEC_NUM_KERNELS
- * While set, every call records events[2j] on its stream just before launching kernel j and
- * events[2j+1] just after it, so hipEventElapsedTime(events[2j], events[2j+1]) is kernel j's duration
- * in the most recent call.  The setting is process-wide and not synchronised: set it from the thread
- * that makes the calls, and turn it off (NULL) before the events are destroyed.
- * Returns SPEC_ERR_INVALID_ARGUMENT if count is wrong.
+ *   events   HOST array of 2 * SPEC_MAX_KERNELS hipEvent_t handles, created by the caller with timing
+ *            enabled; read during the call only.  Entries past 2 * kernels are not recorded.
+ *   kernels  out: kernels this call launched
+ * Nothing is kept between calls: the timing applies to this call alone.  A NULL timing pointer or NULL
+ * events is SPEC_ERR_INVALID_ARGUMENT.
  */
-#define SPEC_NUM_KERNELS 3
-spec_status_t spec_set_kernel_events(void* const* events, int32_t count);
+#define SPEC_MAX_KERNELS 3
+
+typedef struct {
+  void* const* events;
+  int32_t kernels;
+} spec_timing_t;
+
+spec_status_t spec_verify_timed(const void* target_logits, const void* draft_logits, spec_dtype_t dtype,
+                                const int32_t* draft_tokens, const float* temperature, const int32_t* top_k,
+                                const float* top_p, int32_t B, int32_t k, int32_t V, uint64_t seed, uint64_t offset,
+                                int32_t* tokens, int32_t* accept_len, float* logprobs, float* raw_logprobs,
+                                float* alpha, void* workspace, size_t workspace_bytes, void* stream,
+                                spec_timing_t* timing);
+
+spec_status_t spec_tree_verify_timed(const void* target_logits, spec_dtype_t dtype, const int32_t* parent,
+                                     const int32_t* node_tokens, const float* temperature, const int32_t* top_k,
+                                     const float* top_p, int32_t B, int32_t N, int32_t V, uint64_t seed,
+                                     uint64_t offset, int32_t* tokens, int32_t* path, int32_t* accept_len,
+                                     float* logprobs, void* workspace, size_t workspace_bytes, void* stream,
+                                     spec_timing_t* timing);
 
 #ifdef __cplusplus
 }

@@ -73,6 +73,8 @@ class VerifyResult:
     fallback: np.ndarray       # bool [B]
     sentinel: np.ndarray       # bool [B]
     n_accepted: np.ndarray     # int32 [B]
+    topp_rows: np.ndarray | None = None   # float64 [B, 2k+1, 2]: |M/Z_K - P| at the chosen and next larger value
+    accept_pos: np.ndarray | None = None  # float64 [B, k]: |u - p/q| per evaluated accept test (+inf otherwise)
 
     def margin_rows(self, tol_accept: float = 1e-5, tol_gap: float = 1e-5, tol_topp: float = 1e-5) -> np.ndarray:
         """Rows whose outcome a different (correct) rounding could change: boolean [B]."""
@@ -120,6 +122,9 @@ class Oracle:
         L.oracle_spec_verify.argtypes = [_P, _P, _I32, _P, _P, _P, _P, _I32, _I32, _I32, _U64, _U64,
                                          _P, _P, _P, _P, _P, _P, _I32]
         L.oracle_spec_verify.restype = ctypes.c_int
+        L.oracle_spec_verify_ex.argtypes = [_P, _P, _I32, _P, _P, _P, _P, _I32, _I32, _I32, _U64, _U64,
+                                            _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32]
+        L.oracle_spec_verify_ex.restype = ctypes.c_int
         L.oracle_sample.argtypes = [_P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _U64, _U64, _P, _P, _P, _I32]
         L.oracle_sample.restype = ctypes.c_int
         L.oracle_raw_logprobs.argtypes = [_P, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _I32]
@@ -151,16 +156,19 @@ class Oracle:
         l = np.ascontiguousarray(np.asarray(logits, dtype=np.float64))
         V = l.shape[0]
         probs = np.zeros(V, dtype=np.float64)
-        info = np.zeros(6, dtype=np.float64)
+        info = np.zeros(8, dtype=np.float64)
         rc = self.lib.oracle_row_probs(_ptr(l), V, float(T), int(K), float(P), _ptr(probs), _ptr(info))
         if rc != 0:
             raise ValueError("row has no distribution (all -inf)")
         return probs, dict(m=info[0], argmax=int(info[1]), Z=info[2], kept=int(info[3]), thr=info[4],
-                           topp_margin=info[5])
+                           topp_margin=info[5], topp_at=info[6], topp_prev=info[7])
 
     # -- the verify step ------------------------------------------------------------------
     def spec_verify(self, target, draft, draft_tokens, temperature, top_k, top_p, seed: int = 0,
-                    offset: int = 0, num_threads: int = 0) -> VerifyResult:
+                    offset: int = 0, num_threads: int = 0, alt=None, details: bool = False) -> VerifyResult:
+        """The verify step.  ``details`` adds the per-decision distances (topp_rows, accept_pos).  ``alt``
+        (int32 [B, 4], see oracle_spec_verify_ex) computes only the rows with alt[b, 3] != 0, each with the
+        alternative resolutions it names; other rows of the result are zeros."""
         target = np.ascontiguousarray(target)
         draft = np.ascontiguousarray(draft)
         if target.dtype == np.uint16:
@@ -185,13 +193,23 @@ class Oracle:
         al = np.zeros((B, k), dtype=np.float64)
         diag = np.zeros((B, 4), dtype=np.float64)
         fl = np.zeros(B, dtype=np.int32)
-        rc = self.lib.oracle_spec_verify(_ptr(target), _ptr(draft), dtype, _ptr(dt), _ptr(T), _ptr(K), _ptr(P),
-                                         B, k, V, int(seed), int(offset), _ptr(tokens), _ptr(acc), _ptr(lp),
-                                         _ptr(al), _ptr(diag), _ptr(fl), int(num_threads))
+        if alt is None and not details:
+            rc = self.lib.oracle_spec_verify(_ptr(target), _ptr(draft), dtype, _ptr(dt), _ptr(T), _ptr(K), _ptr(P),
+                                             B, k, V, int(seed), int(offset), _ptr(tokens), _ptr(acc), _ptr(lp),
+                                             _ptr(al), _ptr(diag), _ptr(fl), int(num_threads))
+            tr = ap = None
+        else:
+            a = None if alt is None else np.ascontiguousarray(np.asarray(alt, dtype=np.int32).reshape(B, 4))
+            tr = np.zeros((B, 2 * k + 1, 2), dtype=np.float64)
+            ap = np.zeros((B, k), dtype=np.float64)
+            rc = self.lib.oracle_spec_verify_ex(_ptr(target), _ptr(draft), dtype, _ptr(dt), _ptr(T), _ptr(K),
+                                                _ptr(P), B, k, V, int(seed), int(offset), _ptr(tokens), _ptr(acc),
+                                                _ptr(lp), _ptr(al), _ptr(diag), _ptr(fl), _ptr(a), _ptr(tr), _ptr(ap),
+                                                int(num_threads))
         if rc != 0:
             raise ValueError("oracle_spec_verify rejected its scalar arguments")
         return VerifyResult(tokens, acc, lp, al, diag[:, 0].copy(), diag[:, 1].copy(), diag[:, 2].copy(),
-                            diag[:, 3].copy(), (fl & 1) != 0, (fl & 2) != 0, (fl >> 8).astype(np.int32))
+                            diag[:, 3].copy(), (fl & 1) != 0, (fl & 2) != 0, (fl >> 8).astype(np.int32), tr, ap)
 
     # -- tree verification ---------------------------------------------------------------
     def tree_verify(self, target, parent, node_tokens, temperature, top_k, top_p, seed: int = 0, offset: int = 0,

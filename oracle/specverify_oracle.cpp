@@ -150,9 +150,16 @@ struct RowDist {
   int32_t kept = 0;       // number of kept entries
   double thr = -kInf;     // smallest kept logit
   double topp_margin = kInf;
+  double topp_at = kInf;    // |M(v)/Z_K - P| at the chosen value v
+  double topp_prev = kInf;  // |M(v')/Z_K - P| at the next larger distinct value v' (+inf if none)
 };
 
-bool row_dist(const std::vector<double>& l, double T, int32_t K, double P, RowDist& d) {
+// topp_shift selects an alternative resolution of the top-p decision, for rows whose decision lies
+// within rounding of the boundary: 0 = the definition; -1 = one distinct value lower than the chosen
+// one (as if M(v) had fallen just short of P Z_K: one more value kept); +1 = the next larger distinct
+// value (as if M(v') had reached P Z_K: one value fewer kept).  Either is a no-op where no such value
+// exists.
+bool row_dist(const std::vector<double>& l, double T, int32_t K, double P, RowDist& d, int topp_shift = 0) {
   const int32_t V = (int32_t)l.size();
   d.p.assign((size_t)V, 0.0);
   d.m = -kInf;
@@ -213,7 +220,7 @@ bool row_dist(const std::vector<double>& l, double T, int32_t K, double P, RowDi
     });
     const double target = P * ZK;
     double M = 0.0, prevM = -1.0;
-    double chosen = -kInf;
+    double chosen = -kInf, prevv = -kInf;
     size_t i = 0;
     while (i < kv.size()) {
       const double v = kv[i].first;
@@ -230,11 +237,18 @@ bool row_dist(const std::vector<double>& l, double T, int32_t K, double P, RowDi
         break;
       }
       prevM = M;
+      prevv = v;
     }
     if (chosen == -kInf && !kv.empty()) chosen = kv.back().first;  // unreachable for P < 1
-    double margin = std::fabs(M / ZK - P);
-    if (prevM >= 0.0) margin = std::min(margin, std::fabs(prevM / ZK - P));
-    d.topp_margin = margin;
+    d.topp_at = std::fabs(M / ZK - P);
+    d.topp_prev = prevM >= 0.0 ? std::fabs(prevM / ZK - P) : kInf;
+#if ORACLE_MUTANT == 28
+    d.topp_margin = d.topp_at;  // MUTANT 28: the next larger value's distance is left out
+#else
+    d.topp_margin = std::min(d.topp_at, d.topp_prev);
+#endif
+    if (topp_shift < 0 && i < kv.size()) chosen = kv[i].first;  // the next lower distinct value
+    if (topp_shift > 0 && prevv > -kInf) chosen = prevv;        // the next larger distinct value
     thr = std::max(thr, chosen);
   }
 
@@ -260,11 +274,13 @@ bool row_dist(const std::vector<double>& l, double T, int32_t K, double P, RowDi
 }
 
 // Gumbel-max over a weight vector w (entries <= 0 are excluded): argmax of ln w(x) + G(x),
-// lowest index on exact key ties (R13).  Returns the index and the top-2 key gap.
+// lowest index on exact key ties (R13).  Returns the index and the top-2 key gap (natural-log key
+// units).  runner_up = true returns the index of the second-largest key instead (an alternative
+// resolution of a draw whose gap lies within rounding); the winner if there is no second candidate.
 int32_t gumbel_argmax(const std::vector<double>& w, uint64_t seed, uint32_t tag, uint32_t b, uint32_t j,
-                      uint32_t offset, double* gap) {
+                      uint32_t offset, double* gap, bool runner_up = false) {
   double best = -kInf, second = -kInf;
-  int32_t y = -1;
+  int32_t y = -1, y2 = -1;
   for (size_t x = 0; x < w.size(); ++x) {
     if (!(w[x] > 0.0)) continue;
 #if ORACLE_MUTANT == 8
@@ -274,13 +290,22 @@ int32_t gumbel_argmax(const std::vector<double>& w, uint64_t seed, uint32_t tag,
 #endif
     if (key > best) {
       second = best;
+      y2 = y;
       best = key;
       y = (int32_t)x;
     } else if (key > second) {
       second = key;
+      y2 = (int32_t)x;
     }
   }
+#if ORACLE_MUTANT == 27
+  *gap = (second == -kInf) ? kInf : std::exp(best) - std::exp(second);  // MUTANT 27: gap of the exp'd keys
+#else
   *gap = (second == -kInf) ? kInf : best - second;
+#endif
+#if ORACLE_MUTANT != 29
+  if (runner_up && y2 >= 0) return y2;  // MUTANT 29 ignores the runner-up request
+#endif
   return y;
 }
 
@@ -304,6 +329,9 @@ struct VerifyArgs {
   double* alpha;
   double* diag;
   int32_t* dflags;
+  const int32_t* alt;   // [B][4] alternative resolutions, or NULL (see oracle_spec_verify_ex)
+  double* topp_rows;    // [B][2k+1][2] per-row top-p distances, or NULL
+  double* accept_pos;   // [B][k] per-position accept distances, or NULL
 };
 
 void write_sentinel(const VerifyArgs& a, int32_t b) {
@@ -317,10 +345,20 @@ void write_sentinel(const VerifyArgs& a, int32_t b) {
   if (a.diag)
     for (int j = 0; j < 4; ++j) a.diag[(size_t)b * 4 + j] = kInf;
   if (a.dflags) a.dflags[b] = 2;
+  if (a.topp_rows)
+    for (int32_t j = 0; j < 2 * (2 * k + 1); ++j) a.topp_rows[(size_t)b * 2 * (2 * k + 1) + j] = kInf;
+  if (a.accept_pos)
+    for (int32_t i = 0; i < k; ++i) a.accept_pos[(size_t)b * k + i] = kInf;
 }
 
 void verify_row(const VerifyArgs& a, int32_t b) {
   const int32_t k = a.k, V = a.V;
+  // alternative resolutions of this row's near-boundary decisions (all zero: the definition)
+  const int32_t* alt = a.alt ? a.alt + (size_t)b * 4 : nullptr;
+  const uint32_t topp_down = alt ? (uint32_t)alt[0] : 0u, topp_up = alt ? (uint32_t)alt[1] : 0u;
+  const uint32_t flips = alt ? ((uint32_t)alt[2] & 0xffffu) : 0u;
+  const bool runner_up = alt ? (((uint32_t)alt[2] >> 16) & 1u) != 0 : false;
+  auto shift_of = [&](int32_t r) { return ((topp_down >> r) & 1u) ? -1 : (((topp_up >> r) & 1u) ? 1 : 0); };
   const float Tf = a.temperature[b];
   const int32_t K = a.top_k[b];
   const float Pf = a.top_p[b];
@@ -338,14 +376,25 @@ void verify_row(const VerifyArgs& a, int32_t b) {
   double topp_margin = kInf;
   for (int32_t i = 0; i <= k; ++i) {
     load_row(a.target, a.dtype, (size_t)b * (k + 1) + i, V, l);
-    if (row_has_nan_or_posinf(l) || !row_dist(l, T, K, P, p[(size_t)i])) return write_sentinel(a, b);
+    if (row_has_nan_or_posinf(l) || !row_dist(l, T, K, P, p[(size_t)i], shift_of(i))) return write_sentinel(a, b);
     topp_margin = std::min(topp_margin, p[(size_t)i].topp_margin);
   }
   for (int32_t i = 0; i < k; ++i) {
     load_row(a.draft, a.dtype, (size_t)b * k + i, V, l);
-    if (row_has_nan_or_posinf(l) || !row_dist(l, T, K, P, q[(size_t)i])) return write_sentinel(a, b);
+    if (row_has_nan_or_posinf(l) || !row_dist(l, T, K, P, q[(size_t)i], shift_of(k + 1 + i)))
+      return write_sentinel(a, b);
     topp_margin = std::min(topp_margin, q[(size_t)i].topp_margin);
   }
+  if (a.topp_rows) {  // logit row r: targets 0..k, then drafts
+    double* tr = a.topp_rows + (size_t)b * 2 * (2 * k + 1);
+    for (int32_t r = 0; r <= 2 * k; ++r) {
+      const RowDist& d = r <= k ? p[(size_t)r] : q[(size_t)(r - k - 1)];
+      tr[2 * r] = d.topp_at;
+      tr[2 * r + 1] = d.topp_prev;
+    }
+  }
+  if (a.accept_pos)
+    for (int32_t i = 0; i < k; ++i) a.accept_pos[(size_t)b * k + i] = kInf;
 
   // Chain rejection: accept draft x_i while the target allows it and u_i < p_i(x_i) / q_i(x_i);
   // a draft outside q's support is accepted whenever p_i(x_i) > 0 (R5).  Greedy rows reduce to
@@ -358,16 +407,29 @@ void verify_row(const VerifyArgs& a, int32_t b) {
     const double qd = q[(size_t)i].p[(size_t)x];
     const double u = accept_uniform(a.seed, (uint32_t)b, (uint32_t)i, a.offset);
 #if ORACLE_MUTANT == 1
-    const bool accept = qd > 0.0 && (pt == 0.0 || u < qd / pt);  // MUTANT 1: p and q swapped
+    bool accept = qd > 0.0 && (pt == 0.0 || u < qd / pt);  // MUTANT 1: p and q swapped
 #else
-    const bool accept = pt > 0.0 && (qd == 0.0 || u < pt / qd);
+    bool accept = pt > 0.0 && (qd == 0.0 || u < pt / qd);
 #endif
-    if (T != 0.0 && pt > 0.0 && qd > 0.0) accept_margin = std::min(accept_margin, std::fabs(u - pt / qd));
+    if ((flips >> i) & 1u) accept = !accept;  // alternative resolution of a near-boundary test
+    if (T != 0.0 && pt > 0.0 && qd > 0.0) {
+      const double dist = std::fabs(u - pt / qd);
+      accept_margin = std::min(accept_margin, dist);
+      if (a.accept_pos) a.accept_pos[(size_t)b * k + i] = dist;
+    }
     if (!accept) {
       n = i;
       break;
     }
   }
+#if ORACLE_MUTANT == 26
+  for (int32_t i = n + 1; i < k; ++i) {  // MUTANT 26: tests past the first rejection count as well
+    const int32_t x = a.draft_tokens[(size_t)b * k + i];
+    const double pt = p[(size_t)i].p[(size_t)x], qd = q[(size_t)i].p[(size_t)x];
+    const double u = accept_uniform(a.seed, (uint32_t)b, (uint32_t)i, a.offset);
+    if (T != 0.0 && pt > 0.0 && qd > 0.0) accept_margin = std::min(accept_margin, std::fabs(u - pt / qd));
+  }
+#endif
 
   // The committed extra token: residual normalize(max(p_n - q_n, 0)) after a rejection,
   // the bonus from p_k when every draft is accepted.  Drawn by Gumbel-max (verify stream).
@@ -402,7 +464,7 @@ void verify_row(const VerifyArgs& a, int32_t b) {
       w = p[(size_t)k].p;
 #endif
     }
-    y = gumbel_argmax(w, a.seed, 1u, (uint32_t)b, (uint32_t)n, a.offset, &gap);
+    y = gumbel_argmax(w, a.seed, 1u, (uint32_t)b, (uint32_t)n, a.offset, &gap, runner_up);
   }
 
   // Outputs (R8, R9, R10, R11).
@@ -649,6 +711,8 @@ int oracle_row_probs(const double* logits, int32_t V, double T, int32_t K, doubl
     info[3] = (double)d.kept;
     info[4] = d.thr;
     info[5] = d.topp_margin;
+    info[6] = d.topp_at;
+    info[7] = d.topp_prev;
   }
   return 0;
 }
@@ -661,8 +725,28 @@ int oracle_spec_verify(const void* target_logits, const void* draft_logits, int3
   if (B < 1 || k < 1 || V < 1 || offset >= (1ull << 32)) return 1;
   if (dtype != ORACLE_DTYPE_BF16 && dtype != ORACLE_DTYPE_F32) return 1;
   VerifyArgs a{target_logits, draft_logits, dtype, draft_tokens, temperature, top_k, top_p, B, k, V,
-               seed, (uint32_t)offset, tokens, accept_len, logprobs, alpha, diag, dflags};
+               seed, (uint32_t)offset, tokens, accept_len, logprobs, alpha, diag, dflags, nullptr, nullptr,
+               nullptr};
   parallel_rows(B, num_threads, [&](int32_t b) { verify_row(a, b); });
+  return 0;
+}
+
+int oracle_spec_verify_ex(const void* target_logits, const void* draft_logits, int32_t dtype,
+                          const int32_t* draft_tokens, const float* temperature, const int32_t* top_k,
+                          const float* top_p, int32_t B, int32_t k, int32_t V, uint64_t seed, uint64_t offset,
+                          int32_t* tokens, int32_t* accept_len, double* logprobs, double* alpha, double* diag,
+                          int32_t* dflags, const int32_t* alt, double* topp_rows, double* accept_pos,
+                          int32_t num_threads) {
+  if (B < 1 || k < 1 || V < 1 || offset >= (1ull << 32)) return 1;
+  if (dtype != ORACLE_DTYPE_BF16 && dtype != ORACLE_DTYPE_F32) return 1;
+  VerifyArgs a{target_logits, draft_logits, dtype, draft_tokens, temperature, top_k, top_p, B, k, V,
+               seed, (uint32_t)offset, tokens, accept_len, logprobs, alpha, diag, dflags, alt, topp_rows,
+               accept_pos};
+  std::vector<int32_t> rows;  // with alternatives: only the rows asked for
+  for (int32_t b = 0; b < B; ++b)
+    if (!alt || alt[(size_t)b * 4 + 3] != 0) rows.push_back(b);
+  if (rows.empty()) return 0;
+  parallel_rows((int32_t)rows.size(), num_threads, [&](int32_t j) { verify_row(a, rows[(size_t)j]); });
   return 0;
 }
 

@@ -54,11 +54,12 @@ double oracle_gumbel_uniform(uint64_t seed, uint32_t tag, uint32_t b, uint32_t j
  *   K      : top-k; 0 or >= V = off
  *   P      : top-p; >= 1 = off
  *   probs  : out, V doubles, the distribution (zeros outside the kept set)
- *   info   : out (may be NULL), 6 doubles:
+ *   info   : out (may be NULL), 8 doubles:
  *            [0] row max m, [1] lowest argmax, [2] kept-set normaliser Z (sum of exp((l-m)/T) over kept),
  *            [3] number of kept entries, [4] kept threshold value (smallest kept logit),
  *            [5] top-p decision margin (min distance of M(v)/Z_K to P at the chosen value and the next
- *                larger distinct value; +inf if top-p is off or T == 0)
+ *                larger distinct value; +inf if top-p is off or T == 0),
+ *            [6] the distance at the chosen value, [7] the distance at the next larger distinct value
  * Returns 0 on success, nonzero if the row is invalid (all -inf).
  */
 int oracle_row_probs(const double* logits, int32_t V, double T, int32_t K, double P, double* probs, double* info);
@@ -87,6 +88,29 @@ int oracle_spec_verify(const void* target_logits, const void* draft_logits, int3
                        const float* top_p, int32_t B, int32_t k, int32_t V, uint64_t seed, uint64_t offset,
                        int32_t* tokens, int32_t* accept_len, double* logprobs, double* alpha, double* diag,
                        int32_t* dflags, int32_t num_threads);
+
+/*
+ * The verify step with per-decision diagnostics and alternative resolutions, for the parity check of
+ * rows whose outcome a correct rounding could change (the margin rows).  Arguments as in
+ * oracle_spec_verify, plus (each may be NULL):
+ *   alt [B, 4]: row b is computed only if alt[b][3] != 0 (other rows' outputs are left untouched);
+ *               alt[b][0] bit r: logit row r (targets 0..k, then drafts k+1..2k) keeps one more distinct
+ *               value than its top-p threshold (as if M(v) had fallen just short of P Z_K);
+ *               alt[b][1] bit r: logit row r's top-p threshold moves to the next larger distinct value
+ *               (as if that value's M had reached P Z_K);
+ *               alt[b][2] bits 0..k-1: the accept test at that position is decided the other way;
+ *               alt[b][2] bit 16: the draw takes the runner-up of the Gumbel race.
+ *   topp_rows [B, 2k+1, 2] out: per logit row, |M(v)/Z_K - P| at the chosen top-p value and at the next
+ *               larger distinct value (+inf where top-p is off, T == 0, or no such value).
+ *   accept_pos [B, k] out: |u_i - p_i(x_i)/q_i(x_i)| for each evaluated accept test with p, q > 0 and
+ *               T > 0 (+inf for tests not evaluated).
+ */
+int oracle_spec_verify_ex(const void* target_logits, const void* draft_logits, int32_t dtype,
+                          const int32_t* draft_tokens, const float* temperature, const int32_t* top_k,
+                          const float* top_p, int32_t B, int32_t k, int32_t V, uint64_t seed, uint64_t offset,
+                          int32_t* tokens, int32_t* accept_len, double* logprobs, double* alpha, double* diag,
+                          int32_t* dflags, const int32_t* alt, double* topp_rows, double* accept_pos,
+                          int32_t num_threads);
 
 /*
  * Plain (non-speculative) sampler over R independent logit rows [R, V]: Gumbel-max over the

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 
 SPEC_DTYPE_BF16 = 0
 SPEC_DTYPE_F32 = 1
-SPEC_NUM_KERNELS = 3  # kernels per call: 0 = slice statistics, 1 = row merges / thresholds, 2 = accept chain / draws
+SPEC_MAX_KERNELS = 3  # kernels one call launches at most (spec_timing_t.kernels says how many it did)
 STATUS = {0: "SPEC_OK", 1: "SPEC_ERR_INVALID_ARGUMENT", 2: "SPEC_ERR_WORKSPACE",
           3: "SPEC_ERR_UNSUPPORTED_DEVICE", 4: "SPEC_ERR_LAUNCH"}
 
@@ -28,6 +28,11 @@ class StateTensor(ctypes.Structure):
     """spec_state_tensor_t: one stateful tensor of the commit step, stacked across layers."""
     _fields_ = [("verify_state", ctypes.c_void_p), ("state_cache", ctypes.c_void_p),
                 ("row_bytes", ctypes.c_int64), ("layers", ctypes.c_int32)]
+
+
+class Timing(ctypes.Structure):
+    """spec_timing_t: per-call kernel timing (events[2j] / events[2j+1] around kernel j)."""
+    _fields_ = [("events", ctypes.POINTER(ctypes.c_void_p)), ("kernels", ctypes.c_int32)]
 
 
 class SpecVerifyError(RuntimeError):
@@ -65,8 +70,12 @@ def lib() -> ctypes.CDLL:
         L.spec_commit.restype = ctypes.c_int
         L.spec_commit_slots.argtypes = [P, P, P, P, P, I32, I32, I32, P]
         L.spec_commit_slots.restype = ctypes.c_int
-        L.spec_set_kernel_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), I32]
-        L.spec_set_kernel_events.restype = ctypes.c_int
+        L.spec_verify_timed.argtypes = [P, P, ctypes.c_int, P, P, P, P, I32, I32, I32, U64, U64, P, P, P, P, P, P,
+                                        SZ, P, ctypes.POINTER(Timing)]
+        L.spec_verify_timed.restype = ctypes.c_int
+        L.spec_tree_verify_timed.argtypes = [P, ctypes.c_int, P, P, P, P, P, I32, I32, I32, U64, U64, P, P, P, P, P,
+                                             SZ, P, ctypes.POINTER(Timing)]
+        L.spec_tree_verify_timed.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -85,7 +94,8 @@ def workspace_size(B: int, k: int, V: int, dtype: int = SPEC_DTYPE_BF16) -> int:
 
 
 def make_workspace(B: int, k: int, V: int, dtype: int = SPEC_DTYPE_BF16, device="cuda"):
-    """A zero-filled device workspace for spec_verify (reusable across calls on one stream)."""
+    """A device workspace for spec_verify (reusable across calls on one stream; it needs no clearing,
+    zero-filled here only so that a fresh one holds no stale bytes)."""
     import torch
     n = workspace_size(B, k, V, dtype)
     if n == 0:
@@ -104,8 +114,24 @@ def alloc_outputs(B: int, k: int, device="cuda", raw: bool = False):
     return out
 
 
+class KernelTiming:
+    """Per-call kernel timing request: 2 * SPEC_MAX_KERNELS raw hipEvent_t handles (ints, created with
+    timing enabled).  Passed as ``timing=`` to spec_verify / spec_tree_verify, it makes the call go through
+    the timed entry point, which records events[2j] / events[2j+1] around kernel j; afterwards ``kernels``
+    holds how many kernels the call launched."""
+
+    def __init__(self, events):
+        if len(events) != 2 * SPEC_MAX_KERNELS:
+            raise ValueError(f"events: {2 * SPEC_MAX_KERNELS} hipEvent_t handles")
+        self._arr = (ctypes.c_void_p * len(events))(*events)
+        self.kernels = 0
+
+    def _struct(self):
+        return Timing(ctypes.cast(self._arr, ctypes.POINTER(ctypes.c_void_p)), 0)
+
+
 def spec_verify(target_logits, draft_logits, draft_tokens, temperature, top_k, top_p, seed: int = 0,
-                offset: int = 0, out=None, workspace=None, stream=None, raw: bool = False):
+                offset: int = 0, out=None, workspace=None, stream=None, raw: bool = False, timing=None):
     """Run the verify step on device tensors; returns a dict of output tensors.
 
     target_logits [B, k+1, V] and draft_logits [B, k, V] (bf16 or fp32, contiguous, same device),
@@ -113,7 +139,8 @@ def spec_verify(target_logits, draft_logits, draft_tokens, temperature, top_k, t
     ``out`` (from alloc_outputs) and ``workspace`` (from make_workspace) may be passed in to
     avoid allocations; ``stream`` defaults to torch's current stream.  ``raw=True`` calls
     spec_verify_raw and adds "raw_logprobs" (ln softmax of the unprocessed target logits at each
-    committed token).
+    committed token).  ``timing`` (a KernelTiming) calls spec_verify_timed instead, which also records
+    its events around the call's kernels.
     """
     import torch
     B, k1, V = target_logits.shape
@@ -134,7 +161,11 @@ def spec_verify(target_logits, draft_logits, draft_tokens, temperature, top_k, t
             top_k.data_ptr(), top_p.data_ptr(), B, k, V, int(seed), int(offset), out["tokens"].data_ptr(),
             out["accept_len"].data_ptr(), out["logprobs"].data_ptr())
     tail = (out["alpha"].data_ptr(), workspace.data_ptr(), workspace.numel(), ctypes.c_void_p(stream.cuda_stream))
-    if raw:
+    if timing is not None:
+        t = timing._struct()
+        st = lib().spec_verify_timed(*head, out["raw_logprobs"].data_ptr() if raw else None, *tail, ctypes.byref(t))
+        timing.kernels = int(t.kernels)
+    elif raw:
         st = lib().spec_verify_raw(*head, out["raw_logprobs"].data_ptr(), *tail)
     else:
         st = lib().spec_verify(*head, *tail)
@@ -177,7 +208,7 @@ def tree_workspace_size(B: int, N: int, V: int, dtype: int = SPEC_DTYPE_BF16) ->
 
 
 def spec_tree_verify(target_logits, parent, node_tokens, temperature, top_k, top_p, seed: int = 0, offset: int = 0,
-                     out=None, workspace=None, stream=None):
+                     out=None, workspace=None, stream=None, timing=None):
     """Tree verification on device tensors: target_logits [B, N, V] (bf16 or fp32), parent and node_tokens
     int32 [B, N], temperature float32 [B], top_k int32 [B], top_p float32 [B].  Returns a dict with
     tokens [B, N], path [B, N], accept_len [B] (int32) and logprobs [B, N] (float32)."""
@@ -200,11 +231,16 @@ def spec_tree_verify(target_logits, parent, node_tokens, temperature, top_k, top
         workspace = torch.zeros(n, dtype=torch.uint8, device=dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
-    st = lib().spec_tree_verify(target_logits.data_ptr(), dt, parent.data_ptr(), node_tokens.data_ptr(),
-                                temperature.data_ptr(), top_k.data_ptr(), top_p.data_ptr(), B, N, V, int(seed),
-                                int(offset), out["tokens"].data_ptr(), out["path"].data_ptr(),
-                                out["accept_len"].data_ptr(), out["logprobs"].data_ptr(), workspace.data_ptr(),
-                                workspace.numel(), ctypes.c_void_p(stream.cuda_stream))
+    args = (target_logits.data_ptr(), dt, parent.data_ptr(), node_tokens.data_ptr(), temperature.data_ptr(),
+            top_k.data_ptr(), top_p.data_ptr(), B, N, V, int(seed), int(offset), out["tokens"].data_ptr(),
+            out["path"].data_ptr(), out["accept_len"].data_ptr(), out["logprobs"].data_ptr(), workspace.data_ptr(),
+            workspace.numel(), ctypes.c_void_p(stream.cuda_stream))
+    if timing is not None:
+        t = timing._struct()
+        st = lib().spec_tree_verify_timed(*args, ctypes.byref(t))
+        timing.kernels = int(t.kernels)
+    else:
+        st = lib().spec_tree_verify(*args)
     if st != 0:
         raise SpecVerifyError(st, "spec_tree_verify")
     return out
@@ -271,16 +307,3 @@ def spec_commit_slots(state_slot, pos_slot, accept_len, num_slots: int, seq_len=
     if st != 0:
         raise SpecVerifyError(st, "spec_commit_slots")
     return status
-
-
-def set_kernel_events(events):
-    """Benchmark hook: ``events`` is None (off) or 2 * SPEC_NUM_KERNELS raw hipEvent_t handles (ints).
-
-    While set, every later call records events[2j] / events[2j+1] around its j-th kernel on its stream."""
-    if events is None:
-        st = lib().spec_set_kernel_events(None, 0)
-    else:
-        arr = (ctypes.c_void_p * len(events))(*events)
-        st = lib().spec_set_kernel_events(arr, len(events))
-    if st != 0:
-        raise SpecVerifyError(st, "spec_set_kernel_events")

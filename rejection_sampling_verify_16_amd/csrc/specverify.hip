@@ -64,7 +64,7 @@ constexpr int WF = 2048;        // widest exact code window of the whole-row pas
 constexpr int MAXS1 = 64;       // slices per bf16 row at the largest V
 constexpr int MB = 8;           // merge: slices whose histogram words are loaded in one round trip
 constexpr int HCW = NBC / 2 + 1;  // words per slice of packed bin counts + the slice's base bin
-constexpr int NKERN = 3;        // kernels per call
+constexpr int NKERN = SPEC_MAX_KERNELS;  // kernels per call at most
 
 constexpr int WC = 64;          // K1: candidate window (codes below the slice max) of truncated rows
 constexpr int NC = 192;         // K1: candidates recorded per slice at most
@@ -1505,6 +1505,9 @@ __global__ __launch_bounds__(NT) void k1_rows(Params p) {
   const int r = blockIdx.x;
   const int b = r / p.rows, i = r - b * p.rows;
   const RowParams q = row_params(p, b);
+  // Re-arm the batch row's arrival counter of the next kernel (K5 or the tree kernel): this kernel ends
+  // before that one starts, so every call starts from zero whatever the workspace held.
+  if (i == 0 && threadIdx.x == 0) p.cnt5[b] = 0u;
   SV_TRACE_AT(p, (size_t)r * p.S1, 3);
   k1_merge<E, RAW>(p, sm, r, b, i, q);
   SV_TRACE_AT(p, (size_t)r * p.S1, 7);
@@ -2135,7 +2138,6 @@ __device__ __forceinline__ void k5_item(const Params& p, K5Smem& sm, int item, i
   if (arrive_last(&p.cnt5[b], (uint32_t)p.S5, &sm.rs.flag)) {
     SV_TRACE5_AT(p, item, 5);
     k5_finalize<E>(p, sm, b, ok, q);
-    if (tid == 0) atomicExch(&p.cnt5[b], 0u);
     SV_TRACE5_AT(p, item, 6);
   }
   SV_TRACE5_AT(p, item, 7);
@@ -2369,7 +2371,6 @@ __global__ __launch_bounds__(NT) void k_tree(Params p) {
     tree_sentinel(p, b);  // no candidate: not reachable for a valid row
   else
     tree_emit(p, sm, b, q, bidx, bval);
-  if (tid == 0) atomicExch(&p.cnt5[b], 0u);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -2389,11 +2390,11 @@ static bool make_geo(int32_t B, int32_t k, int32_t V, spec_dtype_t dtype, Geo& g
     if (tree_nodes > MAXN) return false;
     k = 0;
   }
-  if (B < 1 || B > (1 << 20) || k < 0 || k > MAXK || V < 8 || V > (1 << 20)) return false;
+  if (B < 1 || B > (1 << 20) || k < 0 || k > MAXK || V < 1 || V > (1 << 20)) return false;
   if (dtype != SPEC_DTYPE_BF16 && dtype != SPEC_DTYPE_F32) return false;
   g.esize = dtype == SPEC_DTYPE_BF16 ? 2 : 4;
   g.EPV = 16 / g.esize;
-  if (V % g.EPV != 0) return false;
+  if (V % g.EPV != 0) return false;  // whole 16-byte vectors per row: V >= 8 (bf16) or V >= 4 (fp32)
   g.rows = tree_nodes > 0 ? tree_nodes : 2 * k + 1;
   if ((long long)B * g.rows > (1 << 24)) return false;  // item counts stay below 2^31
   g.R = B * g.rows;
@@ -2428,7 +2429,6 @@ struct DevInfo {
 };
 static DevInfo g_dev[MAXDEV];
 static std::mutex g_mu;
-static hipEvent_t g_prof[2 * NKERN];  // benchmark hook: events around each kernel (all null: off)
 
 bool device_ok(int dev, int& cus) {
   if (dev < 0 || dev >= MAXDEV) return false;
@@ -2443,41 +2443,47 @@ bool device_ok(int dev, int& cus) {
   return g_dev[dev].state == 1;
 }
 
-static void prof_mark(int idx, hipStream_t st) {
-  if (g_prof[idx]) (void)hipEventRecord(g_prof[idx], st);
+// Per-call kernel timing (the timed entry points): events[2j] / events[2j+1] around kernel j.
+struct Timing {
+  hipEvent_t ev[2 * NKERN];
+  int used;
+};
+static void prof_mark(Timing* t, int idx, hipStream_t st) {
+  if (t && t->ev[idx]) (void)hipEventRecord(t->ev[idx], st);
 }
 
 template <class E>
-static void enqueue(const Params& p, int cus, hipStream_t st) {
+static void enqueue(const Params& p, int cus, hipStream_t st, Timing* tm) {
   static_assert(WTOP / 2 == NT && NBC == NT, "K1 assumes one histogram word pair per thread");
   static_assert((NCOPY & (NCOPY - 1)) == 0 && NCOPY <= 64, "weight-bin copies: a power of two");
   (void)cus;
   const dim3 g1((unsigned)(p.R * p.S1)), gr((unsigned)p.R), g5((unsigned)(p.B * p.S5));
   const bool raw = p.raw_logprobs != nullptr;
-  prof_mark(0, st);
+  prof_mark(tm, 0, st);
   if (raw)
     hipLaunchKernelGGL((k1_stats<E, VPT1, true>), g1, dim3(NT), 0, st, p);
   else
     hipLaunchKernelGGL((k1_stats<E, VPT1, false>), g1, dim3(NT), 0, st, p);
-  prof_mark(1, st);
-  prof_mark(2, st);
+  prof_mark(tm, 1, st);
+  prof_mark(tm, 2, st);
   if (raw)
     hipLaunchKernelGGL((k1_rows<E, true>), gr, dim3(NT), 0, st, p);
   else
     hipLaunchKernelGGL((k1_rows<E, false>), gr, dim3(NT), 0, st, p);
-  prof_mark(3, st);
-  prof_mark(4, st);
+  prof_mark(tm, 3, st);
+  prof_mark(tm, 4, st);
   if (p.mode == MODE_TREE)
     hipLaunchKernelGGL((k_tree<E, VPT5>), g5, dim3(NT), 0, st, p);
   else if (raw)
     hipLaunchKernelGGL((k5_verify<E, VPT5, true>), g5, dim3(NT), 0, st, p);
   else
     hipLaunchKernelGGL((k5_verify<E, VPT5, false>), g5, dim3(NT), 0, st, p);
-  prof_mark(5, st);
+  prof_mark(tm, 5, st);
+  if (tm) tm->used = NKERN;
 }
 
 static spec_status_t launch(Params& p, const Geo& g, spec_dtype_t dtype, void* workspace, size_t workspace_bytes,
-                            void* stream) {
+                            void* stream, Timing* tm = nullptr) {
   if (!workspace || workspace_bytes < g.total || ((uintptr_t)workspace & 15)) return SPEC_ERR_WORKSPACE;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || !device_ok(dev, cus)) return SPEC_ERR_UNSUPPORTED_DEVICE;
@@ -2499,9 +2505,9 @@ static spec_status_t launch(Params& p, const Geo& g, spec_dtype_t dtype, void* w
   p.trace = TRACE_SLOTS > 0 ? (unsigned long long*)(ws + g.off_trace) : nullptr;
   p.trace5 = TRACE_SLOTS > 0 ? (unsigned long long*)(ws + g.off_trace5) : nullptr;
   if (dtype == SPEC_DTYPE_BF16)
-    enqueue<BF16>(p, cus, (hipStream_t)stream);
+    enqueue<BF16>(p, cus, (hipStream_t)stream, tm);
   else
-    enqueue<F32>(p, cus, (hipStream_t)stream);
+    enqueue<F32>(p, cus, (hipStream_t)stream, tm);
   if (hipGetLastError() != hipSuccess) return SPEC_ERR_LAUNCH;
   return SPEC_OK;
 }
@@ -2531,7 +2537,7 @@ static spec_status_t verify_impl(const void* target_logits, const void* draft_lo
                                  const int32_t* draft_tokens, const float* temperature, const int32_t* top_k,
                                  const float* top_p, int32_t B, int32_t k, int32_t V, uint64_t seed, uint64_t offset,
                                  int32_t* tokens, int32_t* accept_len, float* logprobs, float* raw_logprobs,
-                                 float* alpha, void* workspace, size_t workspace_bytes, void* stream) {
+                                 float* alpha, void* workspace, size_t workspace_bytes, void* stream, Timing* tm) {
   Geo g;
   if (k < 1 || !make_geo(B, k, V, dtype, g)) return SPEC_ERR_INVALID_ARGUMENT;
   if (offset >= (1ull << 32)) return SPEC_ERR_INVALID_ARGUMENT;
@@ -2559,7 +2565,7 @@ static spec_status_t verify_impl(const void* target_logits, const void* draft_lo
   p.logprobs = logprobs;
   p.raw_logprobs = raw_logprobs;
   p.alpha = alpha;
-  return launch(p, g, dtype, workspace, workspace_bytes, stream);
+  return launch(p, g, dtype, workspace, workspace_bytes, stream, tm);
 }
 
 extern "C" spec_status_t spec_verify(const void* target_logits, const void* draft_logits, spec_dtype_t dtype,
@@ -2568,7 +2574,7 @@ extern "C" spec_status_t spec_verify(const void* target_logits, const void* draf
                                      uint64_t offset, int32_t* tokens, int32_t* accept_len, float* logprobs,
                                      float* alpha, void* workspace, size_t workspace_bytes, void* stream) {
   return verify_impl(target_logits, draft_logits, dtype, draft_tokens, temperature, top_k, top_p, B, k, V, seed,
-                     offset, tokens, accept_len, logprobs, nullptr, alpha, workspace, workspace_bytes, stream);
+                     offset, tokens, accept_len, logprobs, nullptr, alpha, workspace, workspace_bytes, stream, nullptr);
 }
 
 extern "C" spec_status_t spec_verify_raw(const void* target_logits, const void* draft_logits, spec_dtype_t dtype,
@@ -2579,7 +2585,31 @@ extern "C" spec_status_t spec_verify_raw(const void* target_logits, const void* 
                                          void* stream) {
   if (!raw_logprobs) return SPEC_ERR_INVALID_ARGUMENT;
   return verify_impl(target_logits, draft_logits, dtype, draft_tokens, temperature, top_k, top_p, B, k, V, seed,
-                     offset, tokens, accept_len, logprobs, raw_logprobs, alpha, workspace, workspace_bytes, stream);
+                     offset, tokens, accept_len, logprobs, raw_logprobs, alpha, workspace, workspace_bytes, stream,
+                     nullptr);
+}
+
+// Copies the caller's events into a per-call Timing (nothing outlives the call).
+static bool timing_in(const spec_timing_t* t, Timing& tm) {
+  if (!t || !t->events) return false;
+  for (int j = 0; j < 2 * NKERN; ++j) tm.ev[j] = (hipEvent_t)t->events[j];
+  tm.used = 0;
+  return true;
+}
+
+extern "C" spec_status_t spec_verify_timed(const void* target_logits, const void* draft_logits, spec_dtype_t dtype,
+                                           const int32_t* draft_tokens, const float* temperature,
+                                           const int32_t* top_k, const float* top_p, int32_t B, int32_t k, int32_t V,
+                                           uint64_t seed, uint64_t offset, int32_t* tokens, int32_t* accept_len,
+                                           float* logprobs, float* raw_logprobs, float* alpha, void* workspace,
+                                           size_t workspace_bytes, void* stream, spec_timing_t* timing) {
+  Timing tm;
+  if (!timing_in(timing, tm)) return SPEC_ERR_INVALID_ARGUMENT;
+  const spec_status_t st =
+      verify_impl(target_logits, draft_logits, dtype, draft_tokens, temperature, top_k, top_p, B, k, V, seed, offset,
+                  tokens, accept_len, logprobs, raw_logprobs, alpha, workspace, workspace_bytes, stream, &tm);
+  timing->kernels = tm.used;
+  return st;
 }
 
 extern "C" size_t spec_sample_workspace_size(int32_t R, int32_t V, spec_dtype_t dtype) {
@@ -2625,11 +2655,11 @@ extern "C" size_t spec_tree_verify_workspace_size(int32_t B, int32_t N, int32_t 
   return g.total;
 }
 
-extern "C" spec_status_t spec_tree_verify(const void* target_logits, spec_dtype_t dtype, const int32_t* parent,
-                                          const int32_t* node_tokens, const float* temperature, const int32_t* top_k,
-                                          const float* top_p, int32_t B, int32_t N, int32_t V, uint64_t seed,
-                                          uint64_t offset, int32_t* tokens, int32_t* path, int32_t* accept_len,
-                                          float* logprobs, void* workspace, size_t workspace_bytes, void* stream) {
+static spec_status_t tree_impl(const void* target_logits, spec_dtype_t dtype, const int32_t* parent,
+                               const int32_t* node_tokens, const float* temperature, const int32_t* top_k,
+                               const float* top_p, int32_t B, int32_t N, int32_t V, uint64_t seed, uint64_t offset,
+                               int32_t* tokens, int32_t* path, int32_t* accept_len, float* logprobs, void* workspace,
+                               size_t workspace_bytes, void* stream, Timing* tm) {
   Geo g;
   if (N < 1 || !make_geo(B, 0, V, dtype, g, N)) return SPEC_ERR_INVALID_ARGUMENT;
   if (offset >= (1ull << 32)) return SPEC_ERR_INVALID_ARGUMENT;
@@ -2657,15 +2687,29 @@ extern "C" spec_status_t spec_tree_verify(const void* target_logits, spec_dtype_
   p.tokens = tokens;
   p.accept_len = accept_len;
   p.logprobs = logprobs;
-  return launch(p, g, dtype, workspace, workspace_bytes, stream);
+  return launch(p, g, dtype, workspace, workspace_bytes, stream, tm);
 }
 
-extern "C" spec_status_t spec_set_kernel_events(void* const* events, int32_t count) {
-  if (events == nullptr) {
-    for (auto& e : g_prof) e = nullptr;
-    return SPEC_OK;
-  }
-  if (count != 2 * NKERN) return SPEC_ERR_INVALID_ARGUMENT;
-  for (int j = 0; j < 2 * NKERN; ++j) g_prof[j] = (hipEvent_t)events[j];
-  return SPEC_OK;
+extern "C" spec_status_t spec_tree_verify(const void* target_logits, spec_dtype_t dtype, const int32_t* parent,
+                                          const int32_t* node_tokens, const float* temperature, const int32_t* top_k,
+                                          const float* top_p, int32_t B, int32_t N, int32_t V, uint64_t seed,
+                                          uint64_t offset, int32_t* tokens, int32_t* path, int32_t* accept_len,
+                                          float* logprobs, void* workspace, size_t workspace_bytes, void* stream) {
+  return tree_impl(target_logits, dtype, parent, node_tokens, temperature, top_k, top_p, B, N, V, seed, offset, tokens,
+                   path, accept_len, logprobs, workspace, workspace_bytes, stream, nullptr);
+}
+
+extern "C" spec_status_t spec_tree_verify_timed(const void* target_logits, spec_dtype_t dtype, const int32_t* parent,
+                                                const int32_t* node_tokens, const float* temperature,
+                                                const int32_t* top_k, const float* top_p, int32_t B, int32_t N,
+                                                int32_t V, uint64_t seed, uint64_t offset, int32_t* tokens,
+                                                int32_t* path, int32_t* accept_len, float* logprobs, void* workspace,
+                                                size_t workspace_bytes, void* stream, spec_timing_t* timing) {
+  Timing tm;
+  if (!timing_in(timing, tm)) return SPEC_ERR_INVALID_ARGUMENT;
+  const spec_status_t st = tree_impl(target_logits, dtype, parent, node_tokens, temperature, top_k, top_p, B, N, V,
+                                     seed, offset, tokens, path, accept_len, logprobs, workspace, workspace_bytes,
+                                     stream, &tm);
+  timing->kernels = tm.used;
+  return st;
 }

@@ -182,6 +182,24 @@ def pin_off_switches(o):
         assert g[int(np.argmax(l))] == 1.0
 
 
+def pin_topp_margin_golden(o):
+    """The top-p decision distances against hand-worked rows (tests/golden/topp_margin_cases.txt): at the
+    chosen value, at the next larger distinct value, after top-k renormalisation, with ties kept whole,
+    under a temperature, and off."""
+    for line in read_golden_table("topp_margin_cases.txt"):
+        name, logits, T, K, P, at, prev = [t.strip() for t in line.split("|")]
+        l = [_parse_num(t) for t in logits.split()]
+        _, info = o.row_probs(l, float(T), int(K), float(P))
+        want = {"topp_at": float(at), "topp_prev": float(prev)}
+        want["topp_margin"] = min(want.values())
+        for key, w in want.items():
+            g = info[key]
+            if math.isinf(w):
+                assert math.isinf(g), (name, key, g)
+            else:
+                assert abs(g - w) <= 1e-12, (name, key, g, w)
+
+
 # ---------------------------------------------------------------------------------------
 # verify step
 # ---------------------------------------------------------------------------------------
@@ -787,6 +805,159 @@ def pin_tree_rules(o):
     # a single node: the token is drawn from the root's distribution
     r1 = o.tree_verify(l[:, :1].copy(), np.zeros((1, 1), np.int32), np.zeros((1, 1), np.int32), *_params(1, 0.0))
     assert r1.accept_len[0] == 1 and r1.tokens[0, 0] == 3
+
+
+# ---------------------------------------------------------------------------------------
+# per-row diagnostics: which rows a correct rounding could change, and how
+# ---------------------------------------------------------------------------------------
+
+def _diag_case(o, seed):
+    """A verify batch whose rows mix untruncated, top-k and top-p parameters (tiny V, fresh drafts), with
+    the textbook distributions of every row: (t, d, drafts, T, K, P, p[B][k+1], q[B][k])."""
+    rng = np.random.default_rng(seed)
+    B, k, V = 240, 3, 12
+    t = rng.normal(0.0, 1.3, size=(B, k + 1, V)).astype(np.float32)
+    d = (t[:, :k] + rng.normal(0.0, 0.8, size=(B, k, V))).astype(np.float32)
+    T = f32(rng.uniform(0.6, 1.4, size=B))
+    K = np.where(rng.random(B) < 0.3, 4, 0).astype(np.int32)
+    P = f32(np.where(rng.random(B) < 0.3, 0.85, 1.0))
+    drafts = _fresh_drafts(o, d, T, K, P)
+    p = [[textbook_topk_topp(t[b, i].astype(np.float64), float(T[b]), int(K[b]), float(P[b])) for i in range(k + 1)]
+         for b in range(B)]
+    q = [[textbook_topk_topp(d[b, i].astype(np.float64), float(T[b]), int(K[b]), float(P[b])) for i in range(k)]
+         for b in range(B)]
+    return t, d, drafts, T, K, P, p, q
+
+
+def _chain(o, seed, offset, b, drafts_b, p_b, q_b, flip=None):
+    """Textbook accept chain of one row: (n, per-position distance |u - p/q| of the evaluated tests)."""
+    k = len(q_b)
+    dist = [math.inf] * k
+    for i in range(k):
+        x = int(drafts_b[i])
+        pt, qd = p_b[i][x], q_b[i][x]
+        u = o.accept_uniform(seed, b, i, offset)
+        acc = pt > 0 and (qd == 0 or u < pt / qd)
+        if flip == i:
+            acc = not acc
+        if pt > 0 and qd > 0:
+            dist[i] = abs(u - pt / qd)
+        if not acc:
+            return i, dist
+    return k, dist
+
+
+def _race(o, seed, offset, b, n, w):
+    """Gumbel race of one row in numpy: keys ln w(x) - ln(-ln U) on the draw stream, sorted descending:
+    [(key, x), ...] over w(x) > 0."""
+    keys = []
+    for x in np.flatnonzero(w > 0):
+        U = o.gumbel_uniform(seed, 1, b, n, int(x), offset)
+        keys.append((math.log(w[x]) - math.log(-math.log(U)), int(x)))
+    return sorted(keys, key=lambda kx: (-kx[0], kx[1]))
+
+
+def pin_accept_margin(o):
+    """accept_margin = min |u_i - p_i(x_i)/q_i(x_i)| over the accept tests the chain evaluates (up to and
+    including the first rejection), recomputed from the accept uniforms and textbook distributions; the
+    per-position distances are +inf past the first rejection."""
+    t, d, drafts, T, K, P, p, q = _diag_case(o, 41)
+    seed, off = 3, 5
+    r = o.spec_verify(t, d, drafts, T, K, P, seed=seed, offset=off, details=True)
+    for b in range(t.shape[0]):
+        n, dist = _chain(o, seed, off, b, drafts[b], p[b], q[b])
+        assert r.n_accepted[b] == n, (b, r.n_accepted[b], n)
+        for i, dv in enumerate(dist):
+            assert (math.isinf(dv) and math.isinf(r.accept_pos[b, i])) or abs(r.accept_pos[b, i] - dv) <= 1e-12, \
+                (b, i, r.accept_pos[b, i], dv)
+        want = min(dist)
+        assert (math.isinf(want) and math.isinf(r.accept_margin[b])) or abs(r.accept_margin[b] - want) <= 1e-12, \
+            (b, r.accept_margin[b], want)
+
+
+def pin_gumbel_gap(o):
+    """gumbel_gap = top-1 minus top-2 key of the draw (natural-log units) over the residual max(p_n - q_n, 0)
+    or the bonus p_k, recomputed from the Gumbel uniforms; the drawn token is the top-1 key."""
+    t, d, drafts, T, K, P, p, q = _diag_case(o, 42)
+    seed, off = 8, 2
+    r = o.spec_verify(t, d, drafts, T, K, P, seed=seed, offset=off)
+    k = d.shape[1]
+    for b in range(t.shape[0]):
+        n = int(r.n_accepted[b])
+        w = np.maximum(p[b][n] - q[b][n], 0.0) if n < k else p[b][k]
+        keys = _race(o, seed, off, b, n, w)
+        assert r.tokens[b, n] == keys[0][1], (b, r.tokens[b, n], keys[0])
+        want = keys[0][0] - keys[1][0] if len(keys) > 1 else math.inf
+        assert (math.isinf(want) and math.isinf(r.gumbel_gap[b])) or abs(r.gumbel_gap[b] - want) <= 1e-9, \
+            (b, r.gumbel_gap[b], want)
+
+
+def pin_topp_rows(o):
+    """Per-row top-p distances inside the verify step equal the hand-worked ones: one batch row whose target
+    rows and draft row have cumulative masses 0.5, 0.8, 0.95, 1 (and 0.4, 1 with ties), top-p 0.799999
+    (float32), so the distances are |0.8 - P| or |0.5 - P| and the row's margin is their minimum."""
+    probs = [np.log([0.5, 0.3, 0.15, 0.05]), np.log([0.3, 0.5, 0.05, 0.15]), np.log([0.4, 0.2, 0.2, 0.2])]
+    t = np.stack([probs[0], probs[1]])[None].astype(np.float32)
+    d = probs[2][None, None].astype(np.float32)
+    P = f32([0.799999])
+    r = o.spec_verify(t, d, np.array([[0]], np.int32), f32([1.0]), np.zeros(1, np.int32), P, details=True)
+    Pd = float(P[0])
+    for row, (at, prev) in enumerate([(0.8, 0.5), (0.8, 0.5), (1.0, 0.4)]):
+        lg = (t[0, row] if row < 2 else d[0, 0]).astype(np.float64)
+        e = np.exp(lg - lg.max())
+        cum = np.cumsum(np.sort(e)[::-1]) / e.sum()   # masses of the upper sets, tie-free except row 2
+        if row == 2:
+            cum = np.array([cum[0], cum[-1]])
+        j = int(np.searchsorted(cum, Pd, side="left"))
+        want_at, want_prev = abs(cum[j] - Pd), abs(cum[j - 1] - Pd)
+        assert abs(cum[j] - at) < 1e-6 and abs(cum[j - 1] - prev) < 1e-6
+        np.testing.assert_allclose(r.topp_rows[0, row], [want_at, want_prev], rtol=0, atol=1e-12)
+    assert abs(r.topp_margin[0] - r.topp_rows[0].min()) <= 1e-15
+
+
+def pin_alternative_resolutions(o):
+    """The alternatives the parity check may accept for a margin row are the textbook outcomes of the other
+    resolution: the Gumbel runner-up is the second key of the race; a flipped accept test changes the
+    chain there; a top-p threshold one distinct value lower or higher keeps one value more or fewer."""
+    t, d, drafts, T, K, P, p, q = _diag_case(o, 43)
+    seed, off = 6, 4
+    B, k = d.shape[0], d.shape[1]
+    base = o.spec_verify(t, d, drafts, T, K, P, seed=seed, offset=off)
+    # the runner-up of every row's race
+    alt = np.zeros((B, 4), np.int32)
+    alt[:, 2] = 1 << 16
+    alt[:, 3] = 1
+    r = o.spec_verify(t, d, drafts, T, K, P, seed=seed, offset=off, alt=alt)
+    for b in range(B):
+        n = int(base.n_accepted[b])
+        w = np.maximum(p[b][n] - q[b][n], 0.0) if n < k else p[b][k]
+        keys = _race(o, seed, off, b, n, w)
+        assert r.tokens[b, n] == (keys[1][1] if len(keys) > 1 else keys[0][1]), b
+        assert r.accept_len[b] == base.accept_len[b]
+    # the first accept test decided the other way
+    alt[:, 2] = 1
+    r = o.spec_verify(t, d, drafts, T, K, P, seed=seed, offset=off, alt=alt)
+    for b in range(B):
+        n, _ = _chain(o, seed, off, b, drafts[b], p[b], q[b], flip=0)
+        assert r.n_accepted[b] == n and r.accept_len[b] == n + 1, b
+        np.testing.assert_array_equal(r.tokens[b, :n], drafts[b, :n])
+    # target row 0's top-p threshold one value lower / higher: alpha_0 and the logprob follow the textbook
+    # kept set of one more / one fewer value (rows are tie-free)
+    rows = [b for b in range(B) if P[b] < 1.0]
+    for mask_col, extra in ((0, 1), (1, -1)):
+        alt = np.zeros((B, 4), np.int32)
+        alt[rows, mask_col] = 1
+        alt[rows, 3] = 1
+        r = o.spec_verify(t, d, drafts, T, K, P, seed=seed, offset=off, alt=alt)
+        for b in rows:
+            lg = t[b, 0].astype(np.float64)
+            kept = int((p[b][0] > 0).sum())
+            Kb = int(K[b]) if 0 < K[b] < lg.size else lg.size
+            m = min(max(kept + extra, 1), Kb)
+            order = np.argsort(-lg, kind="stable")
+            pa = np.zeros_like(lg)
+            pa[order[:m]] = softmax_T(lg[order[:m]], float(T[b]))
+            np.testing.assert_allclose(r.alpha[b, 0], np.minimum(pa, q[b][0]).sum(), rtol=0, atol=1e-12)
 
 
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_") and callable(v)]

@@ -48,11 +48,29 @@ def test_workspace_sizes(L):
     assert L.spec_sample_workspace_size(16, 4096, 0) > 0
 
 
-def test_kernel_event_hook_arguments(L):
-    """The benchmark hook checks its count, and NULL turns it off."""
-    assert L.spec_set_kernel_events(None, 0) == 0
-    arr = (ctypes.c_void_p * 3)()
-    assert L.spec_set_kernel_events(arr, 3) == 1
+def test_timed_entry_points_need_their_timing(L):
+    """The timed entry points reject a missing spec_timing_t (or one without events) before any device call,
+    and there is no process-wide timing state to set."""
+    assert not hasattr(L, "spec_set_kernel_events")
+    P = ctypes.c_void_p(16)
+    st = L.spec_verify_timed(P, P, 0, P, P, P, P, 2, 2, 1024, 0, 0, P, P, P, None, P, P, 1 << 30, None, None)
+    assert st == 1
+    t = sv.Timing(None, 0)
+    st = L.spec_verify_timed(P, P, 0, P, P, P, P, 2, 2, 1024, 0, 0, P, P, P, None, P, P, 1 << 30, None,
+                             ctypes.byref(t))
+    assert st == 1
+    st = L.spec_tree_verify_timed(P, 0, P, P, P, P, P, 2, 3, 1024, 0, 0, P, P, P, P, P, 1 << 30, None, None)
+    assert st == 1
+    with pytest.raises(ValueError):
+        sv.KernelTiming([0] * 3)
+
+
+def test_smallest_vocabulary(L):
+    """V needs only whole 16-byte vectors: 8 bf16 or 4 fp32 logits per row."""
+    assert sv.workspace_size(2, 1, 8) > 0
+    assert sv.workspace_size(2, 1, 4, sv.SPEC_DTYPE_F32) > 0
+    assert sv.workspace_size(2, 1, 4) == 0
+    assert L.spec_sample_workspace_size(3, 4, 1) > 0
 
 
 def test_status_strings(L):

@@ -28,8 +28,8 @@ def _check(o, w, offsets, label, drafts=None):
     for off in offsets:
         print(f"[parity] {label} B={w.B} k={w.k} V={w.V} {w.dtype} offset={off}", flush=True)
         g = parity.run_gpu(dev, w.seed, off)
-        r = o.spec_verify(w.target, w.draft, drafts, w.temperature, w.top_k, w.top_p, seed=w.seed, offset=off)
-        rep = parity.compare(g, r, drafts, w.V, label=f"{label}@{off}")
+        r, alt = parity.verify_oracle(o, w.target, w.draft, drafts, w.temperature, w.top_k, w.top_p, w.seed, off)
+        rep = parity.compare(g, r, drafts, w.V, label=f"{label}@{off}", alt=alt)
         print(f"[parity] {label}@{off}: {rep}", flush=True)
         reports.append(rep)
     return reports
@@ -89,6 +89,7 @@ SMALL = [
     ("tiny_topp", 6, 2, 12008, "bf16", dict(temperature=0.9, top_p=0.05)),
     ("f32_greedy", 6, 3, 8192, "f32", dict(temperature=0.0, tie_fraction=0.2)),
     ("min_V", 3, 1, 8, "bf16", dict(temperature=1.0)),
+    ("min_V_f32", 4, 2, 4, "f32", dict(temperature=1.0, mixed_params=True)),
     ("k1_T2", 16, 1, 32768, "bf16", dict(temperature=2.0, top_k=1000, top_p=0.99)),
     # the largest vocabulary: 64 slices per bf16 row (the candidate records' limit), 128 per fp32 row
     ("maxV_bf16_mixed", 4, 2, 1 << 20, "bf16", dict(boost=8.0, mixed_params=True)),
@@ -200,6 +201,29 @@ def test_greedy_rows_among_sampled_rows_and_greedy_sentinels(o):
     assert reps[0]["sentinel"] == 5
 
 
+def test_workspace_needs_no_initialisation(o):
+    """Every call sets up the workspace bytes it reads: a workspace filled with 0xFF before each call (and one
+    left as the previous, different-sized call wrote it) gives the oracle's outputs."""
+    import torch
+    import rejection_sampling_verify_16_amd as sv
+    cases = [W.make(24, 2, 40000, seed=91, boost=8.0, mixed_params=True, name="ws_mixed"),
+             W.make(6, 3, 16384, seed=92, temperature=0.0, tie_fraction=0.3, name="ws_greedy"),
+             W.make(5, 1, 4100, dtype="f32", seed=93, temperature=0.7, top_k=100, top_p=0.9, name="ws_f32")]
+    big = max(sv.workspace_size(w.B, w.k, w.V, sv.SPEC_DTYPE_F32 if w.dtype == "f32" else sv.SPEC_DTYPE_BF16)
+              for w in cases)
+    ws = torch.empty(big, dtype=torch.uint8, device="cuda")
+    for fill in (True, False):
+        for w in cases:
+            if fill:
+                ws.fill_(0xFF)
+            drafts = w.draft_tokens(parity.oracle_sampler(o))
+            dev = parity.device_inputs(w, drafts)
+            print(f"[parity] {w.name} workspace {'0xFF' if fill else 'as left'}", flush=True)
+            g = parity.run_gpu(dev, 4, 6, workspace=ws)
+            r, alt = parity.verify_oracle(o, w.target, w.draft, drafts, w.temperature, w.top_k, w.top_p, 4, 6)
+            parity.compare(g, r, drafts, w.V, label=f"{w.name}/{fill}", alt=alt)
+
+
 def test_gpu_output_marginal_chi2(o):
     """The GPU path's committed first token follows p_0 (1e5 independent batch rows, V = 16)."""
     from scipy import special, stats
@@ -271,8 +295,11 @@ def test_plain_sampler_parity(o, case):
     R = B * k
     logits = dev["draft"].reshape(R, V)
     tt = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).cuda()
+    # a workspace of 0xFF bytes: spec_sample sets up what it reads, as spec_verify does
+    nws = int(sv.lib().spec_sample_workspace_size(R, V, sv.SPEC_DTYPE_F32 if dtype == "f32" else sv.SPEC_DTYPE_BF16))
+    ws = torch.full((nws,), 0xFF, dtype=torch.uint8, device="cuda")
     tok, lp = sv.spec_sample(logits, tt(T, np.float32), tt(K, np.int32), tt(P, np.float32), tt(rb, np.int32),
-                             tt(rp, np.int32), seed=13, offset=4)
+                             tt(rp, np.int32), seed=13, offset=4, workspace=ws)
     torch.cuda.synchronize()
     tok, lp = tok.cpu().numpy(), lp.cpu().numpy()
     strict = gap > parity.GAP_TOL
@@ -292,9 +319,10 @@ RAW_CASES = [
 
 @pytest.mark.parametrize("case", RAW_CASES, ids=[c[0] for c in RAW_CASES])
 def test_raw_logprobs(o, case):
-    """spec_verify_raw: every output of spec_verify unchanged (bit-exact), plus ln softmax of the
-    unprocessed target logits at each committed token, checked against the oracle evaluated at the GPU's
-    own tokens (so margin rows are covered too); NaN in sentinel rows, 0 after the committed slots."""
+    """spec_verify_raw: every output of spec_verify unchanged (bit-exact) and those outputs at parity with
+    the oracle's verify step on the same inputs, seed and offset; plus ln softmax of the unprocessed target
+    logits at each committed token, checked against the oracle evaluated at those (oracle-checked) tokens;
+    NaN in sentinel rows, 0 after the committed slots."""
     import torch
     import rejection_sampling_verify_16_amd as sv
     name, B, k, V, dtype, kw = case
@@ -308,6 +336,9 @@ def test_raw_logprobs(o, case):
     res = {key: v.cpu().numpy() for key, v in res.items()}
     for key in plain:
         np.testing.assert_array_equal(res[key], plain[key], err_msg=f"{name}: {key} changed")
+    r, alt = parity.verify_oracle(o, w.target, w.draft, drafts, w.temperature, w.top_k, w.top_p, 11, 2)
+    rep = parity.compare({key: res[key] for key in plain}, r, drafts, V, label=f"raw/{name}", alt=alt)
+    print(f"[raw] {name}: {rep}", flush=True)
     ref = o.raw_logprobs(w.target, res["tokens"], res["accept_len"])
     sent = res["accept_len"] == 0
     assert np.all(np.isnan(res["raw_logprobs"][sent]))

@@ -44,6 +44,6 @@ def test_random_case(o, i):
     for off in (0, 7):
         print(f"[sweep] case {i}: B={w.B} k={w.k} V={w.V} {w.dtype} offset={off}", flush=True)
         g = parity.run_gpu(dev, 11 + i, off)
-        r = o.spec_verify(w.target, w.draft, drafts, w.temperature, w.top_k, w.top_p, seed=11 + i, offset=off)
-        rep = parity.compare(g, r, drafts, w.V, label=f"sweep{i}@{off}")
+        r, alt = parity.verify_oracle(o, w.target, w.draft, drafts, w.temperature, w.top_k, w.top_p, 11 + i, off)
+        rep = parity.compare(g, r, drafts, w.V, label=f"sweep{i}@{off}", alt=alt)
         print(f"[sweep] case {i}@{off}: {rep}", flush=True)

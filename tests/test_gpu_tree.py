@@ -22,13 +22,17 @@ def _dev_logits(a):
     return torch.from_numpy(a).to("cuda:0")
 
 
-def run_tree_gpu(w, seed, offset):
+def run_tree_gpu(w, seed, offset, garbage_workspace=False):
     import torch
     import rejection_sampling_verify_16_amd as sv
     d = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).to("cuda:0")
+    ws = None
+    if garbage_workspace:  # the workspace needs no initialisation
+        n = sv.tree_workspace_size(w.B, w.N, w.V, sv.SPEC_DTYPE_F32 if w.dtype == "f32" else sv.SPEC_DTYPE_BF16)
+        ws = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda:0")
     out = sv.spec_tree_verify(_dev_logits(w.target), d(w.parent, np.int32), d(w.node_tokens, np.int32),
                               d(w.temperature, np.float32), d(w.top_k, np.int32), d(w.top_p, np.float32),
-                              seed=seed, offset=offset)
+                              seed=seed, offset=offset, workspace=ws)
     torch.cuda.synchronize()
     return {k_: v.cpu().numpy() for k_, v in out.items()}
 
@@ -66,11 +70,11 @@ def compare_tree(g, r, w, label):
             "mean_accept": float(g["accept_len"][~sent].mean()) if (~sent).any() else 0.0}
 
 
-def check(o, w, seed=5, offsets=(1,)):
+def check(o, w, seed=5, offsets=(1,), garbage_workspace=False):
     print(f"tree case {w.name}: B={w.B} N={w.N} V={w.V} {w.dtype}", flush=True)
     reps = []
     for off in offsets:
-        g = run_tree_gpu(w, seed, off)
+        g = run_tree_gpu(w, seed, off, garbage_workspace)
         r = o.tree_verify(w.target, w.parent, w.node_tokens, w.temperature, w.top_k, w.top_p, seed=seed, offset=off)
         reps.append(compare_tree(g, r, w, f"{w.name}@{off}"))
     return reps
@@ -100,6 +104,10 @@ CASES = {
 @pytest.mark.parametrize("case", list(CASES))
 def test_tree_parity(o, case):
     check(o, CASES[case](), offsets=(1, 2))
+
+
+def test_tree_workspace_needs_no_initialisation(o):
+    check(o, CASES["random16_ragged"](), offsets=(3,), garbage_workspace=True)
 
 
 def test_tree_greedy_ties_and_unusable_rows(o):

@@ -9,14 +9,16 @@ in base 2, raw logprobs with the temperature applied, commit of the state after 
 position, commit with layers and rows swapped, sequence length grown by the accepted drafts only,
 commit ignoring the slot map, slot commit one position late, slot commit that drops the old slot, tree draws that keep the rejected children, tree
 children tested against their own mass alone, the parent's distribution after an accepted child, the
-tree's final draw one depth late).
+tree's final draw one depth late; the margin diagnostics: the accept distance taken over tests past the first
+rejection, the Gumbel gap of the exponentiated keys, the top-p distance without the next larger value, and an
+alternative draw that ignores the runner-up).
 """
 import pytest
 
 import oracle
 import oracle_pins
 
-MUTANTS = list(range(1, 26))
+MUTANTS = list(range(1, 30))
 
 
 @pytest.mark.parametrize("mutant", MUTANTS)
