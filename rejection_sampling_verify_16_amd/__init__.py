@@ -47,6 +47,12 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+        # torch ships its own HIP runtime; loading torch first makes the library bind that same runtime
+        # (loaded first, the library would bind the system one and torch would then share it)
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(LIB_PATH)
         P, I32, U64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t
         L.spec_verify_workspace_size.argtypes = [I32, I32, I32, ctypes.c_int]

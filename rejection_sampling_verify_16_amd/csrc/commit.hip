@@ -255,6 +255,7 @@ extern "C" spec_status_t spec_commit(const spec_state_tensor_t* tensors, int32_t
   const uint64_t status_wgs = ((uint64_t)B + CT - 1) / CT;
   uint64_t grid = tiles > status_wgs ? tiles : status_wgs;
   if (grid > MAXGRID) grid = MAXGRID;
+  (void)hipGetLastError();  // an earlier runtime call's error would otherwise be taken for this launch's
   hipLaunchKernelGGL(k_commit, dim3((unsigned)grid), dim3(CT), 0, (hipStream_t)stream, p);
   if (hipGetLastError() != hipSuccess) return SPEC_ERR_LAUNCH;
   return SPEC_OK;
@@ -275,6 +276,7 @@ extern "C" spec_status_t spec_commit_slots(int32_t* state_slot, int32_t* pos_slo
       if (p[i] && p[j] && overlap(p[i], n[i], p[j], n[j])) return SPEC_ERR_INVALID_ARGUMENT;
   int dev = -1, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || !sv::device_ok(dev, cus)) return SPEC_ERR_UNSUPPORTED_DEVICE;
+  (void)hipGetLastError();  // an earlier runtime call's error would otherwise be taken for this launch's
   hipLaunchKernelGGL(k_commit_slots, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, (hipStream_t)stream, state_slot,
                      pos_slot, accept_len, seq_len, status, B, k, num_slots);
   if (hipGetLastError() != hipSuccess) return SPEC_ERR_LAUNCH;

@@ -1,0 +1,90 @@
+// probe.hip -- libsvprobe: test and benchmark probes of libspecverify's device helpers (gfx950).
+//
+// NOT part of the product library: it is built into its own shared object, which only the GPU tests and
+// the benchmark load.  It runs the product's own device code (sv_common.h) on inputs chosen by the host,
+// so that the random stream and the race transform can be checked directly, element by element:
+//   probe_philox       the Philox-4x32-10 block function on given counters and keys (known-answer tests);
+//   probe_race_e2      for every 23-bit uniform code j (U = (j + 0.5) 2^-23): E2 = -log2 U as the draws
+//                      compute it, and the race key scale rcp(E2) (the Gumbel-max draws of the AReno page
+//                      "feat(engine): MTP training loss and speculative decoding for bailing_v3", its
+//                      per-step optimisation table);
+//   probe_u24          for every 24-bit code: the accept uniform (w >> 8) 2^-24 as the accept test sees it;
+//   probe_read_stream  a plain read of a buffer with 16-byte loads (the bandwidth reference the benchmark
+//                      quotes its kernels against).
+// Every entry point takes device pointers, enqueues one kernel on `stream` and returns 0, or 1 for bad
+// arguments (nothing enqueued).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sv_common.h"
+
+namespace {
+
+__global__ void k_philox(const uint32_t* ctr, const uint32_t* key, uint32_t* out, int n) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n) return;
+  const uint4 c = make_uint4(ctr[4 * t], ctr[4 * t + 1], ctr[4 * t + 2], ctr[4 * t + 3]);
+  const uint4 r = sv::philox10(c, key[2 * t], key[2 * t + 1]);
+  out[4 * t] = r.x;
+  out[4 * t + 1] = r.y;
+  out[4 * t + 2] = r.z;
+  out[4 * t + 3] = r.w;
+}
+
+__global__ void k_race_e2(float* e2, float* scale) {
+  const uint32_t j = blockIdx.x * blockDim.x + threadIdx.x;  // grid covers exactly 2^23 codes
+  const uint32_t w = j << 9;                                  // (w >> 9) == j
+  const float e = sv::exp_race_E2(w);
+  e2[j] = e;
+  scale[j] = __builtin_amdgcn_rcpf(e);
+}
+
+__global__ void k_u24(float* u) {
+  const uint32_t j = blockIdx.x * blockDim.x + threadIdx.x;  // grid covers exactly 2^24 codes
+  u[j] = sv::u24(j << 8);
+}
+
+// Each thread xors its 16-byte vectors (grid-stride); one word per workgroup keeps the loads alive.
+__global__ __launch_bounds__(256) void k_read_stream(const uint4* src, size_t nvec, uint32_t* sink) {
+  uint32_t acc = 0;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += (size_t)gridDim.x * blockDim.x) {
+    const uint4 v = src[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  acc = sv::wave_or(acc);
+  if ((threadIdx.x & 63) == 0 && acc == 0x9E3779B9u) sink[blockIdx.x] = acc;  // practically never stored
+}
+
+}  // namespace
+
+extern "C" int probe_philox(const uint32_t* ctr, const uint32_t* key, uint32_t* out, int32_t n, void* stream) {
+  if (n < 1 || !ctr || !key || !out) return 1;
+  (void)hipGetLastError();  // so that the check below is about this launch alone
+  hipLaunchKernelGGL(k_philox, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream, ctr, key, out, n);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+// e2, scale: device float [2^23]
+extern "C" int probe_race_e2(float* e2, float* scale, void* stream) {
+  if (!e2 || !scale) return 1;
+  (void)hipGetLastError();  // so that the check below is about this launch alone
+  hipLaunchKernelGGL(k_race_e2, dim3((1u << 23) / 256), dim3(256), 0, (hipStream_t)stream, e2, scale);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+// u: device float [2^24]
+extern "C" int probe_u24(float* u, void* stream) {
+  if (!u) return 1;
+  (void)hipGetLastError();  // so that the check below is about this launch alone
+  hipLaunchKernelGGL(k_u24, dim3((1u << 24) / 256), dim3(256), 0, (hipStream_t)stream, u);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+// src: device, nvec 16-byte vectors (16-byte aligned); sink: device uint32 [blocks]
+extern "C" int probe_read_stream(const void* src, size_t nvec, uint32_t* sink, int32_t blocks, void* stream) {
+  if (!src || !sink || nvec == 0 || blocks < 1 || ((uintptr_t)src & 15)) return 1;
+  (void)hipGetLastError();  // so that the check below is about this launch alone
+  hipLaunchKernelGGL(k_read_stream, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, (const uint4*)src, nvec,
+                     sink);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}

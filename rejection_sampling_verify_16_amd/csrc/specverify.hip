@@ -2504,6 +2504,9 @@ static spec_status_t launch(Params& p, const Geo& g, spec_dtype_t dtype, void* w
   p.fin5 = (FinalPart*)(ws + g.off_fin5);
   p.trace = TRACE_SLOTS > 0 ? (unsigned long long*)(ws + g.off_trace) : nullptr;
   p.trace5 = TRACE_SLOTS > 0 ? (unsigned long long*)(ws + g.off_trace5) : nullptr;
+  // hipGetLastError reports the last error of any earlier runtime call of this thread (a caller's, too);
+  // read it once before enqueueing so that the check after the launches is about them alone
+  (void)hipGetLastError();
   if (dtype == SPEC_DTYPE_BF16)
     enqueue<BF16>(p, cus, (hipStream_t)stream, tm);
   else
