@@ -90,6 +90,27 @@ spec_status_t spec_verify(const void* target_logits, const void* draft_logits, s
                           size_t workspace_bytes, void* stream);
 
 /*
+ * The verify step for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): spec_verify's arguments and outputs without the
+ * workspace.  The library keeps one scratch array of SPEC_NOALLOC_SCRATCH_BYTES per GPU in its own static
+ * device memory (held by every GPU the library is loaded on, until the process ends) and runs the same
+ * kernels on it; nothing is allocated or freed by the call.
+ *   Sizes whose spec_verify_workspace_size() exceeds SPEC_NOALLOC_SCRATCH_BYTES: SPEC_ERR_WORKSPACE,
+ *   nothing enqueued.  The scratch array's device address is looked up once per GPU, on the first call
+ *   with that GPU current (SPEC_ERR_LAUNCH if that fails).
+ *   Every call on one GPU uses that GPU's one array: calls that overlap on a GPU (on different streams,
+ *   from different threads, or in graphs replayed concurrently) race and give wrong results; order them.
+ *   The array needs no clearing: each call sets up every byte it reads.
+ */
+#define SPEC_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+spec_status_t spec_verify_noalloc(const void* target_logits, const void* draft_logits, spec_dtype_t dtype,
+                                  const int32_t* draft_tokens, const float* temperature, const int32_t* top_k,
+                                  const float* top_p, int32_t B, int32_t k, int32_t V, uint64_t seed,
+                                  uint64_t offset, int32_t* tokens, int32_t* accept_len, float* logprobs,
+                                  float* alpha, void* stream);
+
+/*
  * The verify step with raw logprobs as well: spec_verify's arguments and outputs, plus
  *
  *   raw_logprobs   out float [B, k+1]  for i <= n: ln softmax of target row i's unprocessed logits (no

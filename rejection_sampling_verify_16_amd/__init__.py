@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.spec_commit.restype = ctypes.c_int
         L.spec_commit_slots.argtypes = [P, P, P, P, P, I32, I32, I32, P]
         L.spec_commit_slots.restype = ctypes.c_int
+        L.spec_verify_noalloc.argtypes = [P, P, ctypes.c_int, P, P, P, P, I32, I32, I32, U64, U64, P, P, P, P, P]
+        L.spec_verify_noalloc.restype = ctypes.c_int
         L.spec_verify_timed.argtypes = [P, P, ctypes.c_int, P, P, P, P, I32, I32, I32, U64, U64, P, P, P, P, P, P,
                                         SZ, P, ctypes.POINTER(Timing)]
         L.spec_verify_timed.restype = ctypes.c_int
@@ -177,6 +179,28 @@ def spec_verify(target_logits, draft_logits, draft_tokens, temperature, top_k, t
         st = lib().spec_verify(*head, *tail)
     if st != 0:
         raise SpecVerifyError(st)
+    return out
+
+
+def spec_verify_noalloc(target_logits, draft_logits, draft_tokens, temperature, top_k, top_p, out, seed: int = 0,
+                        offset: int = 0, stream=None):
+    """spec_verify without a workspace (the library's per-GPU static scratch, see spec_verify_noalloc in the
+    C header); ``out`` (from alloc_outputs) is required, so the call allocates nothing."""
+    import torch
+    B, k1, V = target_logits.shape
+    dt = _dtype_code(target_logits)
+    for t in (target_logits, draft_logits, draft_tokens, temperature, top_k, top_p):
+        if not t.is_contiguous():
+            raise ValueError("all inputs must be contiguous")
+    if stream is None:
+        stream = torch.cuda.current_stream(target_logits.device)
+    st = lib().spec_verify_noalloc(target_logits.data_ptr(), draft_logits.data_ptr(), dt, draft_tokens.data_ptr(),
+                                   temperature.data_ptr(), top_k.data_ptr(), top_p.data_ptr(), B, k1 - 1, V, int(seed),
+                                   int(offset), out["tokens"].data_ptr(), out["accept_len"].data_ptr(),
+                                   out["logprobs"].data_ptr(), out["alpha"].data_ptr(),
+                                   ctypes.c_void_p(stream.cuda_stream))
+    if st != 0:
+        raise SpecVerifyError(st, "spec_verify_noalloc")
     return out
 
 

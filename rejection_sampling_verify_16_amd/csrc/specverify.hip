@@ -2580,6 +2580,40 @@ extern "C" spec_status_t spec_verify(const void* target_logits, const void* draf
                      offset, tokens, accept_len, logprobs, nullptr, alpha, workspace, workspace_bytes, stream, nullptr);
 }
 
+// Scratch of spec_verify_noalloc: file-scope static device memory, one copy per GPU.  Host code never
+// uses the array's name as an address: its per-device address comes from hipGetSymbolAddress, looked
+// up once per device with that device current.
+static __device__ __align__(256) uint8_t scratch[SPEC_NOALLOC_SCRATCH_BYTES];
+static void* g_scratch[MAXDEV];
+
+static void* scratch_address(int dev) {
+  if (dev < 0 || dev >= MAXDEV) return nullptr;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch[dev] = ptr;
+  }
+  return g_scratch[dev];
+}
+
+extern "C" spec_status_t spec_verify_noalloc(const void* target_logits, const void* draft_logits, spec_dtype_t dtype,
+                                             const int32_t* draft_tokens, const float* temperature,
+                                             const int32_t* top_k, const float* top_p, int32_t B, int32_t k,
+                                             int32_t V, uint64_t seed, uint64_t offset, int32_t* tokens,
+                                             int32_t* accept_len, float* logprobs, float* alpha, void* stream) {
+  Geo g;
+  if (k < 1 || !make_geo(B, k, V, dtype, g)) return SPEC_ERR_INVALID_ARGUMENT;
+  if (g.total > SPEC_NOALLOC_SCRATCH_BYTES) return SPEC_ERR_WORKSPACE;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || !device_ok(dev, cus)) return SPEC_ERR_UNSUPPORTED_DEVICE;
+  void* ws = scratch_address(dev);
+  if (!ws) return SPEC_ERR_LAUNCH;
+  return verify_impl(target_logits, draft_logits, dtype, draft_tokens, temperature, top_k, top_p, B, k, V, seed,
+                     offset, tokens, accept_len, logprobs, nullptr, alpha, ws, SPEC_NOALLOC_SCRATCH_BYTES, stream,
+                     nullptr);
+}
+
 extern "C" spec_status_t spec_verify_raw(const void* target_logits, const void* draft_logits, spec_dtype_t dtype,
                                          const int32_t* draft_tokens, const float* temperature, const int32_t* top_k,
                                          const float* top_p, int32_t B, int32_t k, int32_t V, uint64_t seed,
