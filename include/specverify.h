@@ -166,8 +166,9 @@ spec_status_t spec_sample(const void* logits, spec_dtype_t dtype, const float* t
  *   Draws are Gumbel-max on spec_verify's draw stream at position = depth.  Greedy rows (T = 0) follow
  *   the child whose token is the row's lowest-index argmax and end on the argmax.
  *
- * A tree whose nodes each have one child gives exactly spec_verify's outputs for draft rows that are
- * one-hot at the draft tokens (0 there, -inf elsewhere).
+ * A tree whose nodes each have one child gives spec_verify's tokens and accept lengths for draft rows
+ * that are one-hot at the draft tokens (0 there, -inf elsewhere), and its logprobs up to the rounding of
+ * the fp32 normaliser sums (which spec_verify may add up in another order).
  *
  *   target_logits  [B, N, V] contiguous, dtype, 16-byte aligned: row i is the target's logits after node i
  *   parent         int32 [B, N]  parent[b][i] in 0..i-1 for i >= 1 (entry 0 ignored)
@@ -283,17 +284,33 @@ const char* spec_verify_status_string(spec_status_t status);
  * launches; `kernels` receives how many that is (1 .. SPEC_MAX_KERNELS; which kernels depends on the
  * sizes and the device).  hipEventElapsedTime(events[2j], events[2j+1]) is then kernel j's duration.
  *
- *   events   HOST array of 2 * SPEC_MAX_KERNELS hipEvent_t handles, created by the caller with timing
- *            enabled; read during the call only.  Entries past 2 * kernels are not recorded.
- *   kernels  out: kernels this call launched
- * Nothing is kept between calls: the timing applies to this call alone.  A NULL timing pointer or NULL
- * events is SPEC_ERR_INVALID_ARGUMENT.
+ *   events      HOST array of 2 * SPEC_MAX_KERNELS hipEvent_t handles, created by the caller with timing
+ *               enabled, or NULL (no events recorded); read during the call only.  Entries past
+ *               2 * kernels are not recorded.
+ *   kernels     out: kernels this call launched (1: the one-launch resident path; 2 or 3: the staged path)
+ *   path        in: SPEC_PATH_AUTO (the library chooses), SPEC_PATH_STAGED (slice statistics, row merges and
+ *               the verify kernel as separate launches) or SPEC_PATH_RESIDENT (one launch that holds the
+ *               logits on chip; bf16 verify calls whose grid fits the device, otherwise the staged path is
+ *               taken, and `kernels` tells which ran).  Every path computes the same results up to fp32
+ *               rounding order.  Other values are SPEC_ERR_INVALID_ARGUMENT.
+ *   wait_limit  0 for the default, or a bound (in ticks of the GPU's 100 MHz clock) on each wait of a
+ *               workgroup for its batch row's other workgroups in the one-launch path (the grid is
+ *               co-resident, so the waits always end; the bound only keeps a stalled grid from hanging: a
+ *               workgroup that gives up turns its batch row into a sentinel row and exits).  Tests use a
+ *               tiny bound to exercise that path from the host.
+ * Nothing is kept between calls: the timing applies to this call alone.  A NULL timing pointer is
+ * SPEC_ERR_INVALID_ARGUMENT.
  */
 #define SPEC_MAX_KERNELS 3
+#define SPEC_PATH_AUTO 0
+#define SPEC_PATH_STAGED 1
+#define SPEC_PATH_RESIDENT 2
 
 typedef struct {
   void* const* events;
   int32_t kernels;
+  int32_t path;
+  uint64_t wait_limit;
 } spec_timing_t;
 
 spec_status_t spec_verify_timed(const void* target_logits, const void* draft_logits, spec_dtype_t dtype,

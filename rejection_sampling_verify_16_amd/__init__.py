@@ -30,9 +30,13 @@ class StateTensor(ctypes.Structure):
                 ("row_bytes", ctypes.c_int64), ("layers", ctypes.c_int32)]
 
 
+PATH_AUTO, PATH_STAGED, PATH_RESIDENT = 0, 1, 2  # SPEC_PATH_*
+
+
 class Timing(ctypes.Structure):
     """spec_timing_t: per-call kernel timing (events[2j] / events[2j+1] around kernel j)."""
-    _fields_ = [("events", ctypes.POINTER(ctypes.c_void_p)), ("kernels", ctypes.c_int32)]
+    _fields_ = [("events", ctypes.POINTER(ctypes.c_void_p)), ("kernels", ctypes.c_int32), ("path", ctypes.c_int32),
+                ("wait_limit", ctypes.c_uint64)]
 
 
 class SpecVerifyError(RuntimeError):
@@ -123,19 +127,26 @@ def alloc_outputs(B: int, k: int, device="cuda", raw: bool = False):
 
 
 class KernelTiming:
-    """Per-call kernel timing request: 2 * SPEC_MAX_KERNELS raw hipEvent_t handles (ints, created with
-    timing enabled).  Passed as ``timing=`` to spec_verify / spec_tree_verify, it makes the call go through
-    the timed entry point, which records events[2j] / events[2j+1] around kernel j; afterwards ``kernels``
-    holds how many kernels the call launched."""
+    """Per-call instrumentation: 2 * SPEC_MAX_KERNELS raw hipEvent_t handles (ints, created with timing
+    enabled) or None, the path to take (``path``: PATH_AUTO, PATH_STAGED or PATH_RESIDENT) and a bound on
+    the one-launch path's waits (``wait_limit``, 100 MHz ticks; 0 = the library's default).  Passed as
+    ``timing=`` to spec_verify / spec_tree_verify, it makes the call go through the timed entry point, which
+    records events[2j] / events[2j+1] around kernel j; afterwards ``kernels`` holds how many kernels the call
+    launched (1: the resident path)."""
 
-    def __init__(self, events):
-        if len(events) != 2 * SPEC_MAX_KERNELS:
+    def __init__(self, events=None, wait_limit: int = 0, path: int = 0):
+        if events is not None and len(events) != 2 * SPEC_MAX_KERNELS:
             raise ValueError(f"events: {2 * SPEC_MAX_KERNELS} hipEvent_t handles")
-        self._arr = (ctypes.c_void_p * len(events))(*events)
+        if path not in (PATH_AUTO, PATH_STAGED, PATH_RESIDENT):
+            raise ValueError("path: PATH_AUTO, PATH_STAGED or PATH_RESIDENT")
+        self._arr = None if events is None else (ctypes.c_void_p * len(events))(*events)
+        self.wait_limit = int(wait_limit)
+        self.path = int(path)
         self.kernels = 0
 
     def _struct(self):
-        return Timing(ctypes.cast(self._arr, ctypes.POINTER(ctypes.c_void_p)), 0)
+        ev = None if self._arr is None else ctypes.cast(self._arr, ctypes.POINTER(ctypes.c_void_p))
+        return Timing(ev, 0, self.path, self.wait_limit)
 
 
 def spec_verify(target_logits, draft_logits, draft_tokens, temperature, top_k, top_p, seed: int = 0,

@@ -10,7 +10,9 @@
 //                      per-step optimisation table);
 //   probe_u24          for every 24-bit code: the accept uniform (w >> 8) 2^-24 as the accept test sees it;
 //   probe_read_stream  a plain read of a buffer with 16-byte loads (the bandwidth reference the benchmark
-//                      quotes its kernels against).
+//                      quotes its kernels against);
+//   probe_dispatch_id  the dispatch's 64-bit id and queue address as a kernel sees them (the per-call tag of
+//                      cross-workgroup flags is built from them).
 // Every entry point takes device pointers, enqueues one kernel on `stream` and returns 0, or 1 for bad
 // arguments (nothing enqueued).
 #include <hip/hip_runtime.h>
@@ -55,7 +57,25 @@ __global__ __launch_bounds__(256) void k_read_stream(const uint4* src, size_t nv
   if ((threadIdx.x & 63) == 0 && acc == 0x9E3779B9u) sink[blockIdx.x] = acc;  // practically never stored
 }
 
+// The dispatch id (the LLVM intrinsic has no clang builtin of its own).
+extern "C" __device__ unsigned long long sv_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
+
+__global__ void k_dispatch_id(unsigned long long* out) {
+  if (threadIdx.x == 0) {
+    out[2 * blockIdx.x] = sv_dispatch_id();
+    out[2 * blockIdx.x + 1] = (unsigned long long)(uintptr_t)__builtin_amdgcn_queue_ptr();
+  }
+}
+
 }  // namespace
+
+// out: device uint64 [2 * blocks]
+extern "C" int probe_dispatch_id(unsigned long long* out, int32_t blocks, void* stream) {
+  if (!out || blocks < 1) return 1;
+  (void)hipGetLastError();  // so that the check below is about this launch alone
+  hipLaunchKernelGGL(k_dispatch_id, dim3((unsigned)blocks), dim3(64), 0, (hipStream_t)stream, out);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
 
 extern "C" int probe_philox(const uint32_t* ctr, const uint32_t* key, uint32_t* out, int32_t n, void* stream) {
   if (n < 1 || !ctr || !key || !out) return 1;

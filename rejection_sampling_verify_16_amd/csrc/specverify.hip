@@ -41,6 +41,7 @@
 #include <cmath>
 #include <cstring>
 #include <mutex>
+#include <type_traits>
 
 #include "specverify.h"
 #include "sv_common.h"
@@ -2373,9 +2374,37 @@ __global__ __launch_bounds__(NT) void k_tree(Params p) {
     tree_emit(p, sm, b, q, bidx, bval);
 }
 
+#include "sv_resident.h"
+
 // ---------------------------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------------------------
+constexpr int RMAXK = 4;      // the resident kernel serves k = 1..RMAXK
+constexpr int RMAXWG = 1024;  // the largest resident grid the workspace is sized for (a GPU with <= 1024 CUs)
+// The library's own choice takes the resident path only up to this many vectors per thread and row (its
+// single workgroup per CU has too few waves to hide latency on longer slices, where the staged path wins).
+constexpr int RAUTO_NV = 3;
+
+// Workspace of the resident kernel with S slices per batch row.
+static size_t resident_bytes(int32_t B, int32_t k, int32_t S) {
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t rows = (size_t)(2 * k + 1), bs = (size_t)B * (size_t)S;
+  return al(bs * rows * sizeof(RPart)) + al(bs * rows * RWIN * 4) + al(bs * sizeof(RFin)) + 2 * al(bs * 8) +
+         (TRACE_SLOTS > 0 ? al(bs * 128) : 0) + 256;
+}
+
+// Slices per batch row the resident kernel would use on a GPU with `cus` compute units (one workgroup per
+// CU): the smallest nv (vectors per thread per row) whose grid B x ceil(V / 4096 nv) fits; false if none.
+static bool resident_plan(int32_t B, int32_t k, int32_t V, int cus, int& nv, int& S) {
+  if (k < 1 || k > RMAXK) return false;
+  for (nv = 1; nv <= rnv_max(k); ++nv) {
+    const int L = RT * BF16::EPV * nv;
+    S = (V + L - 1) / L;
+    if ((long long)B * S <= (long long)cus) return true;
+  }
+  return false;
+}
+
 struct Geo {
   int rows, R, S1, S5, L1, L5, esize, EPV;
   size_t off_cnt5, off_st1, off_hw1, off_hc1, off_cand1, off_ncand1, off_rinfo, off_fin5, off_trace, off_trace5,
@@ -2420,12 +2449,17 @@ static bool make_geo(int32_t B, int32_t k, int32_t V, spec_dtype_t dtype, Geo& g
   take(g.off_trace, R * g.S1 * TRACE_SLOTS * 8);
   take(g.off_trace5, (size_t)B * g.S5 * TRACE_SLOTS * 8);
   g.total = off;
+  // the resident kernel (bf16 verify, k <= RMAXK) lays out its own partials in the same workspace
+  int nv = 0, S = 0;
+  if (dtype == SPEC_DTYPE_BF16 && tree_nodes == 0 && k >= 1 && resident_plan(B, k, V, RMAXWG, nv, S))
+    g.total = std::max(g.total, resident_bytes(B, k, std::max(S, 1)) + 256);
   return true;
 }
 
 struct DevInfo {
   int state;  // 0 unknown, 1 gfx950, 2 other
   int cus;    // compute units
+  int rocc[RMAXK + 1];  // resident kernel: co-resident workgroups per CU (0 unknown, -1 unusable)
 };
 static DevInfo g_dev[MAXDEV];
 static std::mutex g_mu;
@@ -2443,10 +2477,13 @@ bool device_ok(int dev, int& cus) {
   return g_dev[dev].state == 1;
 }
 
-// Per-call kernel timing (the timed entry points): events[2j] / events[2j+1] around kernel j.
+// Per-call kernel timing (the timed entry points): events[2j] / events[2j+1] around kernel j; and the
+// bound on the resident kernel's waits (0: the default).
 struct Timing {
   hipEvent_t ev[2 * NKERN];
   int used;
+  int path;  // SPEC_PATH_*
+  uint64_t wait_limit;
 };
 static void prof_mark(Timing* t, int idx, hipStream_t st) {
   if (t && t->ev[idx]) (void)hipEventRecord(t->ev[idx], st);
@@ -2482,8 +2519,91 @@ static void enqueue(const Params& p, int cus, hipStream_t st, Timing* tm) {
   if (tm) tm->used = NKERN;
 }
 
+template <int KK>
+static int resident_occupancy() {
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kr_verify<KK>, RT, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return -1;
+  }
+  return nb >= 1 ? nb : -1;
+}
+
+// Co-resident workgroups per CU of the resident kernel for k (cached per device); <= 0 if it cannot run.
+static int resident_occ(int dev, int k) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  int& o = g_dev[dev].rocc[k];
+  if (o == 0) o = k == 1 ? resident_occupancy<1>() : k == 2 ? resident_occupancy<2>()
+                  : k == 3 ? resident_occupancy<3>() : resident_occupancy<4>();
+  return o;
+}
+
+// The resident kernel for this call, if its grid fits the device; false (nothing enqueued) otherwise, and
+// also if the runtime refuses the cooperative launch.
+static bool launch_resident(const Params& p, int dev, int cus, uint8_t* ws, size_t ws_bytes, hipStream_t st,
+                            Timing* tm, uint64_t seed, bool forced) {
+  int nv = 0, S = 0;
+  if (p.mode != MODE_VERIFY || p.raw_logprobs || !resident_plan(p.B, p.k, p.V, cus, nv, S)) return false;
+  if (!forced && nv > RAUTO_NV) return false;  // the staged path is faster for longer slices
+  const int occ = resident_occ(dev, p.k);
+  if (occ < 1 || (long long)p.B * S > (long long)occ * cus || resident_bytes(p.B, p.k, S) > ws_bytes) return false;
+  RParams r;
+  std::memset(&r, 0, sizeof r);
+  r.target = p.target;
+  r.draft = p.draft;
+  r.draft_tokens = p.draft_tokens;
+  r.temperature = p.temperature;
+  r.top_k = p.top_k;
+  r.top_p = p.top_p;
+  r.B = p.B;
+  r.k = p.k;
+  r.V = p.V;
+  r.S = S;
+  r.nv = nv;
+  r.L = RT * BF16::EPV * nv;
+  r.key0 = p.key0;
+  r.key1 = p.key1;
+  r.offset = p.offset;
+  r.salt = seed ^ ((uint64_t)p.offset << 32) ^ ((uint64_t)p.B * 0x100000001B3ull) ^ ((uint64_t)p.k << 56) ^
+           ((uint64_t)p.V << 20);
+  r.wait_limit = (tm && tm->wait_limit) ? tm->wait_limit : RWAIT_DEFAULT;
+  r.tokens = p.tokens;
+  r.accept_len = p.accept_len;
+  r.logprobs = p.logprobs;
+  r.alpha = p.alpha;
+  const size_t bs = (size_t)p.B * S, rows = (size_t)(2 * p.k + 1);
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  size_t off = 0;
+  r.part = (RPart*)(ws + off);
+  off += al(bs * rows * sizeof(RPart));
+  r.win = (uint32_t*)(ws + off);
+  off += al(bs * rows * RWIN * 4);
+  r.fin = (RFin*)(ws + off);
+  off += al(bs * sizeof(RFin));
+  r.flag1 = (unsigned long long*)(ws + off);
+  off += al(bs * 8);
+  r.flag2 = (unsigned long long*)(ws + off);
+  off += al(bs * 8);
+  r.trace = TRACE_SLOTS > 0 ? (unsigned long long*)(ws + off) : nullptr;
+  // An ordinary launch: its grid (one workgroup per CU at most, checked above against the occupancy of
+  // this kernel) is resident at once on an otherwise idle device.  A cooperative launch would guarantee it
+  // but costs ~20 us per call on this runtime; the bounded waits keep a stalled grid from hanging instead.
+  prof_mark(tm, 0, st);
+  if (p.k == 1)
+    hipLaunchKernelGGL(kr_verify<1>, dim3((unsigned)bs), dim3(RT), 0, st, r);
+  else if (p.k == 2)
+    hipLaunchKernelGGL(kr_verify<2>, dim3((unsigned)bs), dim3(RT), 0, st, r);
+  else if (p.k == 3)
+    hipLaunchKernelGGL(kr_verify<3>, dim3((unsigned)bs), dim3(RT), 0, st, r);
+  else
+    hipLaunchKernelGGL(kr_verify<4>, dim3((unsigned)bs), dim3(RT), 0, st, r);
+  prof_mark(tm, 1, st);
+  if (tm) tm->used = 1;
+  return true;
+}
+
 static spec_status_t launch(Params& p, const Geo& g, spec_dtype_t dtype, void* workspace, size_t workspace_bytes,
-                            void* stream, Timing* tm = nullptr) {
+                            void* stream, Timing* tm = nullptr, uint64_t seed = 0) {
   if (!workspace || workspace_bytes < g.total || ((uintptr_t)workspace & 15)) return SPEC_ERR_WORKSPACE;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || !device_ok(dev, cus)) return SPEC_ERR_UNSUPPORTED_DEVICE;
@@ -2507,6 +2627,12 @@ static spec_status_t launch(Params& p, const Geo& g, spec_dtype_t dtype, void* w
   // hipGetLastError reports the last error of any earlier runtime call of this thread (a caller's, too);
   // read it once before enqueueing so that the check after the launches is about them alone
   (void)hipGetLastError();
+  const int path = tm ? tm->path : SPEC_PATH_AUTO;
+  if (dtype == SPEC_DTYPE_BF16 && path != SPEC_PATH_STAGED &&
+      launch_resident(p, dev, cus, ws, workspace_bytes, (hipStream_t)stream, tm, seed, path == SPEC_PATH_RESIDENT)) {
+    if (hipGetLastError() != hipSuccess) return SPEC_ERR_LAUNCH;
+    return SPEC_OK;
+  }
   if (dtype == SPEC_DTYPE_BF16)
     enqueue<BF16>(p, cus, (hipStream_t)stream, tm);
   else
@@ -2568,7 +2694,7 @@ static spec_status_t verify_impl(const void* target_logits, const void* draft_lo
   p.logprobs = logprobs;
   p.raw_logprobs = raw_logprobs;
   p.alpha = alpha;
-  return launch(p, g, dtype, workspace, workspace_bytes, stream, tm);
+  return launch(p, g, dtype, workspace, workspace_bytes, stream, tm, seed);
 }
 
 extern "C" spec_status_t spec_verify(const void* target_logits, const void* draft_logits, spec_dtype_t dtype,
@@ -2628,9 +2754,12 @@ extern "C" spec_status_t spec_verify_raw(const void* target_logits, const void* 
 
 // Copies the caller's events into a per-call Timing (nothing outlives the call).
 static bool timing_in(const spec_timing_t* t, Timing& tm) {
-  if (!t || !t->events) return false;
-  for (int j = 0; j < 2 * NKERN; ++j) tm.ev[j] = (hipEvent_t)t->events[j];
+  if (!t) return false;
+  for (int j = 0; j < 2 * NKERN; ++j) tm.ev[j] = t->events ? (hipEvent_t)t->events[j] : nullptr;
   tm.used = 0;
+  if (t->path != SPEC_PATH_AUTO && t->path != SPEC_PATH_STAGED && t->path != SPEC_PATH_RESIDENT) return false;
+  tm.path = t->path;
+  tm.wait_limit = t->wait_limit;
   return true;
 }
 

@@ -59,11 +59,13 @@ def device_inputs(w, drafts, device="cuda"):
                 P=torch.from_numpy(w.top_p).to(device))
 
 
-def run_gpu(dev, seed, offset, out=None, workspace=None):
+def run_gpu(dev, seed, offset, out=None, workspace=None, timing=None):
+    """One verify call on device inputs; ``timing`` (a KernelTiming) selects the path and reports the number
+    of kernels the call launched."""
     import torch
     import rejection_sampling_verify_16_amd as sv
     res = sv.spec_verify(dev["target"], dev["draft"], dev["drafts"], dev["T"], dev["K"], dev["P"], seed=seed,
-                         offset=offset, out=out, workspace=workspace)
+                         offset=offset, out=out, workspace=workspace, timing=timing)
     torch.cuda.synchronize()
     return {k_: v.cpu().numpy() for k_, v in res.items()}
 

@@ -55,14 +55,22 @@ def test_timed_entry_points_need_their_timing(L):
     P = ctypes.c_void_p(16)
     st = L.spec_verify_timed(P, P, 0, P, P, P, P, 2, 2, 1024, 0, 0, P, P, P, None, P, P, 1 << 30, None, None)
     assert st == 1
-    t = sv.Timing(None, 0)
-    st = L.spec_verify_timed(P, P, 0, P, P, P, P, 2, 2, 1024, 0, 0, P, P, P, None, P, P, 1 << 30, None,
-                             ctypes.byref(t))
+    t = sv.Timing(None, 0, 0, 0)
+    st = L.spec_verify_timed(P, P, 0, P, P, P, P, 0, 2, 1024, 0, 0, P, P, P, None, P, P, 1 << 30, None,
+                             ctypes.byref(t))   # B = 0: rejected before any device call
     assert st == 1
     st = L.spec_tree_verify_timed(P, 0, P, P, P, P, P, 2, 3, 1024, 0, 0, P, P, P, P, P, 1 << 30, None, None)
     assert st == 1
     with pytest.raises(ValueError):
         sv.KernelTiming([0] * 3)
+    # a path other than auto / staged / resident is rejected before anything else
+    bad = sv.Timing(None, 0, 7, 0)
+    st = L.spec_verify_timed(P, P, 0, P, P, P, P, 2, 2, 1024, 0, 0, P, P, P, None, P, P, 1 << 30, None,
+                             ctypes.byref(bad))
+    assert st == 1
+    with pytest.raises(ValueError):
+        sv.KernelTiming(path=3)
+    assert (sv.PATH_AUTO, sv.PATH_STAGED, sv.PATH_RESIDENT) == (0, 1, 2)
 
 
 def test_smallest_vocabulary(L):

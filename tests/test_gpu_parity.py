@@ -20,14 +20,20 @@ def o():
     return oracle.get()
 
 
-def _check(o, w, offsets, label, drafts=None):
+def _check(o, w, offsets, label, drafts=None, path=0):
+    """GPU against oracle on the given offsets; ``path`` forces the staged (1) or resident (2) path, and the
+    resident path must then have run as one launch."""
+    import rejection_sampling_verify_16_amd as sv
     if drafts is None:
         drafts = w.draft_tokens(parity.oracle_sampler(o))
     dev = parity.device_inputs(w, drafts)
     reports = []
     for off in offsets:
-        print(f"[parity] {label} B={w.B} k={w.k} V={w.V} {w.dtype} offset={off}", flush=True)
-        g = parity.run_gpu(dev, w.seed, off)
+        print(f"[parity] {label} B={w.B} k={w.k} V={w.V} {w.dtype} offset={off} path={path}", flush=True)
+        tm = sv.KernelTiming(path=path)
+        g = parity.run_gpu(dev, w.seed, off, timing=tm)
+        if path == sv.PATH_RESIDENT:
+            assert tm.kernels == 1, f"{label}: the resident path did not run ({tm.kernels} kernels)"
         r, alt = parity.verify_oracle(o, w.target, w.draft, drafts, w.temperature, w.top_k, w.top_p, w.seed, off)
         rep = parity.compare(g, r, drafts, w.V, label=f"{label}@{off}", alt=alt)
         print(f"[parity] {label}@{off}: {rep}", flush=True)
@@ -111,7 +117,8 @@ def _shift_bf16(a, delta):
     return W.bf16_rne(W.bf16_to_f32(a) + np.float32(delta))
 
 
-def test_candidate_path_edges(o):
+@pytest.mark.parametrize("path", [0, 2], ids=["auto", "resident"])
+def test_candidate_path_edges(o, path):
     """Truncated bf16 rows with few kept entries (finished from the candidates recorded by the
     statistics pass): clustered values with ties at the top-k threshold, token 0 kept with logit
     +0 (its packed candidate is all zero bits), slices that are entirely -inf, and a row whose
@@ -119,7 +126,7 @@ def test_candidate_path_edges(o):
     neg_inf, most_neg = np.uint16(0xFF80), np.uint16(0xFF7F)
     clustered = W.make(6, 3, 30000, seed=4101, target_sigma=0.3, noise_sigma=0.05, top_k=20,
                        name="clustered_topk")
-    _check(o, clustered, [0, 5], "clustered_topk")
+    _check(o, clustered, [0, 5], "clustered_topk", path=path)
     w = W.make(6, 2, 40000, seed=4102, temperature=0.9, top_k=3, top_p=0.9, name="cand_edges")
     w.target = _shift_bf16(w.target, -12.0).reshape(w.target.shape)
     w.draft = _shift_bf16(w.draft, -12.0).reshape(w.draft.shape)
@@ -133,17 +140,18 @@ def test_candidate_path_edges(o):
     w.target[4, :, 3] = np.uint16(0xFF7E)
     w.draft[4, :, :] = neg_inf
     w.draft[4, :, 5::13] = most_neg
-    _check(o, w, [0, 2], "cand_edges")
+    _check(o, w, [0, 2], "cand_edges", path=path)
     # one small slice whose values all lie within 64 codes of -inf (the candidate window reaches -inf)
     tiny = W.make(3, 1, 64, seed=4103, temperature=1.0, top_k=4, name="near_neginf")
     rng = np.random.default_rng(4103)
     for a in (tiny.target, tiny.draft):
         a[...] = rng.integers(0xFF41, 0xFF80, size=a.shape, dtype=np.uint16)
         a[..., ::9] = neg_inf
-    _check(o, tiny, [0, 1], "near_neginf")
+    _check(o, tiny, [0, 1], "near_neginf", path=path)
 
 
-def test_topk_candidate_selection_fallbacks(o):
+@pytest.mark.parametrize("path", [0, 2], ids=["auto", "resident"])
+def test_topk_candidate_selection_fallbacks(o, path):
     """Top-k rows with small K select their threshold from recorded candidates; rows where that cannot
     work fall back to the whole-row selection: a flat row (every slice overflows its record), a top-k
     range that crosses zero (too many codes between the maximum and the threshold), several outliers
@@ -160,10 +168,11 @@ def test_topk_candidate_selection_fallbacks(o):
             w.target[b, i, idx] = W.bf16_rne(rng.uniform(12.0, 14.0, size=24).astype(np.float32))
     w.top_k[4] = 64
     w.top_k[5] = 65                            # one above the limit: histogram selection
-    _check(o, w, [0, 3], "topk_fallbacks")
+    _check(o, w, [0, 3], "topk_fallbacks", path=path)
 
 
-def test_special_values_and_sentinels(o):
+@pytest.mark.parametrize("path", [0, 2], ids=["auto", "resident"])
+def test_special_values_and_sentinels(o, path):
     w = W.make(10, 2, 16384, seed=77, temperature=1.0, top_p=0.8, name="special")
     drafts = w.draft_tokens(parity.oracle_sampler(o))
     neg_inf = np.uint16(0xFF80)
@@ -179,11 +188,12 @@ def test_special_values_and_sentinels(o):
     drafts[7, 1] = w.V                      # draft out of range -> sentinel
     w.target[8, 0, 100] = np.uint16(0x8000)  # -0.0 ties +0.0
     w.target[8, 0, 101] = np.uint16(0x0000)
-    reps = _check(o, w, [0, 3], "special", drafts)
+    reps = _check(o, w, [0, 3], "special", drafts, path=path)
     assert reps[0]["sentinel"] == 7
 
 
-def test_greedy_rows_among_sampled_rows_and_greedy_sentinels(o):
+@pytest.mark.parametrize("path", [0, 2], ids=["auto", "resident"])
+def test_greedy_rows_among_sampled_rows_and_greedy_sentinels(o, path):
     """Greedy batch rows (written by one workgroup from the row statistics) interleaved with sampled and
     truncated rows, and greedy rows that must become sentinel rows."""
     w = W.make(12, 2, 20000, seed=78, boost=8.0, tie_fraction=0.1, mixed_params=True, name="greedy_mix")
@@ -197,11 +207,12 @@ def test_greedy_rows_among_sampled_rows_and_greedy_sentinels(o):
     w.top_k[8] = -2                                      # invalid top-k with temperature 0 -> sentinel
     w.target[9, 0, :] = np.uint16(0xFF80)                # all -inf target row -> sentinel
     w.target[11, :, ::2] = np.uint16(0xFF80)             # -inf entries are legal in greedy rows
-    reps = _check(o, w, [0, 4], "greedy_mix", drafts)
+    reps = _check(o, w, [0, 4], "greedy_mix", drafts, path=path)
     assert reps[0]["sentinel"] == 5
 
 
-def test_workspace_needs_no_initialisation(o):
+@pytest.mark.parametrize("path", [0, 2], ids=["auto", "resident"])
+def test_workspace_needs_no_initialisation(o, path):
     """Every call sets up the workspace bytes it reads: a workspace filled with 0xFF before each call (and one
     left as the previous, different-sized call wrote it) gives the oracle's outputs."""
     import torch
@@ -219,7 +230,7 @@ def test_workspace_needs_no_initialisation(o):
             drafts = w.draft_tokens(parity.oracle_sampler(o))
             dev = parity.device_inputs(w, drafts)
             print(f"[parity] {w.name} workspace {'0xFF' if fill else 'as left'}", flush=True)
-            g = parity.run_gpu(dev, 4, 6, workspace=ws)
+            g = parity.run_gpu(dev, 4, 6, workspace=ws, timing=sv.KernelTiming(path=path))
             r, alt = parity.verify_oracle(o, w.target, w.draft, drafts, w.temperature, w.top_k, w.top_p, 4, 6)
             parity.compare(g, r, drafts, w.V, label=f"{w.name}/{fill}", alt=alt)
 
@@ -319,10 +330,11 @@ RAW_CASES = [
 
 @pytest.mark.parametrize("case", RAW_CASES, ids=[c[0] for c in RAW_CASES])
 def test_raw_logprobs(o, case):
-    """spec_verify_raw: every output of spec_verify unchanged (bit-exact) and those outputs at parity with
-    the oracle's verify step on the same inputs, seed and offset; plus ln softmax of the unprocessed target
-    logits at each committed token, checked against the oracle evaluated at those (oracle-checked) tokens;
-    NaN in sentinel rows, 0 after the committed slots."""
+    """spec_verify_raw: spec_verify's outputs at parity with the oracle's verify step on the same inputs, seed
+    and offset, with the same tokens and accept lengths as spec_verify (whose one-launch path may round its
+    fp32 sums differently: logprobs and alpha agree within the parity tolerances); plus ln softmax of the
+    unprocessed target logits at each committed token, checked against the oracle evaluated at those
+    (oracle-checked) tokens; NaN in sentinel rows, 0 after the committed slots."""
     import torch
     import rejection_sampling_verify_16_amd as sv
     name, B, k, V, dtype, kw = case
@@ -334,8 +346,10 @@ def test_raw_logprobs(o, case):
                          offset=2, raw=True)
     torch.cuda.synchronize()
     res = {key: v.cpu().numpy() for key, v in res.items()}
-    for key in plain:
+    for key in ("tokens", "accept_len"):
         np.testing.assert_array_equal(res[key], plain[key], err_msg=f"{name}: {key} changed")
+    np.testing.assert_allclose(res["logprobs"], plain["logprobs"], rtol=0, atol=parity.LOGPROB_TOL)
+    np.testing.assert_allclose(res["alpha"], plain["alpha"], rtol=0, atol=parity.ALPHA_TOL)
     r, alt = parity.verify_oracle(o, w.target, w.draft, drafts, w.temperature, w.top_k, w.top_p, 11, 2)
     rep = parity.compare({key: res[key] for key in plain}, r, drafts, V, label=f"raw/{name}", alt=alt)
     print(f"[raw] {name}: {rep}", flush=True)

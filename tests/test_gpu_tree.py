@@ -133,8 +133,9 @@ def test_tree_greedy_ties_and_unusable_rows(o):
 
 
 def test_tree_chain_equals_chain_verify():
-    """Chain-shaped trees give exactly the chain verify step's outputs for one-hot draft rows: tokens, accept
-    lengths and logprobs bit for bit (bf16 mixed, fp32, greedy), path = 1..n."""
+    """Chain-shaped trees give the chain verify step's outputs for one-hot draft rows (bf16 mixed, fp32,
+    greedy): tokens and accept lengths bit for bit, path = 1..n, and logprobs equal up to the rounding of the
+    kept-set normaliser (spec_verify's one-launch path sums it in another order than the tree kernels)."""
     import torch
     import rejection_sampling_verify_16_amd as sv
     for name, B, k, V, dtype, kw in [("bf16_mixed", 64, 2, 157184, "bf16", dict(boost=12.0, mixed_params=True)),
@@ -161,7 +162,7 @@ def test_tree_chain_equals_chain_verify():
         t = {k_: v.cpu().numpy() for k_, v in t.items()}
         np.testing.assert_array_equal(t["accept_len"], c["accept_len"])
         np.testing.assert_array_equal(t["tokens"], c["tokens"])
-        np.testing.assert_array_equal(t["logprobs"], c["logprobs"])
+        np.testing.assert_allclose(t["logprobs"], c["logprobs"], rtol=0, atol=4e-6)
         for b in range(B):
             n = c["accept_len"][b] - 1
             assert list(t["path"][b]) == list(range(1, n + 1)) + [-1] * (k + 1 - n)
