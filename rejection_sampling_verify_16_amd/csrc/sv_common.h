@@ -27,6 +27,9 @@ struct BF16 {
   __device__ static inline float load1(const void* row, int x) {
     return __uint_as_float((uint32_t)((const uint16_t*)row)[x] << 16);
   }
+  // the raw bits of one logit, and their value (a load whose result is only stored waits only there)
+  __device__ static inline uint32_t load1_raw(const void* row, int x) { return ((const uint16_t*)row)[x]; }
+  __device__ static inline float from_raw(uint32_t h) { return __uint_as_float(h << 16); }
 };
 
 struct F32 {
@@ -36,6 +39,8 @@ struct F32 {
     return __uint_as_float(e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w);
   }
   __device__ static inline float load1(const void* row, int x) { return ((const float*)row)[x]; }
+  __device__ static inline uint32_t load1_raw(const void* row, int x) { return ((const uint32_t*)row)[x]; }
+  __device__ static inline float from_raw(uint32_t h) { return __uint_as_float(h); }
 };
 
 // Order-preserving unsigned keys (larger value -> larger key; -0 and +0 share one key; key 0 never
@@ -110,7 +115,39 @@ __device__ inline uint4 philox10(uint4 c, uint32_t k0, uint32_t k1) {
   return c;
 }
 
+// Two Philox-4x32-10 blocks under one key, rounds interleaved (two independent dependency chains).
+__device__ inline void philox10x2(uint4& c0, uint4& c1, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t a0 = (uint64_t)0xD2511F53u * c0.x, a1 = (uint64_t)0xD2511F53u * c1.x;
+    const uint64_t b0 = (uint64_t)0xCD9E8D57u * c0.z, b1 = (uint64_t)0xCD9E8D57u * c1.z;
+    const uint32_t n00 = (uint32_t)(b0 >> 32) ^ c0.y ^ k0, n01 = (uint32_t)(b1 >> 32) ^ c1.y ^ k0;
+    const uint32_t n20 = (uint32_t)(a0 >> 32) ^ c0.w ^ k1, n21 = (uint32_t)(a1 >> 32) ^ c1.w ^ k1;
+    c0.y = (uint32_t)b0;
+    c1.y = (uint32_t)b1;
+    c0.w = (uint32_t)a0;
+    c1.w = (uint32_t)a1;
+    c0.x = n00;
+    c1.x = n01;
+    c0.z = n20;
+    c1.z = n21;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+}
+
 __device__ inline float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// A workgroup barrier for LDS traffic only: this wave's LDS operations complete (lgkmcnt 0), then the
+// barrier.  Unlike __syncthreads() it does not wait for global loads in flight (data prefetched for later
+// work keeps streaming in across it); the signal fences keep the compiler from moving memory accesses
+// across it.  Not for data handed over through global memory or LDS DMA.
+__device__ __forceinline__ void lds_sync() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left at their maxima
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // Accept uniform: top 24 bits, exact in fp32.
 __device__ inline float u24(uint32_t w) { return (float)(w >> 8) * 0x1p-24f; }

@@ -171,16 +171,6 @@ struct RSmem {
   uint32_t hist[2][WTOP];    // phase 1: code counts of a row (two arrays, by row parity; zero between uses)
 };
 
-// A workgroup barrier for LDS traffic only: this wave's LDS operations complete (lgkmcnt 0), then the
-// barrier.  Unlike __syncthreads() it does not wait for the global and LDS DMA loads in flight (the slice's
-// data is still arriving while phase 1 reduces the rows that are in); the signal fences keep the compiler
-// from moving memory accesses across it.  Not for data handed over through global memory or LDS DMA.
-__device__ __forceinline__ void lds_sync() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt left at their maxima
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
 
 // The LDS byte address of a shared-memory pointer.
 __device__ __forceinline__ uint32_t lds_addr(const void* q) {
