@@ -4,11 +4,18 @@ One step = one spec_verify() call over one batch of synthetic inputs already res
 (default workload: B=64, k=2, V=157184, bf16, mixed temperature / top-k / top-p per row).
 Input sets are rotated so that the working set exceeds the 256 MB Infinity Cache.
 
-Prints one JSON line.  Besides the throughput it reports
+Prints one JSON line.  Besides the throughput (whole timed region) it reports
+  samples:      the timed calls split into --samples equal runs: median / min / max per call;
   roofline:     the statistics kernel (it streams every logit once): algorithmic logit bytes per
                 launch / its average duration (HIP events the library records around each of its
                 kernels, over a second pass of the same calls), against the 8 TB/s HBM peak;
-  cpu_baseline: the CPU oracle timed on this host on a bounded sample of the same workload;
+  read_stream:  a plain read of the same number of bytes (the probe library's 16-byte loads), the
+                bandwidth one pass over the logits can reach on this GPU;
+  traffic:      HBM bytes per call from the committed PMC summary (when taken on these sources):
+                each kernel's and the whole call's, against the algorithmic logit bytes;
+  cpu_baseline: the CPU oracle timed on this host on a bounded sample of the same workload, with the
+                host's core count, the threads used and a one-thread figure; and the oracle's margin rows
+                (outcomes a correct rounding could change, exempt from bit-exact comparison) per workload;
   commit:       the commit step after verify (spec_commit) on a hybrid-model state workload, with its own
                 throughput, roofline and CPU baseline (skip with --no-commit, alone with --commit-only).
 """
@@ -31,7 +38,7 @@ METRIC = "verified rows/s + logits HBM GB/s (% peak), B=64 k=2 V=157184 bf16"
 HBM_PEAK_GBPS = 8000.0
 ROTATE_BYTES = 1 << 30
 _CSRC = os.path.join(ROOT, "rejection_sampling_verify_16_amd", "csrc")
-KERNEL_SRC = [os.path.join(_CSRC, f) for f in ("specverify.hip", "sv_common.h")]
+KERNEL_SRC = [os.path.join(_CSRC, f) for f in ("specverify.hip", "sv_common.h", "sv_resident.h")]
 COMMIT_SRC = [os.path.join(_CSRC, "commit.hip")]
 
 
@@ -49,23 +56,106 @@ def kernel_digest(files=None) -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic_target(config: str):
-    """(summary file, kernel name fragment, sources) of the dominant kernel of a workload."""
+def _traffic_target(config: str, resident: bool = False):
+    """(summary file, kernel name, sources) of the dominant kernel of a workload (on the resident path: the
+    resident kernel's own summary)."""
     if config == "commit":
         return os.path.join(ROOT, "profiles", "traffic_commit.json"), "k_commit", COMMIT_SRC
+    if resident:
+        return os.path.join(ROOT, "profiles", f"traffic_config{config}_resident.json"), "kr_verify", KERNEL_SRC
     return os.path.join(ROOT, "profiles", f"traffic_config{config}.json"), "k1_stats", KERNEL_SRC
 
 
-def load_traffic(config: str):
-    """HBM traffic per launch from the committed PMC summary, if it was taken on this kernel."""
-    path, _, files = _traffic_target(config)
+KERNELS_STAGED = ("k1_stats", "k1_rows", "k5_verify")
+KERNELS_RESIDENT = ("kr_verify",)
+
+
+def load_traffic(config: str, knames=None):
+    """HBM traffic per call from the committed PMC summary, if it was taken on these kernel sources and on
+    the kernels the call launches: {"kernel_bytes": the first kernel's, "call_bytes": all of them,
+    "per_kernel": {name: bytes}}, or None."""
+    path, main, files = _traffic_target(config, resident=bool(knames) and tuple(knames) == KERNELS_RESIDENT)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
     if t.get("kernel_digest") != kernel_digest(files):
         return None
-    return t.get("bytes_per_launch")
+    per = {}
+    for name, v in t.get("kernels", {}).items():
+        short = name.split("<")[0].split("::")[-1]
+        per[short] = v["fetch_bytes"] + v["write_bytes"]
+    want = list(knames) if knames else [main]
+    if any(kn not in per for kn in want):
+        return None
+    return {"kernel_bytes": per[want[0]], "call_bytes": float(sum(per[kn] for kn in want)),
+            "per_kernel": {kn: per[kn] for kn in want}, "file": path}
+
+
+def _kernel_bytes(tr):
+    return tr["kernel_bytes"] if tr else None
+
+
+def timed_calls(step, n, samples, stream):
+    """n calls back to back in one timed region (device events around it), with events between `samples`
+    equal runs of them: (total ms, ms per call, host wall seconds, {median / min / max us per call})."""
+    import torch
+    samples = max(1, min(samples, n))
+    bounds = [round(j * n / samples) for j in range(samples + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(samples + 1)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    evs[0].record(stream)
+    for j in range(samples):
+        for i in range(bounds[j], bounds[j + 1]):
+            step(i)
+        evs[j + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    total = evs[0].elapsed_time(evs[-1])
+    per = [evs[j].elapsed_time(evs[j + 1]) / (bounds[j + 1] - bounds[j]) * 1e3 for j in range(samples)
+           if bounds[j + 1] > bounds[j]]
+    return total, total / n, wall, {"runs": len(per), "calls_per_run": n // samples,
+                                    "us_per_call_median": float(np.median(per)), "us_per_call_min": float(min(per)),
+                                    "us_per_call_max": float(max(per))}
+
+
+def read_stream_reference(dev, nbytes, reps=20):
+    """Median bandwidth of a plain 16-byte-load read of nbytes (rotating over buffers that together exceed
+    the last-level cache), from the probe library; None if it is not built."""
+    import ctypes
+    import torch
+    probe = os.path.join(ROOT, "rejection_sampling_verify_16_amd", "libsvprobe.so")
+    if not os.path.exists(probe):
+        return None
+    L = ctypes.CDLL(probe)
+    L.probe_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    L.probe_read_stream.restype = ctypes.c_int
+    nvec = nbytes // 16
+    nbuf = max(2, math.ceil(ROTATE_BYTES / max(nbytes, 1)))
+    bufs = [torch.empty(nvec * 16, dtype=torch.uint8, device=dev).fill_(j + 1) for j in range(nbuf)]
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks = cus * 8
+    sink = torch.zeros(blocks, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    per = []
+    for it in range(reps + 3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        rc = L.probe_read_stream(ctypes.c_void_p(bufs[it % nbuf].data_ptr()), nvec, ctypes.c_void_p(sink.data_ptr()),
+                                 blocks, ctypes.c_void_p(stream.cuda_stream))
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if rc != 0:
+            return None
+        if it >= 3:
+            per.append(e0.elapsed_time(e1))
+    ms = float(np.median(per))
+    del bufs
+    torch.cuda.empty_cache()
+    gbps = nvec * 16 / (ms * 1e-3) / 1e9
+    return {"bytes": nvec * 16, "us_median": ms * 1e3, "GBps": gbps, "pct_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS,
+            "kernel": "k_read_stream", "grid": [blocks, 256]}
 
 
 def main():
@@ -86,8 +176,15 @@ def main():
     ap.add_argument("--configs", default="1,2,4a,4b,5",
                     help="other workloads timed after the headline one (comma list; empty: none)")
     ap.add_argument("--configs-only", action="store_true", help="only the other workloads")
+    ap.add_argument("--path", choices=["auto", "staged", "resident"], default="auto",
+                    help="the library's path for the verify calls (auto: its own choice)")
+    ap.add_argument("--samples", type=int, default=10, help="runs the timed calls are split into (median / min)")
+    ap.add_argument("--no-read-stream", action="store_true", help="skip the read-only stream reference")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
-                    help="only run a plain device-to-device copy of this many MiB, 5 times (PMC calibration)")
+                    help="only run a plain device-to-device copy of this many MiB, 5 times (PMC calibration of "
+                         "WRITE_SIZE; with --read-probe: a plain read instead, for FETCH_SIZE)")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="with --copy-probe-mb: the probe library's read-only stream instead of the copy")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="summarise rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of this benchmark and of the copy "
                          "probe into profiles/traffic_config<C>.json (no GPU needed)")
@@ -112,6 +209,12 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe_mb and args.read_probe:
+        n = args.copy_probe_mb << 20
+        for _ in range(5):
+            rs = read_stream_reference(dev, n, reps=1)
+        print(json.dumps({"read_probe_bytes": n, "reads": 5 * 4, "last": rs}), flush=True)
+        return
     if args.copy_probe_mb:
         n = args.copy_probe_mb << 20
         a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -142,8 +245,14 @@ def main():
     stream = torch.cuda.current_stream(dev)
     offsets = w.offsets
 
+    path = {"auto": sv.PATH_AUTO, "staged": sv.PATH_STAGED, "resident": sv.PATH_RESIDENT}[args.path]
+
     def step(i, timing=None):
         t_, d_ = sets[i % n_sets]
+        if timing is None and path != sv.PATH_AUTO:
+            timing = sv.KernelTiming(path=path)
+        elif timing is not None:
+            timing.path = path
         sv.spec_verify(t_, d_, drafts, T, K, P, seed=w.seed, offset=offsets[i % len(offsets)], out=out,
                        workspace=ws, stream=stream, raw=args.raw_logprobs, timing=timing)
 
@@ -151,30 +260,19 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # ---- timed region: exactly `steps` calls ----
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    ms = e0.elapsed_time(e1)
-    ms_per_step = ms / args.steps
+    # ---- timed region: exactly `steps` calls, with events between equal runs of them ----
+    ms, ms_per_step, wall, samples = timed_calls(step, args.steps, args.samples, stream)
 
     # ---- per-kernel durations: HIP events recorded by the library around each of its kernels,
     # on the stream the kernels run on, over a second pass of the same `steps` calls ----
     kms = kernel_durations(sv, step, args.steps, stream)
-    k1_ms = kms[0]
-    km_ms = kms[1] if len(kms) > 1 else 0.0
-    k5_ms = kms[2] if len(kms) > 2 else 0.0
+    knames = KERNELS_RESIDENT if len(kms) == 1 else KERNELS_STAGED[:len(kms)]
     logit_bytes = w.logit_bytes
     draft_pos_bytes = w.B * 2 * w.k * w.V * (2 if bf16 else 4)  # rows K5 re-reads (bonus row aside)
+    k1_ms = kms[0]  # the kernel that streams every logit once: K1, or the resident kernel
     k1_gbps = logit_bytes / (k1_ms * 1e-3) / 1e9
     rows_per_s = B / (ms_per_step * 1e-3)
-    traffic = load_traffic(args.config)
+    tr = load_traffic(args.config, knames)
 
     result = {
         "metric": METRIC,
@@ -190,8 +288,9 @@ def main():
         "dtype": "bf16" if bf16 else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "k": k, "V": V, "logit_bytes_per_step": logit_bytes,
-                   "raw_logprobs": bool(args.raw_logprobs),
+                   "raw_logprobs": bool(args.raw_logprobs), "path": args.path,
                    "rotating_input_sets": n_sets},
+        "samples": samples,
         "logits_GBps": logit_bytes / (ms_per_step * 1e-3) / 1e9,
         "pct_hbm_peak": 100.0 * logit_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "wall_s": wall,
@@ -201,21 +300,29 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": k1_gbps / HBM_PEAK_GBPS,
-            "traffic": traffic,
-            "kernel": "k1_stats",
+            "traffic": tr["kernel_bytes"] if tr else None,
+            "kernel": knames[0],
             "kernel_ms_mean": k1_ms,
             "algorithmic_bytes": logit_bytes,
         },
-        "kernels": {
-            "k1_stats": {"ms_mean": k1_ms, "bytes": logit_bytes, "GBps": k1_gbps},
-            # per-row merges of K1's slice partials and the kept thresholds (re-reads only rows whose
-            # threshold needs a count over the whole row)
-            "k1_rows": {"ms_mean": km_ms},
-            # K5 streams the draft-position rows of batch rows it cannot finish from recorded
-            # candidates; this is its traffic when every row is streamed (an upper bound)
-            "k5_verify": {"ms_mean": k5_ms, "bytes_all_rows_streamed": draft_pos_bytes},
-        },
+        "kernels": {knames[j]: {"ms_mean": kms[j]} for j in range(len(kms))},
     }
+    result["kernels"][knames[0]].update({"bytes": logit_bytes, "GBps": k1_gbps})
+    if "k5_verify" in result["kernels"]:
+        # K5 streams the draft-position rows of batch rows it cannot finish from recorded candidates; this
+        # is its traffic when every row is streamed (an upper bound)
+        result["kernels"]["k5_verify"]["bytes_all_rows_streamed"] = draft_pos_bytes
+    if tr:
+        result["traffic"] = {"whole_call_bytes": tr["call_bytes"], "algorithmic_bytes": logit_bytes,
+                             "whole_call_ratio": tr["call_bytes"] / logit_bytes, "per_kernel": tr["per_kernel"],
+                             "source": os.path.relpath(tr["file"], ROOT)}
+    else:
+        result["traffic"] = None
+    if not args.no_read_stream:
+        rs = read_stream_reference(dev, logit_bytes)
+        if rs:
+            rs["call_pct_of_read_stream"] = 100.0 * result["logits_GBps"] / rs["GBps"]
+        result["read_stream"] = rs
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, drafts.cpu().numpy(), args.cpu_seconds)
@@ -279,27 +386,25 @@ def bench_configs(args, dev):
         for i in range(10):
             step(i)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(n):
-            step(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / n
+        _, ms, _, samples = timed_calls(step, n, args.samples, stream)
         kms = kernel_durations(sv, step, n, stream)
-        k1_ms = kms[0]
-        km_ms = kms[1] if len(kms) > 1 else 0.0
-        k5_ms = kms[2] if len(kms) > 2 else 0.0
+        knames = KERNELS_RESIDENT if len(kms) == 1 else KERNELS_STAGED[:len(kms)]
         acc = out["accept_len"].float().mean().item()
         gbps = w.logit_bytes / (ms * 1e-3) / 1e9
-        k1_gbps = w.logit_bytes / (k1_ms * 1e-3) / 1e9
+        k1_gbps = w.logit_bytes / (kms[0] * 1e-3) / 1e9
         res[name] = {
             "workload": w.name, "B": w.B, "k": w.k, "V": w.V, "dtype": w.dtype, "calls": n,
-            "us_per_call": ms * 1e3, "verified_rows_per_s": w.B / (ms * 1e-3), "logit_bytes_per_call": w.logit_bytes,
-            "logits_GBps": gbps, "pct_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS,
-            "kernels_us": {"k1_stats": k1_ms * 1e3, "k1_rows": km_ms * 1e3, "k5_verify": k5_ms * 1e3},
-            "k1_stats_roofline_frac": k1_gbps / HBM_PEAK_GBPS, "mean_accept_len": acc,
+            "us_per_call": ms * 1e3, "samples": samples, "verified_rows_per_s": w.B / (ms * 1e-3),
+            "logit_bytes_per_call": w.logit_bytes, "logits_GBps": gbps, "pct_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS,
+            "kernels_us": {knames[j]: kms[j] * 1e3 for j in range(len(kms))},
+            "stream_kernel_roofline_frac": k1_gbps / HBM_PEAK_GBPS, "mean_accept_len": acc,
         }
+        tr = load_traffic(name, knames)
+        if tr:
+            res[name]["traffic"] = {"whole_call_bytes": tr["call_bytes"], "whole_call_ratio": tr["call_bytes"] / w.logit_bytes,
+                                    "per_kernel": tr["per_kernel"], "source": os.path.relpath(tr["file"], ROOT)}
+        if not args.no_cpu_baseline:
+            res[name]["oracle_margin"] = oracle_margins(w, drafts.cpu().numpy())
         print(f"[bench] config {name}: {ms * 1e3:.1f} us/call", file=sys.stderr, flush=True)
         del sets, out, ws, tgt0, drf0
         torch.cuda.empty_cache()
@@ -333,13 +438,7 @@ def bench_tree(args, dev):
     for i in range(10):
         step(i)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(n):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / n
+    _, ms, _, samples = timed_calls(step, n, args.samples, stream)
     k1_ms, km_ms, kt_ms = kernel_durations(sv, step, n, stream)
     gbps = w.logit_bytes / (k1_ms * 1e-3) / 1e9
     acc = out["accept_len"].cpu().numpy()
@@ -349,6 +448,7 @@ def bench_tree(args, dev):
         "unit": "verified rows/s",
         "steps": n,
         "ms_per_step": ms,
+        "samples": samples,
         "dtype": "bf16",
         "config": {"workload": w.name, "B": w.B, "N": w.N, "V": w.V, "parents": list(W.EAGLE_TREE_9),
                    "logit_bytes_per_step": w.logit_bytes, "rotating_input_sets": n_sets},
@@ -361,7 +461,7 @@ def bench_tree(args, dev):
     if not args.no_cpu_baseline:
         import oracle
         o = oracle.get()
-        threads = min(os.cpu_count() or 1, 16)
+        threads = min(host_cores(), 16)
         calls, t0 = 0, time.perf_counter()
         while True:
             o.tree_verify(w.target, w.parent, w.node_tokens, w.temperature, w.top_k, w.top_p, seed=w.seed,
@@ -371,7 +471,7 @@ def bench_tree(args, dev):
             if el >= min(args.cpu_seconds, 5.0) or calls >= 200:
                 break
         res["cpu_baseline"] = {"value": w.B * calls / el, "unit": "verified rows/s", "cores": threads,
-                               "kind": "oracle",
+                               "host_cores": host_cores(), "kind": "oracle",
                                "sample": f"{calls} full calls of the tree workload ({w.B} rows each), {el:.1f} s"}
     return res
 
@@ -428,7 +528,7 @@ def bench_commit(args, dev):
                                         "row_bytes": int(t.verify_state[0, 0, 0].nbytes)} for t in w.tensors},
                    "committed_rows": int(((w.accept_len >= 1) & (w.accept_len <= w.k + 1)).sum())},
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": gbps / HBM_PEAK_GBPS, "traffic": load_traffic("commit"), "kernel": "k_commit",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": _kernel_bytes(load_traffic("commit")), "kernel": "k_commit",
                      "kernel_ms_mean": ms_kernel, "algorithmic_bytes": moved},
     }
     # the same commit by slot numbers: verify would have written each position's state into a scratch slot
@@ -472,8 +572,16 @@ def bench_commit(args, dev):
     return res
 
 
+def _kernel_name(full: str) -> str:
+    """A kernel's name without its parameter list (and without an anonymous-namespace prefix)."""
+    full = full.replace("(anonymous namespace)::", "")
+    return full.split("(")[0]
+
+
 def _pmc_per_kernel(run_dir, counter):
-    """Mean value of one counter per kernel name over the dispatches of a rocprofv3 --pmc CSV run."""
+    """Median value of one counter per kernel name over the dispatches of a rocprofv3 --pmc CSV run (the
+    median: a run's first dispatch of a kernel can belong to a different-sized call, such as the drafts'
+    own sampling call)."""
     import csv
     import glob
     files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
@@ -483,9 +591,9 @@ def _pmc_per_kernel(run_dir, counter):
     for r in csv.DictReader(open(files[0])):
         if r.get("Counter_Name") != counter:
             continue
-        name = r.get("Kernel_Name", "").split("(")[0]
+        name = _kernel_name(r.get("Kernel_Name", ""))
         vals.setdefault(name, []).append(float(r["Counter_Value"]))
-    return {k: (float(np.mean(v)), len(v)) for k, v in vals.items()}
+    return {k: (float(np.median(v)), len(v)) for k, v in vals.items()}
 
 
 def pmc_report(dirs):
@@ -498,7 +606,7 @@ def pmc_report(dirs):
         if not files:
             raise SystemExit(f"no counter_collection.csv under {d}")
         for r in csv.DictReader(open(files[0])):
-            name = r.get("Kernel_Name", "").split("(")[0]
+            name = _kernel_name(r.get("Kernel_Name", ""))
             if "sv::" not in name:
                 continue
             vals.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
@@ -512,8 +620,9 @@ def pmc_report(dirs):
 
 
 def pmc_summary(args):
-    """HBM traffic of the statistics kernel from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by
-    the ratio of true bytes to the same counter's reading for a plain copy kernel of known size."""
+    """HBM traffic per kernel from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by the ratio of
+    true bytes to the same counter's reading for a plain kernel of known size (the largest-reading kernel of
+    each calibration run: a read-only stream for FETCH_SIZE, a copy for WRITE_SIZE, both --copy-probe-mb)."""
     fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.pmc_summary
     copy_bytes = (args.copy_probe_mb or 256) << 20
 
@@ -527,9 +636,10 @@ def pmc_summary(args):
     w_scale = copy_bytes / (cw_kib * 1024.0)
     fetch = _pmc_per_kernel(fetch_dir, "FETCH_SIZE")
     write = _pmc_per_kernel(write_dir, "WRITE_SIZE")
-    path, main_kernel, files = _traffic_target(args.config)
-    out = {"config": args.config, "kernel_digest": kernel_digest(files), "copy_probe_bytes": copy_bytes,
-           "copy_kernel": cf_name, "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
+    path, main_kernel, files = _traffic_target(args.config, resident=args.path == "resident")
+    out = {"config": args.config, "path": args.path, "kernel_digest": kernel_digest(files), "copy_probe_bytes": copy_bytes,
+           "copy_kernel": cf_name, "fetch_scale": f_scale, "write_scale": w_scale,
+           "fetch_scale_kernel": cf_name, "write_scale_kernel": cw_name, "kernels": {}}
     for name, (kib, n) in fetch.items():
         if "sv::" not in name:
             continue
@@ -567,11 +677,45 @@ def kernel_durations(sv, step, n, stream):
     return tuple(float(np.mean(x)) for x in per)
 
 
-def cpu_baseline(w, drafts, seconds):
-    """The CPU oracle, as it stands, on whole calls of the same workload until ~`seconds` pass."""
+# Margin tolerances of the parity bar: accept test |u - p/q|, Gumbel top-2 gap, top-p |M / Z_K - P|.
+MARGIN_ACCEPT, MARGIN_GAP, MARGIN_TOPP = 1e-5, 1e-5, 1e-6
+
+
+def host_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def oracle_margins(w, drafts, offsets=None):
+    """The CPU oracle's margin rows of a workload (cpu_baseline leg): batch rows whose outcome a correct
+    rounding could change (exempt from the bit-exact comparison, checked against the oracle's alternative
+    resolutions by the parity tests), and its sentinel rows, over the given offsets (default: the first)."""
     import oracle
     o = oracle.get()
-    threads = min(os.cpu_count() or 1, 16)
+    offs = offsets if offsets is not None else [w.offsets[0]]
+    margin = sentinel = 0
+    t0 = time.perf_counter()
+    for off in offs:
+        r = o.spec_verify(w.target, w.draft, drafts, w.temperature, w.top_k, w.top_p, seed=w.seed, offset=off,
+                          num_threads=min(host_cores(), 16))
+        m = r.margin_rows(MARGIN_ACCEPT, MARGIN_GAP, MARGIN_TOPP) & ~r.sentinel
+        margin += int(m.sum())
+        sentinel += int(r.sentinel.sum())
+    return {"margin_rows": margin, "sentinel_rows": sentinel, "batch_rows": w.B * len(offs), "offsets": len(offs),
+            "tolerances": {"accept": MARGIN_ACCEPT, "gumbel_gap": MARGIN_GAP, "top_p": MARGIN_TOPP},
+            "seconds": time.perf_counter() - t0}
+
+
+def cpu_baseline(w, drafts, seconds):
+    """The CPU oracle, as it stands, on whole calls of the same workload until ~`seconds` pass (all usable
+    host cores, at most 16), a one-thread figure on a bounded sample of its batch rows, and the oracle's
+    margin rows of the workload."""
+    import oracle
+    o = oracle.get()
+    cores = host_cores()
+    threads = min(cores, 16)
     calls, t0 = 0, time.perf_counter()
     while True:
         o.spec_verify(w.target, w.draft, drafts, w.temperature, w.top_k, w.top_p, seed=w.seed,
@@ -580,8 +724,23 @@ def cpu_baseline(w, drafts, seconds):
         el = time.perf_counter() - t0
         if el >= seconds or calls >= 1000:
             break
-    return {"value": w.B * calls / el, "unit": "verified rows/s", "cores": threads, "kind": "oracle",
-            "sample": f"{calls} full calls of the benchmark workload ({w.B} batch rows each), {el:.1f} s"}
+    # one thread, on the first few batch rows (the same rows every run)
+    nb = min(w.B, 8)
+    calls1, t1 = 0, time.perf_counter()
+    while True:
+        o.spec_verify(w.target[:nb], w.draft[:nb], drafts[:nb], w.temperature[:nb], w.top_k[:nb], w.top_p[:nb],
+                      seed=w.seed, offset=w.offsets[0], num_threads=1)
+        calls1 += 1
+        el1 = time.perf_counter() - t1
+        if el1 >= min(seconds, 5.0) or calls1 >= 1000:
+            break
+    return {"value": w.B * calls / el, "unit": "verified rows/s", "cores": threads, "host_cores": cores,
+            "kind": "oracle",
+            "sample": f"{calls} full calls of the benchmark workload ({w.B} batch rows each), {el:.1f} s, "
+                      f"{threads} threads",
+            "one_thread": {"value": nb * calls1 / el1, "unit": "verified rows/s", "cores": 1,
+                           "sample": f"{calls1} calls on the first {nb} batch rows, {el1:.1f} s"},
+            "margin": oracle_margins(w, drafts)}
 
 
 if __name__ == "__main__":

@@ -1542,13 +1542,18 @@ __device__ inline float kept_p(float f, float m, float c, float lz, float fthr) 
 // are only compared with each other.
 __device__ inline float race_key(float w, uint32_t word) { return w * __builtin_amdgcn_rcpf(exp_race_E2(word)); }
 
-// Race candidate update: larger key wins, the lower index on an exact tie.
+// Race candidate update: larger key wins, the lower index on an exact tie (selects, no branch).
 __device__ inline void race_take(float& best, int& bidx, float& bval, float key, int idx, float val) {
-  if (key > best || (key == best && idx < bidx)) {
-    best = key;
-    bidx = idx;
-    bval = val;
-  }
+  const bool take = (key > best) | ((key == best) & (idx < bidx));  // bitwise: no short-circuit branches
+  best = take ? key : best;
+  bidx = take ? idx : bidx;
+  bval = take ? val : bval;
+}
+
+// Race key of weight w with stream word `word`, or -1 (never taken: keys of positive weights are positive)
+// when w is 0: computed for every entry of a group, so that no entry branches.
+__device__ inline float race_key_or_none(float w, uint32_t word) {
+  return w > 0.0f ? race_key(w, word) : -1.0f;
 }
 
 // Workgroup race winner (key, index, logit) into every thread.
@@ -1777,10 +1782,8 @@ __device__ __forceinline__ void race_slice(const Params& p, const uint4 (&va)[VP
       const uint4 w4 = philox10(make_uint4((uint32_t)x >> 2, sb, (tag << 24) | sj, p.offset), p.key0, p.key1);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if (w[e] > 0.0f) {
-          const uint32_t word = e == 0 ? w4.x : e == 1 ? w4.y : e == 2 ? w4.z : w4.w;
-          race_take(best, bidx, bval, race_key(w[e], word), x + e, E::get(a, g + e));
-        }
+        const uint32_t word = e == 0 ? w4.x : e == 1 ? w4.y : e == 2 ? w4.z : w4.w;
+        race_take(best, bidx, bval, race_key_or_none(w[e], word), x + e, E::get(a, g + e));
       }
     }
   }
@@ -2381,9 +2384,10 @@ __global__ __launch_bounds__(NT) void k_tree(Params p) {
 // ---------------------------------------------------------------------------------------------
 constexpr int RMAXK = 4;      // the resident kernel serves k = 1..RMAXK
 constexpr int RMAXWG = 1024;  // the largest resident grid the workspace is sized for (a GPU with <= 1024 CUs)
-// The library's own choice takes the resident path only up to this many vectors per thread and row (its
-// single workgroup per CU has too few waves to hide latency on longer slices, where the staged path wins).
-constexpr int RAUTO_NV = 3;
+// The library's own choice takes the resident path only up to this many vectors per thread and row: none
+// at present (measured on MI355X, the staged path is as fast or faster on every workload that fits: its
+// single workgroup per CU has too few waves to hide the latency of its exchanges and reductions).
+constexpr int RAUTO_NV = 0;
 
 // Workspace of the resident kernel with S slices per batch row.
 static size_t resident_bytes(int32_t B, int32_t k, int32_t S) {

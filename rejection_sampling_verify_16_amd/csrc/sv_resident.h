@@ -719,8 +719,7 @@ __device__ __forceinline__ void r_race8(const RParams& p, int b, int j_pos, int 
   philox10x2_loop(c0, c1, p.key0, p.key1);
   const uint32_t words[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
-    if (wr[e] > 0.0f) race_take(best, bidx, bval, race_key(wr[e], words[e]), x + e, BF16::get(wa, e));
+  for (int e = 0; e < 8; ++e) race_take(best, bidx, bval, race_key_or_none(wr[e], words[e]), x + e, BF16::get(wa, e));
 }
 
 // Gumbel-max candidates of one 4-logit group (weights wr, logits of the row drawn from at g of vector wa).
