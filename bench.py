@@ -636,8 +636,9 @@ def pmc_summary(args):
     w_scale = copy_bytes / (cw_kib * 1024.0)
     fetch = _pmc_per_kernel(fetch_dir, "FETCH_SIZE")
     write = _pmc_per_kernel(write_dir, "WRITE_SIZE")
-    path, main_kernel, files = _traffic_target(args.config, resident=args.path == "resident")
-    out = {"config": args.config, "path": args.path, "kernel_digest": kernel_digest(files), "copy_probe_bytes": copy_bytes,
+    path_opt = getattr(args, "path", "auto")
+    path, main_kernel, files = _traffic_target(args.config, resident=path_opt == "resident")
+    out = {"config": args.config, "path": path_opt, "kernel_digest": kernel_digest(files), "copy_probe_bytes": copy_bytes,
            "copy_kernel": cf_name, "fetch_scale": f_scale, "write_scale": w_scale,
            "fetch_scale_kernel": cf_name, "write_scale_kernel": cw_name, "kernels": {}}
     for name, (kib, n) in fetch.items():
