@@ -61,6 +61,8 @@ def _traffic_target(config: str, resident: bool = False):
     resident kernel's own summary)."""
     if config == "commit":
         return os.path.join(ROOT, "profiles", "traffic_commit.json"), "k_commit", COMMIT_SRC
+    if config == "tree":
+        return os.path.join(ROOT, "profiles", "traffic_tree.json"), "k1_stats", KERNEL_SRC
     if resident:
         return os.path.join(ROOT, "profiles", f"traffic_config{config}_resident.json"), "kr_verify", KERNEL_SRC
     return os.path.join(ROOT, "profiles", f"traffic_config{config}.json"), "k1_stats", KERNEL_SRC
@@ -120,9 +122,10 @@ def timed_calls(step, n, samples, stream):
                                     "us_per_call_max": float(max(per))}
 
 
-def read_stream_reference(dev, nbytes, reps=20):
-    """Median bandwidth of a plain 16-byte-load read of nbytes (rotating over buffers that together exceed
-    the last-level cache), from the probe library; None if it is not built."""
+def read_stream_reference(dev, nbytes, runs=8, per_run=10):
+    """Bandwidth of a plain 16-byte-load read of nbytes from the probe library, timed the way the verify
+    calls are: `runs` runs of `per_run` launches back to back between events, rotating over buffers that
+    together exceed the last-level cache; the median run gives the figure.  None if the probe is not built."""
     import ctypes
     import torch
     probe = os.path.join(ROOT, "rejection_sampling_verify_16_amd", "libsvprobe.so")
@@ -138,24 +141,33 @@ def read_stream_reference(dev, nbytes, reps=20):
     blocks = cus * 8
     sink = torch.zeros(blocks, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
+
+    def launch(i):
+        return L.probe_read_stream(ctypes.c_void_p(bufs[i % nbuf].data_ptr()), nvec, ctypes.c_void_p(sink.data_ptr()),
+                                   blocks, ctypes.c_void_p(stream.cuda_stream))
+
+    for i in range(2 * nbuf):  # warm-up
+        if launch(i) != 0:
+            return None
+    torch.cuda.synchronize()
     per = []
-    for it in range(reps + 3):
+    i = 0
+    for _ in range(runs):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        rc = L.probe_read_stream(ctypes.c_void_p(bufs[it % nbuf].data_ptr()), nvec, ctypes.c_void_p(sink.data_ptr()),
-                                 blocks, ctypes.c_void_p(stream.cuda_stream))
+        for _ in range(per_run):
+            if launch(i) != 0:
+                return None
+            i += 1
         e1.record(stream)
         torch.cuda.synchronize()
-        if rc != 0:
-            return None
-        if it >= 3:
-            per.append(e0.elapsed_time(e1))
+        per.append(e0.elapsed_time(e1) / per_run)
     ms = float(np.median(per))
     del bufs
     torch.cuda.empty_cache()
     gbps = nvec * 16 / (ms * 1e-3) / 1e9
     return {"bytes": nvec * 16, "us_median": ms * 1e3, "GBps": gbps, "pct_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS,
-            "kernel": "k_read_stream", "grid": [blocks, 256]}
+            "kernel": "k_read_stream", "grid": [blocks, 256], "timing": f"{runs} runs of {per_run} back-to-back launches"}
 
 
 def main():
@@ -163,7 +175,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--config", default="3", help="workload: 1, 2, 3, 4a, 4b, 5 (with --pmc-summary also: commit)")
+    ap.add_argument("--config", default="3",
+                    help="workload: 1, 2, 3, 4a, 4b, 5 (with --pmc-summary also: commit, tree)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--raw-logprobs", action="store_true",
                     help="time spec_verify_raw (also the raw logprobs of the committed tokens)")
@@ -211,9 +224,8 @@ def main():
     torch.cuda.set_device(dev)
     if args.copy_probe_mb and args.read_probe:
         n = args.copy_probe_mb << 20
-        for _ in range(5):
-            rs = read_stream_reference(dev, n, reps=1)
-        print(json.dumps({"read_probe_bytes": n, "reads": 5 * 4, "last": rs}), flush=True)
+        rs = read_stream_reference(dev, n, runs=2, per_run=5)
+        print(json.dumps({"read_probe_bytes": n, "result": rs}), flush=True)
         return
     if args.copy_probe_mb:
         n = args.copy_probe_mb << 20
@@ -458,6 +470,14 @@ def bench_tree(args, dev):
                      "kernel_ms_mean": k1_ms, "algorithmic_bytes": w.logit_bytes},
         "kernels": {"k1_stats": {"ms_mean": k1_ms}, "k1_rows": {"ms_mean": km_ms}, "k_tree": {"ms_mean": kt_ms}},
     }
+    tr = load_traffic("tree", ("k1_stats", "k1_rows", "k_tree"))
+    if tr:
+        res["roofline"]["traffic"] = tr["kernel_bytes"]
+        res["traffic"] = {"whole_call_bytes": tr["call_bytes"], "algorithmic_bytes": w.logit_bytes,
+                          "whole_call_ratio": tr["call_bytes"] / w.logit_bytes, "per_kernel": tr["per_kernel"],
+                          "source": os.path.relpath(tr["file"], ROOT)}
+    else:
+        res["traffic"] = None
     if not args.no_cpu_baseline:
         import oracle
         o = oracle.get()
