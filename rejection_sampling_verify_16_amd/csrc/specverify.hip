@@ -211,7 +211,7 @@ __device__ inline bool arrive_last(uint32_t* counter, uint32_t total, int* flag)
   __syncthreads();
   if (total == 1) return true;  // the only arrival: no round trip (the counter stays at 0)
   if (threadIdx.x == 0) *flag = (atomicAdd(counter, 1u) == total - 1) ? 1 : 0;
-  lds_sync();
+  __syncthreads();
   return *flag != 0;
 }
 
@@ -274,7 +274,7 @@ __device__ __forceinline__ void block_stats(RedSmem& rs, float& m, int& a, float
     rs.g[wave] = s;
     rs.u[wave] = fl;
   }
-  lds_sync();
+  __syncthreads();
   m = rs.f[0];
   a = rs.i[0];
   s = rs.g[0];
@@ -286,7 +286,7 @@ __device__ __forceinline__ void block_stats(RedSmem& rs, float& m, int& a, float
     s = ss;
     fl |= rs.u[w];
   }
-  lds_sync();
+  __syncthreads();
 }
 
 // Workgroup NaN-propagating max into every thread.
@@ -295,10 +295,10 @@ __device__ __forceinline__ float block_nan_max(RedSmem& rs, float m) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = nan_max(m, __shfl_xor(m, o, 64));
   if (lane == 0) rs.f[wave] = m;
-  lds_sync();
+  __syncthreads();
   m = rs.f[0];
   for (int w = 1; w < NWAVE; ++w) m = nan_max(m, rs.f[w]);
-  lds_sync();
+  __syncthreads();
   return m;
 }
 
@@ -309,11 +309,11 @@ __device__ __forceinline__ void block_maxarg(RedSmem& rs, float& m, int& a) {
     rs.f[wave] = m;
     rs.i[wave] = a;
   }
-  lds_sync();
+  __syncthreads();
   m = rs.f[0];
   a = rs.i[0];
   for (int w = 1; w < NWAVE; ++w) maxarg_combine(m, a, rs.f[w], rs.i[w]);
-  lds_sync();
+  __syncthreads();
 }
 
 // Workgroup sum into every thread.
@@ -322,10 +322,10 @@ __device__ __forceinline__ uint32_t block_sum_u32(RedSmem& rs, uint32_t v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   if (lane == 0) rs.u[wave] = v;
-  lds_sync();
+  __syncthreads();
   uint32_t t = 0;
   for (int w = 0; w < NWAVE; ++w) t += rs.u[w];
-  lds_sync();
+  __syncthreads();
   return t;
 }
 
@@ -334,10 +334,10 @@ __device__ __forceinline__ uint32_t block_max_u32(RedSmem& rs, uint32_t v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor(v, o, 64));
   if (lane == 0) rs.u[wave] = v;
-  lds_sync();
+  __syncthreads();
   uint32_t t = 0;
   for (int w = 0; w < NWAVE; ++w) t = max(t, rs.u[w]);
-  lds_sync();
+  __syncthreads();
   return t;
 }
 
@@ -346,10 +346,10 @@ __device__ __forceinline__ int block_first(RedSmem& rs, bool pred) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int fl = first_lane(pred);
   if (lane == 0) rs.i[wave] = fl < 64 ? wave * 64 + fl : NT;
-  lds_sync();
+  __syncthreads();
   int r = NT;
   for (int w = 0; w < NWAVE; ++w) r = min(r, rs.i[w]);
-  lds_sync();
+  __syncthreads();
   return r;
 }
 
@@ -414,9 +414,9 @@ __device__ __forceinline__ void row_cutoff(RadixSmem& sm, RedSmem& rs, const uin
     for (int lev = 0; lev < LEVELS; ++lev) {
       sm.hcnt[tid] = 0;
       sm.hmass[tid] = 0;
-      lds_sync();
+      __syncthreads();
       radix_hist<E, true>(sm, src, nvec, lev, prefix, 0u, m, c);
-      lds_sync();
+      __syncthreads();
       const int d = 255 - tid;  // thread t scans bins in descending key order
       const uint32_t cnt = sm.hcnt[d];
       const unsigned long long ms = sm.hmass[d];
@@ -429,12 +429,12 @@ __device__ __forceinline__ void row_cutoff(RadixSmem& sm, RedSmem& rs, const uin
         sm.sel_mexcl = minc - ms;
         sm.sel_m = ms;
       }
-      lds_sync();
+      __syncthreads();
       need -= sm.sel_excl;
       mabove += sm.sel_mexcl;
       prefix = (prefix << 8) | sm.sel;
       if (lev == LEVELS - 1) zk = mabove + sm.sel_m;
-      lds_sync();
+      __syncthreads();
     }
     thr = prefix;
     have_zk = true;
@@ -446,18 +446,18 @@ __device__ __forceinline__ void row_cutoff(RadixSmem& sm, RedSmem& rs, const uin
     double target = 0.0;
     for (int lev = 0; lev < LEVELS; ++lev) {
       sm.hmass[tid] = 0;
-      lds_sync();
+      __syncthreads();
       radix_hist<E, false>(sm, src, nvec, lev, prefix, thr, m, c);
-      lds_sync();
+      __syncthreads();
       const int d = 255 - tid;
       const unsigned long long ms = sm.hmass[d];
       const unsigned long long minc = block_inclusive_scan<unsigned long long>(ms, rs.scan64);
       if (lev == 0) {
         if (!have_zk) {
           if (tid == NT - 1) sm.sel_m = minc;  // total kept mass
-          lds_sync();
+          __syncthreads();
           zk = sm.sel_m;
-          lds_sync();
+          __syncthreads();
         }
         target = (double)P * (double)zk;
       }
@@ -467,11 +467,11 @@ __device__ __forceinline__ void row_cutoff(RadixSmem& sm, RedSmem& rs, const uin
         sm.sel_mexcl = mexcl;
         sm.sel_m = ms;
       }
-      lds_sync();
+      __syncthreads();
       mabove += sm.sel_mexcl;
       prefix = (prefix << 8) | sm.sel;
       if (lev == LEVELS - 1) zk = mabove + sm.sel_m;
-      lds_sync();
+      __syncthreads();
     }
     thr = prefix;
   }
@@ -505,7 +505,7 @@ __device__ __forceinline__ bool select_run(const uint32_t* cnt, int n, uint32_t 
     ss.sel_k = -1;
     ss.sel_p = -1;
   }
-  lds_sync();
+  __syncthreads();
   unsigned long long zk = 0;
   int selk = -1;
   // chunks of 2 * NT entries, thread t owns entries 2t and 2t+1 of a chunk
@@ -534,11 +534,11 @@ __device__ __forceinline__ bool select_run(const uint32_t* cnt, int n, uint32_t 
         rs.u[0] = ic;
         rs.scan64[0] = im;
       }
-      lds_sync();
+      __syncthreads();
       ccarry = rs.u[0];
       mcarry = rs.scan64[0];
       const int sk = ss.sel_k;
-      lds_sync();
+      __syncthreads();
       if (sk >= 0) break;
     }
     selk = ss.sel_k;
@@ -567,10 +567,10 @@ __device__ __forceinline__ bool select_run(const uint32_t* cnt, int n, uint32_t 
         ss.zp = im;
       }
       if (tid == NT - 1) rs.scan64[0] = im;
-      lds_sync();
+      __syncthreads();
       mcarry = rs.scan64[0];
       const int sp = ss.sel_p;
-      lds_sync();
+      __syncthreads();
       if (sp >= 0) break;
     }
     selp = ss.sel_p;
@@ -672,10 +672,10 @@ __device__ __forceinline__ bool coarse_window(K1Smem& sm, float m, float c, floa
     sm.rs.scand[0] = U;
     sm.rs.u[0] = nin;
   }
-  lds_sync();
+  __syncthreads();
   const double Utot = sm.rs.scand[0];
   const uint32_t ntot = sm.rs.u[0];
-  lds_sync();
+  __syncthreads();
   const double wunder = exp2(fmin(-((double)Am + NBC) / BRC - mc, 0.0));
   const double Ubelow = Utot - U + (double)((uint32_t)V - ntot) * wunder;
   const double t = (double)P * (double)Ztot;
@@ -700,7 +700,7 @@ __device__ __forceinline__ bool window_pass(K1Smem& sm, const uint8_t* row, int 
   const int width = (int)(khi - klo + 1);
   uint32_t* h = sm.u.mg.cnt;
   for (int j = tid; j < width; j += NT) h[j] = 0;
-  lds_sync();
+  __syncthreads();
   const uint4* src = (const uint4*)row;
   const int nvec = V / BF16::EPV;
   uint32_t acnt = 0;
@@ -736,10 +736,10 @@ __device__ __forceinline__ bool window_pass(K1Smem& sm, const uint8_t* row, int 
     sm.win[0] = tc;
     sm.rs.scan64[0] = tm;
   }
-  lds_sync();
+  __syncthreads();
   const uint32_t above_c = sm.win[0];
   const unsigned long long above_m = sm.rs.scan64[0];
-  lds_sync();
+  __syncthreads();
   int sel = -1;
   unsigned long long zsel = 0;
   if (!select_run(h, width, khi, m, c, sm.ss, sm.rs, above_c, above_m, ztot_fixed, useK, K, useP, P, sel, zsel))
@@ -765,7 +765,7 @@ __device__ __forceinline__ bool window_list_pass(K1Smem& sm, const uint8_t* row,
   uint32_t* ucnt = sm.u.mg.cnt + 2 * LCAP;   // their counts
   uint32_t* fcnt = sm.u.mg.cnt + 3 * LCAP;   // per entry: its key's count at the key's first occurrence, else 0
   if (tid == 0) sm.win[3] = 0;
-  lds_sync();
+  __syncthreads();
   const uint4* src = (const uint4*)row;
   const int nvec = V / BF16::EPV;
   uint32_t acnt = 0;
@@ -802,11 +802,11 @@ __device__ __forceinline__ bool window_list_pass(K1Smem& sm, const uint8_t* row,
     sm.win[0] = tc;
     sm.rs.scan64[0] = tm;
   }
-  lds_sync();
+  __syncthreads();
   const uint32_t above_c = sm.win[0];
   const unsigned long long above_m = sm.rs.scan64[0];
   const uint32_t nl = sm.win[3];
-  lds_sync();
+  __syncthreads();
   if (nl > (uint32_t)LCAP) return false;
   // first occurrences of each key with the key's count; then each one's rank among the distinct keys
   for (int e = tid; e < (int)nl; e += NT) {
@@ -819,7 +819,7 @@ __device__ __forceinline__ bool window_list_pass(K1Smem& sm, const uint8_t* row,
     }
     fcnt[e] = first ? count : 0u;
   }
-  lds_sync();
+  __syncthreads();
   uint32_t nd = 0;
   for (int e = tid; e < (int)nl; e += NT) {
     if (fcnt[e] == 0u) continue;
@@ -832,9 +832,9 @@ __device__ __forceinline__ bool window_list_pass(K1Smem& sm, const uint8_t* row,
   }
   const uint32_t ndist = block_inclusive_scan<uint32_t>(nd, sm.rs.scan32);
   if (tid == NT - 1) sm.win[2] = ndist;
-  lds_sync();
+  __syncthreads();
   const int n = (int)sm.win[2];
-  lds_sync();
+  __syncthreads();
   int sel = -1;
   unsigned long long zsel = 0;
   if (!select_run(ucnt, n, khi, m, c, sm.ss, sm.rs, above_c, above_m, ztot_fixed, useK, K, useP, P, sel, zsel, ucode))
@@ -869,7 +869,7 @@ __device__ __forceinline__ bool cand_select(const Params& p, K1Smem& sm, int r, 
   const unsigned long long om = __ballot(ovf);
   if (tid == 0) sm.win[2] = (uint32_t)om, sm.win[3] = (uint32_t)(om >> 32);
   if (ovf) sm.u.mg.ncs[tid] = 0;
-  lds_sync();
+  __syncthreads();
   const unsigned long long omask = ((unsigned long long)sm.win[3] << 32) | sm.win[2];
   for (int base = 0; base < S * NC; base += NT * 4) {
     uint32_t xs[4];
@@ -909,7 +909,7 @@ __device__ __forceinline__ bool cand_select(const Params& p, K1Smem& sm, int r, 
       }
     }
   }
-  lds_sync();
+  __syncthreads();
   int sel = -1;
   unsigned long long zsel = 0;
   if (!select_run(cnt, nb, keym, m, q.c, sm.ss, sm.rs, 0u, 0ull, 0.0, q.useK, q.K, q.useP, q.P, sel, zsel))
@@ -1013,7 +1013,7 @@ __device__ __forceinline__ void k1_merge(const Params& p, K1Smem& sm, int r, int
           }
         }
       }
-      lds_sync();
+      __syncthreads();
       int sel = -1;
       unsigned long long zsel = 0;
       if (select_run(cnt, WTOP, keym, m, q.c, sm.ss, sm.rs, 0u, 0ull, ztot, q.useK, q.K, q.useP, q.P, sel, zsel)) {
@@ -1046,7 +1046,7 @@ __device__ __forceinline__ void k1_merge(const Params& p, K1Smem& sm, int r, int
             }
           }
         }
-        lds_sync();
+        __syncthreads();
         uint32_t klo = 0, khi = 0;
         if (coarse_window(sm, m, q.c, q.P, sum, p.V, keym, klo, khi)) {
           if (khi - klo + 1u <= (uint32_t)WF)
@@ -1059,7 +1059,7 @@ __device__ __forceinline__ void k1_merge(const Params& p, K1Smem& sm, int r, int
       }
     }
     if (!done) {
-      lds_sync();
+      __syncthreads();
       row_cutoff<E>(sm.u.rad, sm.rs, row_ptr(p, b, i, esize), p.V, m, q.c, q.K, q.P, thr, Z);
     }
   }
@@ -1175,7 +1175,7 @@ __device__ __forceinline__ void k1_hist(K1Smem& sm, const uint4 (&v)[VPT], int n
       }
     }
   }
-  lds_sync();
+  __syncthreads();
   const uint32_t nflag = sm.u.st.nflag;
   if (nflag > (uint32_t)NFLAG) {
     if (tid == 0) sm.u.st.ncand = NC + 1;
@@ -1353,7 +1353,7 @@ __device__ __forceinline__ void k1_item(const Params& p, K1Smem& sm, int item, i
       sm.u.st.wmax[wave] = wm;
       sm.u.st.wfloor[wave] = wf;
     }
-    lds_sync();
+    __syncthreads();
     float ms = sm.u.st.wmax[0];
     uint32_t fk = sm.u.st.wfloor[0];
 #pragma unroll
@@ -1414,7 +1414,7 @@ __device__ __forceinline__ void k1_item(const Params& p, K1Smem& sm, int item, i
           k1_hist<VPT, false>(sm, v, nv, x0, ms, q.c, cbase, sum);
       }
       m = ms;  // the sums above are relative to the slice max
-      lds_sync();
+      __syncthreads();
       uint32_t* hw = p.hw1 + ((size_t)r * p.S1 + s) * (WTOP / 2);
       pst32(&hw[tid], sm.u.st.hw[2 * tid] | (sm.u.st.hw[2 * tid + 1] << 16));  // WTOP / 2 == NT
       const uint32_t nc = sm.u.st.ncand;
@@ -1571,12 +1571,12 @@ __device__ __forceinline__ void block_race(RedSmem& rs, float& best, int& bidx, 
     rs.i[wave] = bidx;
     rs.g[wave] = bval;
   }
-  lds_sync();
+  __syncthreads();
   best = rs.f[0];
   bidx = rs.i[0];
   bval = rs.g[0];
   for (int w = 1; w < NWAVE; ++w) race_take(best, bidx, bval, rs.f[w], rs.i[w], rs.g[w]);
-  lds_sync();
+  __syncthreads();
 }
 
 // Gumbel-max candidates over w(x) = exp2((l - m) c) on the kept entries of one 16-byte vector
@@ -1895,7 +1895,7 @@ __device__ __forceinline__ void k5_sparse(const Params& p, K5Smem& sm, int b, in
   if (pair && tid >= 64 && tid < 64 + S) sm.ncs2[tid - 64] = ld32(&p.ncand1[(size_t)Rd * S + tid - 64]);
   if (pair)
     for (int j = tid; j < HT; j += NT) sm.hidx[j] = -1;
-  lds_sync();
+  __syncthreads();
   const float mt = sm.m[rt], lt = sm.lz[rt];
   const uint32_t kt = thr_key(sm.fthr[rt]);
   uint32_t xt[NSLOT];
@@ -1922,7 +1922,7 @@ __device__ __forceinline__ void k5_sparse(const Params& p, K5Smem& sm, int b, in
         }
       }
     }
-    lds_sync();
+    __syncthreads();
   }
   // target kept entries: alpha (2^40 fixed point: the candidates' slot order varies from call to call,
   // and this sum does not depend on it) and the residual or bonus race
@@ -1971,7 +1971,7 @@ __device__ __forceinline__ void k5_sparse(const Params& p, K5Smem& sm, int b, in
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
     if (lane == 0) sm.asum[wave] = acc;
-    lds_sync();
+    __syncthreads();
     if (tid == 0) {
       unsigned long long v = 0;
       for (int w = 0; w < NWAVE; ++w) v += sm.asum[w];
@@ -2057,7 +2057,7 @@ __device__ __forceinline__ void k5_item(const Params& p, K5Smem& sm, int item, i
   // the others leave.  (Tested only after the loads above are issued, so that other rows do not wait
   // for the temperature before issuing them.)
   if (q.greedy && s != 0) return;
-  lds_sync();
+  __syncthreads();
   SV_TRACE5_AT(p, item, 1);
   bool ok = q.ok;
   for (int i = 0; i < k; ++i) ok = ok && sm.tok[i] >= 0 && sm.tok[i] < p.V;
@@ -2093,14 +2093,14 @@ __device__ __forceinline__ void k5_item(const Params& p, K5Smem& sm, int item, i
       const int fr = first_lane(reject);
       if (tid == 0) sm.n = fr < k ? fr : k;
     }
-    lds_sync();
+    __syncthreads();
     SV_TRACE5_AT(p, item, 2);
     const int n = sm.n;
     if constexpr (E::KEYBITS == 16) {
       if (sparse) {  // workgroup s finishes positions s, s + S5, ... from the candidates; no arrivals
         for (int pi = s; pi <= k; pi += p.S5) {
           k5_sparse<E>(p, sm, b, n, pi, q);
-          lds_sync();  // the shared tables are reused by the next position
+          __syncthreads();  // the shared tables are reused by the next position
         }
         if (s <= k) SV_TRACE5_AT(p, item, 3);
         SV_TRACE5_AT(p, item, 7);
@@ -2273,7 +2273,7 @@ __global__ __launch_bounds__(NT) void k_tree(Params p) {
     const int qq = tid & 3;
     sm.u[tid] = u24(qq == 0 ? w4.x : qq == 1 ? w4.y : qq == 2 ? w4.z : w4.w);
   }
-  lds_sync();
+  __syncthreads();
   // the tree: every node but the root has an earlier parent and a token in range; siblings differ
   bool bad = false;
   if (tid < N) {
@@ -2290,7 +2290,7 @@ __global__ __launch_bounds__(NT) void k_tree(Params p) {
     return;
   }
   if (tid >= 1 && tid < N) sm.gl[tid] = E::load1(row_ptr(p, b, sm.par[tid], esize), sm.tok[tid]);
-  lds_sync();
+  __syncthreads();
   if (tid == 0) {
     int u = 0, d = 0, leaf = 0;
     for (;;) {
@@ -2330,7 +2330,7 @@ __global__ __launch_bounds__(NT) void k_tree(Params p) {
     sm.stop = u;
     sm.leaf = leaf;
   }
-  lds_sync();
+  __syncthreads();
   const int u = sm.stop, d = sm.d;
   if (q.greedy) {
     if (s == 0) tree_emit(p, sm, b, q, sm.arg[u], sm.m[u]);
