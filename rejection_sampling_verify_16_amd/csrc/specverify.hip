@@ -1312,7 +1312,7 @@ __device__ __forceinline__ void k1_item(const Params& p, K1Smem& sm, int item, i
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
           const float f = E::get(v[u], e);
-          nan = nan || (f != f);
+          nan = nan | (f != f);  // bitwise: no branch per entry
           if (f > m) {
             m = f;
             a = x0 + j * EPV + e;
@@ -1592,7 +1592,7 @@ __device__ __forceinline__ void gumbel_vec(const uint4& v, int xbase, float m, f
     for (int e = 0; e < 4; ++e) {
       const float f = E::get(v, g + e);
       w[e] = f >= fthr ? fexp2((f - m) * c) : 0.0f;
-      any = any || w[e] > 0.0f;
+      any = any | (w[e] > 0.0f);
     }
     if (any) {
       const int x = xbase + g;
@@ -1759,7 +1759,7 @@ __device__ __forceinline__ void race_slice(const Params& p, const uint4 (&va)[VP
     const uint4 a = pick_vec<VPT>(va, u);
     bool kept = false;
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) kept = kept || E::get(a, e) >= tt;
+    for (int e = 0; e < EPV; ++e) kept = kept | (E::get(a, e) >= tt);  // bitwise: no branch per entry
     if (!kept) continue;
     const uint4 bv = RESID ? pick_vec<VPT>(vb, u) : a;
 #pragma unroll 1
@@ -1775,7 +1775,7 @@ __device__ __forceinline__ void race_slice(const Params& p, const uint4 (&va)[VP
         } else {
           w[e] = ft >= tt ? fexp2((ft - mt) * c) : 0.0f;
         }
-        any = any || w[e] > 0.0f;
+        any = any | (w[e] > 0.0f);
       }
       if (!any) continue;
       const int x = x0 + j * EPV + g;
@@ -1810,8 +1810,8 @@ __device__ __forceinline__ void k5_position(const Params& p, K5Smem& sm, int b, 
     if (TRUNC) {
       bool any = false;
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) any = any || E::get(va[u], e) >= tt;
-      live = live && any;
+      for (int e = 0; e < EPV; ++e) any = any | (E::get(va[u], e) >= tt);  // bitwise: no branch per entry
+      live = live & any;
     }
     if (live) {
 #pragma unroll
@@ -2191,7 +2191,7 @@ __device__ __forceinline__ void tree_resid_slice(const Params& p, const TreeSmem
     const uint4 a = pick_vec<VPT>(va, u);
     bool kept = false;
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) kept = kept || E::get(a, e) >= tt;
+    for (int e = 0; e < EPV; ++e) kept = kept | (E::get(a, e) >= tt);  // bitwise: no branch per entry
     if (!kept) continue;
 #pragma unroll 1
     for (int g = 0; g < EPV; g += 4) {
@@ -2204,7 +2204,7 @@ __device__ __forceinline__ void tree_resid_slice(const Params& p, const TreeSmem
         if (w[e] > 0.0f)
           for (int t = 0; t < nex; ++t)
             if (sm.ex[t] == x + e) w[e] = 0.0f;
-        any = any || w[e] > 0.0f;
+        any = any | (w[e] > 0.0f);
       }
       if (!any) continue;
       const uint4 w4 = philox10(make_uint4((uint32_t)x >> 2, sb, (1u << 24) | sj, p.offset), p.key0, p.key1);
