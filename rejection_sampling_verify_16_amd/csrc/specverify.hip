@@ -1745,11 +1745,12 @@ __device__ inline void load_slice(const uint8_t* row, int x0, int nv, uint4 (&v)
 // RESID: r(x) = max(p(x) - q(x), 0) of a target / draft pair; otherwise w(x) = exp2((l - m) c) on the
 // kept entries of one row.  Either is 0 wherever the (target) logit is below the kept threshold tt, so
 // a vector with no entry >= tt is skipped before any exp2.  Stream (tag, b, position j).  The winner's
-// (target) logit rides along.
-template <class E, int VPT, bool RESID>
+// (target) logit rides along.  ALPHA (with RESID): also adds min(p, q) of every entry to acc -- the
+// alpha partial sum of the position, from the same p and q.
+template <class E, int VPT, bool RESID, bool ALPHA = false>
 __device__ __forceinline__ void race_slice(const Params& p, const uint4 (&va)[VPT], const uint4 (&vb)[VPT], int x0, int nv, float c,
                            float mt, float lt, float tt, float md, float ld, float td, uint32_t tag, uint32_t sb,
-                           uint32_t sj, float& best, int& bidx, float& bval) {
+                           uint32_t sj, float& best, int& bidx, float& bval, float* acc = nullptr) {
   constexpr int EPV = E::EPV;
   const int tid = threadIdx.x;
 #pragma unroll 1
@@ -1771,7 +1772,9 @@ __device__ __forceinline__ void race_slice(const Params& p, const uint4 (&va)[VP
         const float ft = E::get(a, g + e);
         if (RESID) {
           const float fd = E::get(bv, g + e);
-          w[e] = kept_p(ft, mt, c, lt, tt) - kept_p(fd, md, c, ld, td);
+          const float pp = kept_p(ft, mt, c, lt, tt), qq = kept_p(fd, md, c, ld, td);
+          if (ALPHA) *acc += fminf(pp, qq);
+          w[e] = pp - qq;
         } else {
           w[e] = ft >= tt ? fexp2((ft - mt) * c) : 0.0f;
         }
@@ -1790,9 +1793,10 @@ __device__ __forceinline__ void race_slice(const Params& p, const uint4 (&va)[VP
 }
 
 // Alpha partial sum of draft position i over this slice (va / vb: its target / draft slices), and the
-// residual race if i is the first rejected position.  min(p, q) is taken on the log2 weights, so it
-// costs one exp2.  TRUNC: the batch row is truncated (some entries have p = 0); then a vector without
-// a kept target entry adds nothing and is skipped.
+// residual race if i is the first rejected position.  Off the drawing position min(p, q) is taken on the
+// log2 weights, so it costs one exp2; at it, the race computes p and q anyway and alpha takes their
+// minimum.  TRUNC: the batch row is truncated (some entries have p = 0); then a vector without a kept
+// target entry adds nothing and is skipped.
 template <class E, int VPT, bool TRUNC>
 __device__ __forceinline__ void k5_position(const Params& p, K5Smem& sm, int b, int i, int n, int x0, int nv, float c,
                             const uint4 (&va)[VPT], const uint4 (&vb)[VPT], float& best, int& bidx, float& bval) {
@@ -1803,6 +1807,14 @@ __device__ __forceinline__ void k5_position(const Params& p, K5Smem& sm, int b, 
   const float lt = sm.lz[i], ld = sm.lz[k + 1 + i];
   const float tt = sm.fthr[i], td = sm.fthr[k + 1 + i];
   float acc = 0.0f;
+  if (i == n) {
+    // the drawing position: alpha and the residual race in one pass over p and q
+    race_slice<E, VPT, true, true>(p, va, vb, x0, nv, c, mt, lt, tt, md, ld, td, 1u, (uint32_t)b, (uint32_t)n, best,
+                                   bidx, bval, &acc);
+    acc = wave_sum(acc);
+    if (lane == 0) sm.wacc[i][wave] = acc;
+    return;
+  }
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
     const int j = tid + u * NT;
@@ -1826,9 +1838,6 @@ __device__ __forceinline__ void k5_position(const Params& p, K5Smem& sm, int b, 
       }
     }
   }
-  if (i == n)
-    race_slice<E, VPT, true>(p, va, vb, x0, nv, c, mt, lt, tt, md, ld, td, 1u, (uint32_t)b, (uint32_t)n, best, bidx,
-                             bval);
   acc = wave_sum(acc);
   if (lane == 0) sm.wacc[i][wave] = acc;
 }
@@ -2148,7 +2157,7 @@ __device__ __forceinline__ void k5_item(const Params& p, K5Smem& sm, int item, i
 }
 
 template <class E, int VPT, bool RAW>
-__global__ __launch_bounds__(NT) void k5_verify(Params p) {
+__global__ __launch_bounds__(NT, RAW ? 4 : 5) void k5_verify(Params p) {
   __shared__ K5Smem sm;
   int b, s;
   // row-major items: workgroups go to the XCDs round-robin, so each batch row's slices spread over
