@@ -1766,7 +1766,6 @@ __device__ __forceinline__ void race_slice(const Params& p, const uint4 (&va)[VP
 #pragma unroll 1
     for (int g = 0; g < EPV; g += 4) {
       float w[4];
-      bool any = false;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float ft = E::get(a, g + e);
@@ -1778,9 +1777,9 @@ __device__ __forceinline__ void race_slice(const Params& p, const uint4 (&va)[VP
         } else {
           w[e] = ft >= tt ? fexp2((ft - mt) * c) : 0.0f;
         }
-        any = any | (w[e] > 0.0f);
       }
-      if (!any) continue;
+      // no positive weight in the group: no draw (the largest of the four, one compare)
+      if (!(fmaxf(fmaxf(w[0], w[1]), fmaxf(w[2], w[3])) > 0.0f)) continue;
       const int x = x0 + j * EPV + g;
       const uint4 w4 = philox10(make_uint4((uint32_t)x >> 2, sb, (tag << 24) | sj, p.offset), p.key0, p.key1);
 #pragma unroll

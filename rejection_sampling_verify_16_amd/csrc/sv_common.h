@@ -156,7 +156,7 @@ __device__ inline float u24(uint32_t w) { return (float)(w >> 8) * 0x1p-24f; }
 // The Gumbel key ln w + G equals ln(w / E) with E = -ln U; E2 = E / ln 2 only rescales every key
 // by the same factor, so argmax_x w(x) / E2(x) is the Gumbel-max draw.
 __device__ inline float exp_race_E2(uint32_t w) {
-  const float U = ((float)(w >> 9) + 0.5f) * 0x1p-23f;
+  const float U = fmaf((float)(w >> 9), 0x1p-23f, 0x1p-24f);  // ((w >> 9) + 1/2) 2^-23, exact (one fma)
   return -__builtin_amdgcn_logf(U);
 }
 
