@@ -238,20 +238,32 @@ __device__ inline RowParams row_params(const Params& p, int b) {
   return q;
 }
 
-// Wave butterfly of (max, lowest argmax, sum of exp2((l - max) c), flags).
+// Combine (max, lowest argmax, sum of exp2((l - max) c), flags) with a second such quadruple.
+__device__ inline void stats_combine(float& m, int& a, float& s, uint32_t& fl, float m2, int a2, float s2, uint32_t f2,
+                                     float c) {
+  float mm = m, ss = s;
+  lse_combine(mm, ss, m2, s2, c);
+  maxarg_combine(m, a, m2, a2);
+  s = ss;
+  fl |= f2;
+}
+// Wave reduction of (max, lowest argmax, sum of exp2((l - max) c), flags) into every lane (DPP steps inside
+// the rows, then the four rows' quadruples).
 __device__ inline void wave_stats(float& m, int& a, float& s, uint32_t& fl, float c) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float m2 = __shfl_xor(m, o, 64);
-    const int a2 = __shfl_xor(a, o, 64);
-    const float s2 = __shfl_xor(s, o, 64);
-    const uint32_t f2 = __shfl_xor(fl, o, 64);
-    float mm = m, ss = s;
-    lse_combine(mm, ss, m2, s2, c);
-    maxarg_combine(m, a, m2, a2);
-    s = ss;
-    fl |= f2;
-  }
+#define SV_STATS_STEP(C) \
+  stats_combine(m, a, s, fl, dpp_mov_f<C>(m), (int)dpp_mov_u<C>((uint32_t)a), dpp_mov_f<C>(s), dpp_mov_u<C>(fl), c)
+  SV_ROW_STEPS(SV_STATS_STEP);
+#undef SV_STATS_STEP
+  float m0 = row_f(m, 0), s0 = row_f(s, 0), m2 = row_f(m, 2), s2 = row_f(s, 2);
+  int a0 = (int)row_u((uint32_t)a, 0), a2 = (int)row_u((uint32_t)a, 2);
+  uint32_t f0 = row_u(fl, 0), f2 = row_u(fl, 2);
+  stats_combine(m0, a0, s0, f0, row_f(m, 1), (int)row_u((uint32_t)a, 1), row_f(s, 1), row_u(fl, 1), c);
+  stats_combine(m2, a2, s2, f2, row_f(m, 3), (int)row_u((uint32_t)a, 3), row_f(s, 3), row_u(fl, 3), c);
+  stats_combine(m0, a0, s0, f0, m2, a2, s2, f2, c);
+  m = m0;
+  a = a0;
+  s = s0;
+  fl = f0;
 }
 
 struct RedSmem {
@@ -292,8 +304,7 @@ __device__ __forceinline__ void block_stats(RedSmem& rs, float& m, int& a, float
 // Workgroup NaN-propagating max into every thread.
 __device__ __forceinline__ float block_nan_max(RedSmem& rs, float m) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = nan_max(m, __shfl_xor(m, o, 64));
+  m = wave_nan_max(m);
   if (lane == 0) rs.f[wave] = m;
   __syncthreads();
   m = rs.f[0];
@@ -319,8 +330,7 @@ __device__ __forceinline__ void block_maxarg(RedSmem& rs, float& m, int& a) {
 // Workgroup sum into every thread.
 __device__ __forceinline__ uint32_t block_sum_u32(RedSmem& rs, uint32_t v) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  v = wave_sum_u32(v);
   if (lane == 0) rs.u[wave] = v;
   __syncthreads();
   uint32_t t = 0;
@@ -331,8 +341,7 @@ __device__ __forceinline__ uint32_t block_sum_u32(RedSmem& rs, uint32_t v) {
 
 __device__ __forceinline__ uint32_t block_max_u32(RedSmem& rs, uint32_t v) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor(v, o, 64));
+  v = wave_max_u32(v);
   if (lane == 0) rs.u[wave] = v;
   __syncthreads();
   uint32_t t = 0;
@@ -1346,8 +1355,7 @@ __device__ __forceinline__ void k1_item(const Params& p, K1Smem& sm, int item, i
       sm.u.st.over = 0;
     }
     float wm = m;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) wm = nan_max(wm, __shfl_xor(wm, o, 64));
+    wm = wave_nan_max(wm);
     const uint32_t wf = wave_kth_key(key16f(m), KC / NWAVE);
     if (lane == 0) {
       sm.u.st.wmax[wave] = wm;
@@ -1559,12 +1567,19 @@ __device__ inline float race_key_or_none(float w, uint32_t word) {
 // Workgroup race winner (key, index, logit) into every thread.
 __device__ __forceinline__ void block_race(RedSmem& rs, float& best, int& bidx, float& bval) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float k2 = __shfl_xor(best, o, 64);
-    const int i2 = __shfl_xor(bidx, o, 64);
-    const float v2 = __shfl_xor(bval, o, 64);
-    race_take(best, bidx, bval, k2, i2, v2);
+#define SV_RACE_STEP(C) \
+  race_take(best, bidx, bval, dpp_mov_f<C>(best), (int)dpp_mov_u<C>((uint32_t)bidx), dpp_mov_f<C>(bval))
+  SV_ROW_STEPS(SV_RACE_STEP);
+#undef SV_RACE_STEP
+  {
+    float b0 = row_f(best, 0), v0 = row_f(bval, 0), b2 = row_f(best, 2), v2 = row_f(bval, 2);
+    int i0 = (int)row_u((uint32_t)bidx, 0), i2 = (int)row_u((uint32_t)bidx, 2);
+    race_take(b0, i0, v0, row_f(best, 1), (int)row_u((uint32_t)bidx, 1), row_f(bval, 1));
+    race_take(b2, i2, v2, row_f(best, 3), (int)row_u((uint32_t)bidx, 3), row_f(bval, 3));
+    race_take(b0, i0, v0, b2, i2, v2);
+    best = b0;
+    bidx = i0;
+    bval = v0;
   }
   if (lane == 0) {
     rs.f[wave] = best;
@@ -1976,8 +1991,7 @@ __device__ __forceinline__ void k5_sparse(const Params& p, K5Smem& sm, int b, in
     }
   }
   if (pair) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    acc = wave_sum_u64(acc);
     if (lane == 0) sm.asum[wave] = acc;
     __syncthreads();
     if (tid == 0) {

@@ -161,17 +161,72 @@ __device__ inline float exp_race_E2(uint32_t w) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Wave / workgroup reductions (fixed order: deterministic).
+// Wave / workgroup reductions and scans (fixed order: deterministic).
+//
+// Cross-lane moves without LDS: inside each row of 16 lanes, DPP moves -- quad permutes [1,0,3,2] and
+// [2,3,0,1] (the partners lane ^ 1 and lane ^ 2), the half-row mirror (lane 7 - i within 8) and the row
+// mirror (15 - i within 16); once a group's lanes hold equal partials, a mirror partner holds the same
+// partial as lane ^ 4 / lane ^ 8 would.  Across the four rows, the rows' partials are read as scalars
+// (lanes 0, 16, 32, 48) and combined as (r0 . r1) . (r2 . r3), the order of a butterfly.  Every lane gets
+// the result.  Callers run with the whole wave active.
 // ---------------------------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov_f(float x) {
+  return __uint_as_float(dpp_mov_u<CTRL>(__float_as_uint(x)));
+}
+__device__ __forceinline__ uint32_t row_u(uint32_t x, int r) { return (uint32_t)__builtin_amdgcn_readlane((int)x, 16 * r); }
+__device__ __forceinline__ float row_f(float x, int r) { return __uint_as_float(row_u(__float_as_uint(x), r)); }
+constexpr int DPP_QX1 = 0xB1, DPP_QX2 = 0x4E, DPP_HMIRROR = 0x141, DPP_MIRROR = 0x140;
+
+// One butterfly step inside the rows: combine with the partner of step 0..3 (x1, x2, half-row, row mirror).
+#define SV_ROW_STEPS(STEP)  \
+  STEP(DPP_QX1);            \
+  STEP(DPP_QX2);            \
+  STEP(DPP_HMIRROR);        \
+  STEP(DPP_MIRROR)
+
 __device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+#define SV_SUM_STEP(C) v += dpp_mov_f<C>(v)
+  SV_ROW_STEPS(SV_SUM_STEP);
+#undef SV_SUM_STEP
+  return (row_f(v, 0) + row_f(v, 1)) + (row_f(v, 2) + row_f(v, 3));
 }
 __device__ inline uint32_t wave_or(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, 64);
-  return v;
+#define SV_OR_STEP(C) v |= dpp_mov_u<C>(v)
+  SV_ROW_STEPS(SV_OR_STEP);
+#undef SV_OR_STEP
+  return (row_u(v, 0) | row_u(v, 1)) | (row_u(v, 2) | row_u(v, 3));
+}
+__device__ inline uint32_t wave_sum_u32(uint32_t v) {
+#define SV_SUMU_STEP(C) v += dpp_mov_u<C>(v)
+  SV_ROW_STEPS(SV_SUMU_STEP);
+#undef SV_SUMU_STEP
+  return (row_u(v, 0) + row_u(v, 1)) + (row_u(v, 2) + row_u(v, 3));
+}
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+#define SV_MAXU_STEP(C) v = max(v, dpp_mov_u<C>(v))
+  SV_ROW_STEPS(SV_MAXU_STEP);
+#undef SV_MAXU_STEP
+  return max(max(row_u(v, 0), row_u(v, 1)), max(row_u(v, 2), row_u(v, 3)));
+}
+__device__ inline unsigned long long wave_sum_u64(unsigned long long v) {
+#define SV_SUM64_STEP(C)                                                                                    \
+  v += ((unsigned long long)dpp_mov_u<C>((uint32_t)(v >> 32)) << 32) | dpp_mov_u<C>((uint32_t)v)
+  SV_ROW_STEPS(SV_SUM64_STEP);
+#undef SV_SUM64_STEP
+  auto row64 = [&](int r) { return ((unsigned long long)row_u((uint32_t)(v >> 32), r) << 32) | row_u((uint32_t)v, r); };
+  return (row64(0) + row64(1)) + (row64(2) + row64(3));
+}
+
+__device__ inline float wave_nan_max(float v) {  // NaN-propagating
+#define SV_NMAX_STEP(C) v = nan_max(v, dpp_mov_f<C>(v))
+  SV_ROW_STEPS(SV_NMAX_STEP);
+#undef SV_NMAX_STEP
+  return nan_max(nan_max(row_f(v, 0), row_f(v, 1)), nan_max(row_f(v, 2), row_f(v, 3)));
 }
 
 // (max, lowest argmax) of a value; idx = INT32_MAX means "none".
@@ -182,12 +237,16 @@ __device__ inline void maxarg_combine(float& m, int& a, float m2, int a2) {
   }
 }
 __device__ inline void wave_maxarg(float& m, int& a) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float m2 = __shfl_xor(m, o, 64);
-    const int a2 = __shfl_xor(a, o, 64);
-    maxarg_combine(m, a, m2, a2);
-  }
+#define SV_MAXARG_STEP(C) maxarg_combine(m, a, dpp_mov_f<C>(m), (int)dpp_mov_u<C>((uint32_t)a))
+  SV_ROW_STEPS(SV_MAXARG_STEP);
+#undef SV_MAXARG_STEP
+  float m0 = row_f(m, 0), m2 = row_f(m, 2);
+  int a0 = (int)row_u((uint32_t)a, 0), a2 = (int)row_u((uint32_t)a, 2);
+  maxarg_combine(m0, a0, row_f(m, 1), (int)row_u((uint32_t)a, 1));
+  maxarg_combine(m2, a2, row_f(m, 3), (int)row_u((uint32_t)a, 3));
+  maxarg_combine(m0, a0, m2, a2);
+  m = m0;
+  a = a0;
 }
 
 // Combine two (max, sum of exp2((l - max) c)) pairs.
@@ -200,17 +259,46 @@ __device__ inline void lse_combine(float& m, float& s, float m2, float s2, float
   }
 }
 
-// Inclusive scan over the 64 lanes of a wave (lane order).
-template <class T>
-__device__ inline T wave_incl_scan(T v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const T n = __shfl_up(v, o, 64);
-    if (lane >= o) v += n;
-  }
+// Inclusive scans in lane order: DPP row shifts by 1, 2, 4 and 8 lanes (lanes without a source add 0), then
+// row 15's and row 31's totals broadcast into the rows above them.
+template <int CTRL, int ROWM>
+__device__ __forceinline__ uint32_t dpp_or0_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWM, 0xF, false);
+}
+#define SV_SCAN_STEPS(STEP) \
+  STEP(0x111, 0xF);         \
+  STEP(0x112, 0xF);         \
+  STEP(0x114, 0xF);         \
+  STEP(0x118, 0xF);         \
+  STEP(0x142, 0xA);         \
+  STEP(0x143, 0xC)
+__device__ inline uint32_t wave_incl_scan_u32(uint32_t v) {
+#define SV_SCAN32_STEP(C, R) v += dpp_or0_u<C, R>(v)
+  SV_SCAN_STEPS(SV_SCAN32_STEP);
+#undef SV_SCAN32_STEP
   return v;
 }
+__device__ inline unsigned long long wave_incl_scan_u64(unsigned long long v) {
+#define SV_SCAN64_STEP(C, R) \
+  v += ((unsigned long long)dpp_or0_u<C, R>((uint32_t)(v >> 32)) << 32) | dpp_or0_u<C, R>((uint32_t)v)
+  SV_SCAN_STEPS(SV_SCAN64_STEP);
+#undef SV_SCAN64_STEP
+  return v;
+}
+__device__ inline double wave_incl_scan_f64(double v) {
+#define SV_SCANF64_STEP(C, R)                                                                                \
+  {                                                                                                          \
+    const unsigned long long b = (unsigned long long)__double_as_longlong(v);                                \
+    v += __longlong_as_double((long long)(((unsigned long long)dpp_or0_u<C, R>((uint32_t)(b >> 32)) << 32) | \
+                                          dpp_or0_u<C, R>((uint32_t)b)));                                    \
+  }
+  SV_SCAN_STEPS(SV_SCANF64_STEP);
+#undef SV_SCANF64_STEP
+  return v;
+}
+__device__ inline uint32_t wave_incl_scan(uint32_t v) { return wave_incl_scan_u32(v); }
+__device__ inline unsigned long long wave_incl_scan(unsigned long long v) { return wave_incl_scan_u64(v); }
+__device__ inline double wave_incl_scan(double v) { return wave_incl_scan_f64(v); }
 
 // Lowest lane whose predicate holds (64 if none).
 __device__ inline int first_lane(bool pred) {
@@ -222,11 +310,7 @@ __device__ inline int first_lane(bool pred) {
 template <class T>
 __device__ inline T block_inclusive_scan(T v, T* lds_tmp /* >= NWAVE */) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const T n = __shfl_up(v, o, 64);
-    if (lane >= o) v += n;
-  }
+  v = wave_incl_scan(v);
   if (lane == 63) lds_tmp[wave] = v;
   __syncthreads();
   T add = 0;

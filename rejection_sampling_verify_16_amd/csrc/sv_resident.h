@@ -370,7 +370,7 @@ __device__ __forceinline__ void rblock_race(RSmem& sm, float& best, int& bidx, f
 // ---- wave-level helpers of the merge ----
 template <class T>
 __device__ inline T wave_excl_scan(T v, T& total) {
-  const T incl = wave_incl_scan<T>(v);
+  const T incl = wave_incl_scan(v);
   total = __shfl(incl, 63, 64);
   return incl - v;
 }
