@@ -1,0 +1,54 @@
+"""Compiler resource report of the product kernels (CPU only: hipcc cross-compiles for gfx950): no kernel spills
+registers to scratch memory, and the streaming kernels keep the occupancy their launch bounds ask for.  A spill
+or a register array indexed at run time puts values in scratch, and every access then waits on memory: on the
+statistics kernel that made a call over 1.4x slower, with results unchanged, so no parity test would notice."""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(ROOT, "rejection_sampling_verify_16_amd", "csrc")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+# smallest occupancy (waves per SIMD) each kernel family must keep
+MIN_WAVES = {"k1_stats": 7, "k1_rows": 6, "k5_verify": 4, "k_tree": 4, "k_commit": 4, "kr_verify": 2}
+
+
+def _resources(src):
+    from rejection_sampling_verify_16_amd import build
+    flags = [f for f in build.HIPCC_FLAGS if f not in ("-shared",)]
+    out = os.path.join("/tmp", f"svres_{os.getpid()}_{os.path.basename(src)}.o")
+    cmd = [HIPCC, *flags, "-c", "-I", os.path.join(ROOT, "include"), "-o", out,
+           "-Rpass-analysis=kernel-resource-usage", src]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if os.path.exists(out):
+        os.remove(out)
+    assert r.returncode == 0, r.stderr[-2000:]
+    kernels, cur = {}, None
+    for line in r.stderr.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            cur = m.group(1)
+            kernels[cur] = {}
+            continue
+        m = re.search(r"remark:\s+([A-Za-z ]+?)(?: \[[^\]]*\])?: (\d+)", line)
+        if m and cur:
+            kernels[cur][m.group(1).strip()] = int(m.group(2))
+    return kernels
+
+
+@pytest.mark.skipif(not shutil.which(HIPCC) and not os.path.exists(HIPCC), reason="hipcc not available")
+@pytest.mark.parametrize("src", ["specverify.hip", "commit.hip"])
+def test_no_scratch_and_occupancy(src):
+    kernels = _resources(os.path.join(CSRC, src))
+    assert kernels, "no kernel resource report"
+    for name, res in kernels.items():
+        print(f"{name}: VGPRs {res.get('VGPRs')} scratch {res.get('ScratchSize')} waves/SIMD {res.get('Occupancy')}")
+        assert res.get("ScratchSize", 0) == 0, f"{name} uses scratch memory: {res}"
+        for fam, w in MIN_WAVES.items():
+            if fam in name:
+                assert res.get("Occupancy", 0) >= w, f"{name}: occupancy {res.get('Occupancy')} < {w}"
