@@ -4,6 +4,7 @@
 // the benchmark load.  It runs the product's own device code (sv_common.h) on inputs chosen by the host,
 // so that the random stream and the race transform can be checked directly, element by element:
 //   probe_philox       the Philox-4x32-10 block function on given counters and keys (known-answer tests);
+//   probe_philox_uk    the same with one key for the whole launch, the form the verify kernels use;
 //   probe_race_e2      for every 23-bit uniform code j (U = (j + 0.5) 2^-23): E2 = -log2 U as the draws
 //                      compute it, and the race key scale rcp(E2) (the Gumbel-max draws of the AReno page
 //                      "feat(engine): MTP training loss and speculative decoding for bailing_v3", its
@@ -27,6 +28,18 @@ __global__ void k_philox(const uint32_t* ctr, const uint32_t* key, uint32_t* out
   if (t >= n) return;
   const uint4 c = make_uint4(ctr[4 * t], ctr[4 * t + 1], ctr[4 * t + 2], ctr[4 * t + 3]);
   const uint4 r = sv::philox10(c, key[2 * t], key[2 * t + 1]);
+  out[4 * t] = r.x;
+  out[4 * t + 1] = r.y;
+  out[4 * t + 2] = r.z;
+  out[4 * t + 3] = r.w;
+}
+
+// philox10_uk, the verify kernels' form: one key for the whole launch (kernel arguments, so uniform).
+__global__ void k_philox_uk(const uint32_t* ctr, uint32_t k0, uint32_t k1, uint32_t* out, int n) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n) return;
+  const uint4 c = make_uint4(ctr[4 * t], ctr[4 * t + 1], ctr[4 * t + 2], ctr[4 * t + 3]);
+  const uint4 r = sv::philox10_uk(c, k0, k1);
   out[4 * t] = r.x;
   out[4 * t + 1] = r.y;
   out[4 * t + 2] = r.z;
@@ -81,6 +94,15 @@ extern "C" int probe_philox(const uint32_t* ctr, const uint32_t* key, uint32_t* 
   if (n < 1 || !ctr || !key || !out) return 1;
   (void)hipGetLastError();  // so that the check below is about this launch alone
   hipLaunchKernelGGL(k_philox, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream, ctr, key, out, n);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+// As probe_philox with one key (k0, k1) for all n counters.
+extern "C" int probe_philox_uk(const uint32_t* ctr, uint32_t k0, uint32_t k1, uint32_t* out, int32_t n, void* stream) {
+  if (n < 1 || !ctr || !out) return 1;
+  (void)hipGetLastError();  // so that the check below is about this launch alone
+  hipLaunchKernelGGL(k_philox_uk, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream, ctr, k0, k1, out,
+                     n);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

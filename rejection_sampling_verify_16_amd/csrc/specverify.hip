@@ -1611,7 +1611,7 @@ __device__ __forceinline__ void gumbel_vec(const uint4& v, int xbase, float m, f
     }
     if (any) {
       const int x = xbase + g;
-      const uint4 w4 = philox10(make_uint4((uint32_t)x >> 2, b, (tag << 24) | j, p.offset), p.key0, p.key1);
+      const uint4 w4 = philox10_uk(make_uint4((uint32_t)x >> 2, b, (tag << 24) | j, p.offset), p.key0, p.key1);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if (w[e] > 0.0f) {
@@ -1768,6 +1768,11 @@ __device__ __forceinline__ void race_slice(const Params& p, const uint4 (&va)[VP
                            uint32_t sj, float& best, int& bidx, float& bval, float* acc = nullptr) {
   constexpr int EPV = E::EPV;
   const int tid = threadIdx.x;
+  // This thread's best so far.  Its entries come in increasing index order, so a strict compare keeps the
+  // lowest index among equal keys; the start value -0.5 lies between "no weight" (-1) and every real key
+  // (>= 0), and the caller's candidate is merged with the full tie rule at the end.
+  float lb = -0.5f, lv = 0.0f;
+  int li = INT_MAX;
 #pragma unroll 1
   for (int u = 0; u < VPT; ++u) {
     const int j = tid + u * NT;
@@ -1796,14 +1801,19 @@ __device__ __forceinline__ void race_slice(const Params& p, const uint4 (&va)[VP
       // no positive weight in the group: no draw (the largest of the four, one compare)
       if (!(fmaxf(fmaxf(w[0], w[1]), fmaxf(w[2], w[3])) > 0.0f)) continue;
       const int x = x0 + j * EPV + g;
-      const uint4 w4 = philox10(make_uint4((uint32_t)x >> 2, sb, (tag << 24) | sj, p.offset), p.key0, p.key1);
+      const uint4 w4 = philox10_uk(make_uint4((uint32_t)x >> 2, sb, (tag << 24) | sj, p.offset), p.key0, p.key1);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t word = e == 0 ? w4.x : e == 1 ? w4.y : e == 2 ? w4.z : w4.w;
-        race_take(best, bidx, bval, race_key_or_none(w[e], word), x + e, E::get(a, g + e));
+        const float key = race_key_or_none(w[e], word);
+        const bool take = key > lb;  // a later index never wins a tie
+        lb = take ? key : lb;
+        li = take ? x + e : li;
+        lv = take ? E::get(a, g + e) : lv;
       }
     }
   }
+  race_take(best, bidx, bval, lb, li, lv);
 }
 
 // Alpha partial sum of draft position i over this slice (va / vb: its target / draft slices), and the
@@ -1891,7 +1901,7 @@ __device__ inline void sparse_plain_race(const Params& p, const uint32_t (&xs)[N
     if (xs[t] == 0xffffffffu) continue;
     const float w = fexp2((fs[t] - m) * c);
     if (w > 0.0f) {
-      const uint4 w4 = philox10(make_uint4(xs[t] >> 2, sb, (tag << 24) | sj, p.offset), p.key0, p.key1);
+      const uint4 w4 = philox10_uk(make_uint4(xs[t] >> 2, sb, (tag << 24) | sj, p.offset), p.key0, p.key1);
       const uint32_t qq = xs[t] & 3u;
       race_take(best, bidx, bval, race_key(w, qq == 0 ? w4.x : qq == 1 ? w4.y : qq == 2 ? w4.z : w4.w), (int)xs[t],
                 fs[t]);
@@ -1982,7 +1992,7 @@ __device__ __forceinline__ void k5_sparse(const Params& p, K5Smem& sm, int b, in
       if (draw) {
         const float w = fexp2(lp) - fexp2(lq);
         if (w > 0.0f) {
-          const uint4 w4 = philox10(make_uint4(x >> 2, sb, (tag << 24) | sj, p.offset), p.key0, p.key1);
+          const uint4 w4 = philox10_uk(make_uint4(x >> 2, sb, (tag << 24) | sj, p.offset), p.key0, p.key1);
           const uint32_t qq = x & 3u;
           race_take(best, bidx, bval, race_key(w, qq == 0 ? w4.x : qq == 1 ? w4.y : qq == 2 ? w4.z : w4.w), (int)x,
                     ft[t]);
@@ -2060,7 +2070,7 @@ __device__ __forceinline__ void k5_item(const Params& p, K5Smem& sm, int item, i
     load_slice<E, VPT>(row_ptr(p, b, k + 1, esize), x0, nv, b0);
   }
   if (tid < k) {
-    const uint4 w4 = philox10(make_uint4((uint32_t)tid >> 2, (uint32_t)b, 0u, p.offset), p.key0, p.key1);
+    const uint4 w4 = philox10_uk(make_uint4((uint32_t)tid >> 2, (uint32_t)b, 0u, p.offset), p.key0, p.key1);
     const int qq = tid & 3;
     sm.u[tid] = u24(qq == 0 ? w4.x : qq == 1 ? w4.y : qq == 2 ? w4.z : w4.w);
     sm.tok[tid] = tokv;
@@ -2229,7 +2239,7 @@ __device__ __forceinline__ void tree_resid_slice(const Params& p, const TreeSmem
         any = any | (w[e] > 0.0f);
       }
       if (!any) continue;
-      const uint4 w4 = philox10(make_uint4((uint32_t)x >> 2, sb, (1u << 24) | sj, p.offset), p.key0, p.key1);
+      const uint4 w4 = philox10_uk(make_uint4((uint32_t)x >> 2, sb, (1u << 24) | sj, p.offset), p.key0, p.key1);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if (w[e] > 0.0f) {
@@ -2291,7 +2301,7 @@ __global__ __launch_bounds__(NT) void k_tree(Params p) {
     sm.state[tid] = ri->state;
     sm.par[tid] = p.parent[(size_t)b * N + tid];
     sm.tok[tid] = p.draft_tokens[(size_t)b * N + tid];
-    const uint4 w4 = philox10(make_uint4((uint32_t)tid >> 2, (uint32_t)b, 0u, p.offset), p.key0, p.key1);
+    const uint4 w4 = philox10_uk(make_uint4((uint32_t)tid >> 2, (uint32_t)b, 0u, p.offset), p.key0, p.key1);
     const int qq = tid & 3;
     sm.u[tid] = u24(qq == 0 ? w4.x : qq == 1 ? w4.y : qq == 2 ? w4.z : w4.w);
   }

@@ -115,6 +115,41 @@ __device__ inline uint4 philox10(uint4 c, uint32_t k0, uint32_t k1) {
   return c;
 }
 
+// a ^ b ^ k in one instruction (v_bitop3_b32, truth table 0x96), k from a scalar register.  Only for a k
+// that is the same in every lane of the wave: the "s" operand takes lane 0's value.
+__device__ __forceinline__ uint32_t xor3_uk(uint32_t a, uint32_t b, uint32_t k) {
+  uint32_t r;
+  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(k));
+  return r;
+}
+
+// philox10 for a key that is uniform across the wave (the verify kernels' keys are kernel arguments).  The
+// first two rounds stay plain code: counters whose words other than x are uniform keep half of those rounds
+// on the scalar unit.  From the third round on every word differs per lane, and each new word's two xors
+// fold into one three-input xor with the round key.
+__device__ inline uint4 philox10_uk(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+    uint32_t n0, n2;
+    if (r < 2) {
+      n0 = (uint32_t)(p1 >> 32) ^ c.y ^ k0;
+      n2 = (uint32_t)(p0 >> 32) ^ c.w ^ k1;
+    } else {
+      n0 = xor3_uk((uint32_t)(p1 >> 32), c.y, k0);
+      n2 = xor3_uk((uint32_t)(p0 >> 32), c.w, k1);
+    }
+    c.y = (uint32_t)p1;
+    c.w = (uint32_t)p0;
+    c.x = n0;
+    c.z = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
 // Two Philox-4x32-10 blocks under one key, rounds interleaved (two independent dependency chains).
 __device__ inline void philox10x2(uint4& c0, uint4& c1, uint32_t k0, uint32_t k1) {
 #pragma unroll

@@ -34,9 +34,10 @@ def P():
     L = ctypes.CDLL(PROBE)
     vp, i32 = ctypes.c_void_p, ctypes.c_int32
     L.probe_philox.argtypes = [vp, vp, vp, i32, vp]
+    L.probe_philox_uk.argtypes = [vp, ctypes.c_uint32, ctypes.c_uint32, vp, i32, vp]
     L.probe_race_e2.argtypes = [vp, vp, vp]
     L.probe_u24.argtypes = [vp, vp]
-    for f in (L.probe_philox, L.probe_race_e2, L.probe_u24):
+    for f in (L.probe_philox, L.probe_philox_uk, L.probe_race_e2, L.probe_u24):
         f.restype = ctypes.c_int
     return L
 
@@ -68,6 +69,40 @@ def test_philox_random_counters_match_oracle(P):
     o = oracle.get()
     want = np.array([o.philox(ctr[i], key[i]) for i in range(n)], dtype=np.uint32)
     np.testing.assert_array_equal(got, want)
+
+
+def _philox_uk_gpu(P, ctr, key):
+    import torch
+    c = torch.from_numpy(np.ascontiguousarray(ctr, dtype=np.uint32).view(np.int32)).cuda()
+    out = torch.empty_like(c)
+    assert P.probe_philox_uk(c.data_ptr(), int(key[0]), int(key[1]), out.data_ptr(), c.shape[0], None) == 0
+    torch.cuda.synchronize()
+    return out.cpu().numpy().view(np.uint32)
+
+
+def test_philox_uniform_key_kat_on_device(P):
+    """The verify kernels' form (one key per launch, three-input xors from the third round on)."""
+    rows = [[int(t, 16) for t in line.split()] for line in oracle_pins.read_golden_table("philox4x32_10_kat.txt")]
+    v = np.array(rows, dtype=np.uint64).astype(np.uint32)
+    for r in v:
+        got = _philox_uk_gpu(P, r[None, 0:4], r[4:6])
+        np.testing.assert_array_equal(got[0], r[6:10])
+
+
+def test_philox_uniform_key_random_counters_match_oracle(P):
+    """Counters shaped like the draws' (x >> 2 per lane; position, row and offset words shared by the
+    wave) and fully random ones, under a few keys."""
+    rng = np.random.default_rng(23)
+    o = oracle.get()
+    n = 2048
+    for key in ([0, 0], [0xFFFFFFFF, 0xFFFFFFFF], list(rng.integers(0, 2**32, size=2, dtype=np.uint64))):
+        key = np.array(key, dtype=np.uint64).astype(np.uint32)
+        ctr = rng.integers(0, 2**32, size=(n, 4), dtype=np.uint64).astype(np.uint32)
+        ctr[: n // 2, 0] = np.arange(n // 2, dtype=np.uint32)
+        ctr[: n // 2, 1:] = ctr[0, 1:]
+        got = _philox_uk_gpu(P, ctr, key)
+        want = np.array([o.philox(ctr[i], key) for i in range(n)], dtype=np.uint32)
+        np.testing.assert_array_equal(got, want)
 
 
 def test_race_transform_exhaustive(P):
