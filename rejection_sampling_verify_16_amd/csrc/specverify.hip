@@ -2216,6 +2216,8 @@ __device__ __forceinline__ void tree_resid_slice(const Params& p, const TreeSmem
                                                  float& best, int& bidx, float& bval) {
   constexpr int EPV = E::EPV;
   const int tid = threadIdx.x, nex = sm.nex;
+  float lb = -0.5f, lv = 0.0f;  // this thread's best, as in race_slice: entries in increasing index order
+  int li = INT_MAX;
 #pragma unroll 1
   for (int u = 0; u < VPT; ++u) {
     const int j = tid + u * NT;
@@ -2242,13 +2244,16 @@ __device__ __forceinline__ void tree_resid_slice(const Params& p, const TreeSmem
       const uint4 w4 = philox10_uk(make_uint4((uint32_t)x >> 2, sb, (1u << 24) | sj, p.offset), p.key0, p.key1);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if (w[e] > 0.0f) {
-          const uint32_t word = e == 0 ? w4.x : e == 1 ? w4.y : e == 2 ? w4.z : w4.w;
-          race_take(best, bidx, bval, race_key(w[e], word), x + e, E::get(a, g + e));
-        }
+        const uint32_t word = e == 0 ? w4.x : e == 1 ? w4.y : e == 2 ? w4.z : w4.w;
+        const float key = race_key_or_none(w[e], word);
+        const bool take = key > lb;
+        lb = take ? key : lb;
+        li = take ? x + e : li;
+        lv = take ? E::get(a, g + e) : lv;
       }
     }
   }
+  race_take(best, bidx, bval, lb, li, lv);
 }
 
 __device__ __forceinline__ void tree_sentinel(const Params& p, int b) {

@@ -669,15 +669,16 @@ __device__ inline void r_sentinel(const RParams& p, int b, int KK) {
   if (tid == 0) p.accept_len[b] = 0;
 }
 
-// Philox-4x32-10 as philox10, with the rounds in a loop: the resident kernel instantiates it at every
-// vector slot of its unrolled loops, where ten inlined rounds would multiply the code size.
+// Philox-4x32-10 as philox10_uk (the key is uniform: kernel arguments), with the rounds in a loop: the
+// resident kernel instantiates it at every vector slot of its unrolled loops, where ten inlined rounds would
+// multiply the code size.
 __device__ __forceinline__ uint4 philox10_loop(uint4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll 1
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c.y ^ k0;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c.w ^ k1;
+    const uint32_t n0 = xor3_uk((uint32_t)(p1 >> 32), c.y, k0);
+    const uint32_t n2 = xor3_uk((uint32_t)(p0 >> 32), c.w, k1);
     c.y = (uint32_t)p1;
     c.w = (uint32_t)p0;
     c.x = n0;
@@ -688,14 +689,15 @@ __device__ __forceinline__ uint4 philox10_loop(uint4 c, uint32_t k0, uint32_t k1
   return c;
 }
 
-// Two Philox-4x32-10 blocks (counters c0, c1) under one key, rounds interleaved: two independent chains.
+// Two Philox-4x32-10 blocks (counters c0, c1) under one uniform key, rounds interleaved: two independent
+// chains.
 __device__ __forceinline__ void philox10x2_loop(uint4& c0, uint4& c1, uint32_t k0, uint32_t k1) {
 #pragma unroll 1
   for (int r = 0; r < 10; ++r) {
     const uint64_t a0 = (uint64_t)0xD2511F53u * c0.x, a1 = (uint64_t)0xD2511F53u * c1.x;
     const uint64_t b0 = (uint64_t)0xCD9E8D57u * c0.z, b1 = (uint64_t)0xCD9E8D57u * c1.z;
-    const uint32_t n00 = (uint32_t)(b0 >> 32) ^ c0.y ^ k0, n01 = (uint32_t)(b1 >> 32) ^ c1.y ^ k0;
-    const uint32_t n20 = (uint32_t)(a0 >> 32) ^ c0.w ^ k1, n21 = (uint32_t)(a1 >> 32) ^ c1.w ^ k1;
+    const uint32_t n00 = xor3_uk((uint32_t)(b0 >> 32), c0.y, k0), n01 = xor3_uk((uint32_t)(b1 >> 32), c1.y, k0);
+    const uint32_t n20 = xor3_uk((uint32_t)(a0 >> 32), c0.w, k1), n21 = xor3_uk((uint32_t)(a1 >> 32), c1.w, k1);
     c0.y = (uint32_t)b0;
     c1.y = (uint32_t)b1;
     c0.w = (uint32_t)a0;
