@@ -2289,7 +2289,10 @@ __device__ __forceinline__ void tree_emit(const Params& p, const TreeSmem& sm, i
 }
 
 template <class E, int VPT>
-__global__ __launch_bounds__(NT) void k_tree(Params p) {
+// At most 80 scalar registers in the compiler's total (the attribute's 82 gives 80, a few spilled to vector
+// lanes): the hardware holds eight 256-thread workgroups per CU only up to that total, and the tree items are
+// latency-bound (unconstrained, 92 scalars gave seven per CU and a 0.5 us slower kernel).
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_num_sgpr(82))) void k_tree(Params p) {
   __shared__ TreeSmem sm;
   constexpr int EPV = E::EPV;
   constexpr int esize = 16 / EPV;
