@@ -53,7 +53,7 @@ constexpr int MODE_SAMPLE = 1;  // plain sampler: k = 0, one logit row per batch
 constexpr int MODE_TREE = 2;    // tree verification: N = rows = k + 1 target rows per batch row, no draft rows
 constexpr int MAXN = 64;        // nodes per draft tree
 constexpr int MAXDEV = 64;
-constexpr int VPT1 = 8;         // K1: 16-byte vectors per thread per slice
+constexpr int VPT1 = 9;         // K1: 16-byte vectors per thread per slice (18432 bf16 logits)
 constexpr int VPT5 = 2;         // K5
 constexpr int OCC1 = 7;         // K1 workgroups per CU (register budget of its launch bounds)
 constexpr int FVPT = 2;         // whole-row passes of one workgroup: vectors per thread per step

@@ -24,7 +24,7 @@ def _case(i):
     epv = 4 if dtype == "f32" else 8
     B = int(rng.integers(1, 9))
     k = int(rng.integers(1, 9))
-    V = int(rng.integers(1, 5001)) * epv          # ragged against the 4096- and 16384-logit slices
+    V = int(rng.integers(1, 5001)) * epv          # ragged against the 4096- and 18432-logit slices
     w = W.make(B, k, V, dtype=dtype, seed=9100 + i, target_sigma=float(rng.uniform(1.0, 4.0)),
                noise_sigma=float(rng.uniform(0.2, 1.5)), boost=float(rng.choice([0.0, 8.0])),
                tie_fraction=float(rng.choice([0.0, 0.2])), name=f"sweep{i}")
