@@ -54,6 +54,8 @@ constexpr int MODE_TREE = 2;    // tree verification: N = rows = k + 1 target ro
 constexpr int MAXN = 64;        // nodes per draft tree
 constexpr int MAXDEV = 64;
 constexpr int VPT1 = 9;         // K1: 16-byte vectors per thread per slice (18432 bf16 logits)
+constexpr int VPT1W = 12;       // K1, bf16 calls of many slices (at least K1W_ITEMS of 24576 logits): wider slices
+constexpr int K1W_ITEMS = 8192; //   (several rounds of the slice kernel's workgroup slots: its per-slice work dominates)
 constexpr int VPT5 = 2;         // K5
 constexpr int OCC1 = 7;         // K1 workgroups per CU (register budget of its launch bounds)
 constexpr int FVPT = 2;         // whole-row passes of one workgroup: vectors per thread per step
@@ -1496,8 +1498,9 @@ __device__ __forceinline__ void k1_item(const Params& p, K1Smem& sm, int item, i
   SV_TRACE_AT(p, item, 2);
 }
 
+// Wide slices with raw logprobs need more registers than seven workgroups per CU leave (they would spill).
 template <class E, int VPT, bool RAW>
-__global__ __launch_bounds__(NT, OCC1) void k1_stats(Params p) {
+__global__ __launch_bounds__(NT, (RAW && VPT > VPT1) ? OCC1 - 1 : OCC1) void k1_stats(Params p) {
   __shared__ K1Smem sm;
   int r, s;
   item_rs(blockIdx.x, p.R, p.S1, r, s);
@@ -2450,7 +2453,7 @@ static bool resident_plan(int32_t B, int32_t k, int32_t V, int cus, int& nv, int
 }
 
 struct Geo {
-  int rows, R, S1, S5, L1, L5, esize, EPV;
+  int rows, R, S1, S5, L1, L5, esize, EPV, vpt1;
   size_t off_cnt5, off_st1, off_hw1, off_hc1, off_cand1, off_ncand1, off_rinfo, off_fin5, off_trace, off_trace5,
       total;
 };
@@ -2471,7 +2474,15 @@ static bool make_geo(int32_t B, int32_t k, int32_t V, spec_dtype_t dtype, Geo& g
   g.rows = tree_nodes > 0 ? tree_nodes : 2 * k + 1;
   if ((long long)B * g.rows > (1 << 24)) return false;  // item counts stay below 2^31
   g.R = B * g.rows;
-  g.L1 = NT * g.EPV * VPT1;
+  // Wide slices only where K1 runs many rounds of items: there the per-slice work (histogram clears,
+  // partials, candidate staging) and the number of partials each merge reads count for more than the tail of
+  // the last round, which wider slices lengthen on calls of few rounds.
+  g.vpt1 = VPT1;
+  if (dtype == SPEC_DTYPE_BF16) {
+    const long long sw = (V + NT * g.EPV * VPT1W - 1) / (NT * g.EPV * VPT1W);
+    if ((long long)g.R * sw >= K1W_ITEMS) g.vpt1 = VPT1W;
+  }
+  g.L1 = NT * g.EPV * g.vpt1;
   g.L5 = NT * g.EPV * VPT5;
   g.S1 = (V + g.L1 - 1) / g.L1;
   g.S5 = (V + g.L5 - 1) / g.L5;
@@ -2541,9 +2552,17 @@ static void enqueue(const Params& p, int cus, hipStream_t st, Timing* tm) {
   const dim3 g1((unsigned)(p.R * p.S1)), gr((unsigned)p.R), g5((unsigned)(p.B * p.S5));
   const bool raw = p.raw_logprobs != nullptr;
   prof_mark(tm, 0, st);
-  if (raw)
+  bool wide = false;  // the slice width the geometry chose (bf16 only)
+  if constexpr (E::KEYBITS == 16) wide = p.L1 == NT * E::EPV * VPT1W;
+  if constexpr (E::KEYBITS == 16) {
+    if (wide && raw)
+      hipLaunchKernelGGL((k1_stats<E, VPT1W, true>), g1, dim3(NT), 0, st, p);
+    else if (wide)
+      hipLaunchKernelGGL((k1_stats<E, VPT1W, false>), g1, dim3(NT), 0, st, p);
+  }
+  if (!wide && raw)
     hipLaunchKernelGGL((k1_stats<E, VPT1, true>), g1, dim3(NT), 0, st, p);
-  else
+  else if (!wide)
     hipLaunchKernelGGL((k1_stats<E, VPT1, false>), g1, dim3(NT), 0, st, p);
   prof_mark(tm, 1, st);
   prof_mark(tm, 2, st);

@@ -325,6 +325,9 @@ RAW_CASES = [
     ("greedy_ties", 24, 2, 40000, "bf16", dict(temperature=0.0, tie_fraction=0.2)),
     ("f32_trunc", 8, 3, 12000, "f32", dict(temperature=0.7, top_k=30, top_p=0.9)),
     ("k1_T2_topp", 16, 1, 32768, "bf16", dict(temperature=2.0, top_p=0.8)),
+    # enough slices (9 x 304 rows x 3) for the statistics kernel's wide slices (24576 logits, ragged tail)
+    ("wide_mixed", 304, 4, 50000, "bf16", dict(boost=8.0, mixed_params=True)),
+    ("wide_greedy_ties", 304, 4, 50000, "bf16", dict(temperature=0.0, tie_fraction=0.2)),
 ]
 
 

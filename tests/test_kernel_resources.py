@@ -16,6 +16,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # smallest occupancy (waves per SIMD) each kernel family must keep
 MIN_WAVES = {"k1_stats": 7, "k1_rows": 6, "k5_verify": 4, "k_tree": 4, "k_commit": 4, "kr_verify": 2}
+# exceptions by mangled-name fragment: wide slices with raw logprobs run one workgroup per CU fewer
+MIN_WAVES_EXACT = {"k1_statsINS_4BF16ELi12ELb1": 6}
 # Largest scalar-register total (as the compiler reports it) of kernels that must run eight 256-thread
 # workgroups per CU: measured on gfx950, the hardware holds eight up to 80 and seven at 82, whatever occupancy
 # the compiler reports.
@@ -58,8 +60,10 @@ def test_no_scratch_and_occupancy(src):
     for name, res in kernels.items():
         print(f"{name}: VGPRs {res.get('VGPRs')} scratch {res.get('ScratchSize')} waves/SIMD {res.get('Occupancy')}")
         assert res.get("ScratchSize", 0) == 0, f"{name} uses scratch memory: {res}"
+        exact = [w for frag, w in MIN_WAVES_EXACT.items() if frag in name]
         for fam, w in MIN_WAVES.items():
             if fam in name:
+                w = exact[0] if exact else w
                 assert res.get("Occupancy", 0) >= w, f"{name}: occupancy {res.get('Occupancy')} < {w}"
         for fam, n in MAX_SGPRS.items():
             if fam in _demangled(name):
