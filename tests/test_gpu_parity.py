@@ -97,10 +97,12 @@ SMALL = [
     ("min_V", 3, 1, 8, "bf16", dict(temperature=1.0)),
     ("min_V_f32", 4, 2, 4, "f32", dict(temperature=1.0, mixed_params=True)),
     ("k1_T2", 16, 1, 32768, "bf16", dict(temperature=2.0, top_k=1000, top_p=0.99)),
-    # the largest vocabulary: 64 slices per bf16 row (the candidate records' limit), 128 per fp32 row
+    # the largest vocabulary: 57 slices per bf16 row (the candidate records allow 64), 114 per fp32 row
     ("maxV_bf16_mixed", 4, 2, 1 << 20, "bf16", dict(boost=8.0, mixed_params=True)),
     ("maxV_f32_topk", 2, 1, 1 << 20, "f32", dict(temperature=0.8, top_k=40, top_p=0.9)),
-    # many batch rows of a small vocabulary: grids of 40k (statistics and merges) and 20k (verify) workgroups
+    # the largest vocabulary with enough rows for the statistics kernel's wide slices (192 rows x 43 slices)
+    ("maxV_wide_mixed", 64, 1, 1 << 20, "bf16", dict(boost=8.0, mixed_params=True)),
+    # many batch rows of a small vocabulary: grids of 60k (statistics and merges) and 20k (verify) workgroups
     ("many_rows", 20000, 1, 64, "bf16", dict(boost=4.0, mixed_params=True)),
     ("many_rows_k8", 2000, 8, 256, "f32", dict(mixed_params=True)),
 ]
