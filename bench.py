@@ -170,6 +170,33 @@ def read_stream_reference(dev, nbytes, runs=8, per_run=10):
             "kernel": "k_read_stream", "grid": [blocks, 256], "timing": f"{runs} runs of {per_run} back-to-back launches"}
 
 
+def occupancy_probe(dev, spin_ticks=2000):
+    """Most 256-thread workgroups alive at once, per register reservation, from the probe library's spin
+    kernel (4 workgroups per CU more than can fit, each waiting spin_ticks of the 100 MHz wall clock).  The
+    compiler's own occupancy report says 8 waves per SIMD for all but the 102-SGPR and 69-VGPR variants (7)."""
+    import ctypes
+    import torch
+    probe = os.path.join(ROOT, "rejection_sampling_verify_16_amd", "libsvprobe.so")
+    L = ctypes.CDLL(probe)
+    L.probe_occupancy.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_ulonglong, ctypes.c_void_p]
+    L.probe_occupancy.restype = ctypes.c_int
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks = cus * 12
+    out = torch.zeros(2 * blocks, dtype=torch.int64, device=dev)
+    names = ["plain", "80 SGPRs", "82 SGPRs", "102 SGPRs", "61 VGPRs", "69 VGPRs"]
+    res = {"cus": cus, "workgroups": blocks, "threads": 256}
+    for v, name in enumerate(names):
+        out.zero_()
+        assert L.probe_occupancy(v, ctypes.c_void_p(out.data_ptr()), blocks, spin_ticks, None) == 0
+        torch.cuda.synchronize()
+        t = out.cpu().numpy().reshape(blocks, 2)
+        ev = np.concatenate([np.stack([t[:, 0], np.ones(blocks)], 1), np.stack([t[:, 1], -np.ones(blocks)], 1)])
+        ev = ev[np.lexsort((ev[:, 1], ev[:, 0]))]  # ends before starts at equal stamps
+        live = int(np.cumsum(ev[:, 1]).max())
+        res[name] = {"max_resident": live, "per_cu": live / cus}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -196,6 +223,8 @@ def main():
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB, 5 times (PMC calibration of "
                          "WRITE_SIZE; with --read-probe: a plain read instead, for FETCH_SIZE)")
+    ap.add_argument("--occupancy-probe", action="store_true",
+                    help="only report how many workgroups the hardware holds at once per register reservation")
     ap.add_argument("--read-probe", action="store_true",
                     help="with --copy-probe-mb: the probe library's read-only stream instead of the copy")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
@@ -222,6 +251,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.occupancy_probe:
+        print(json.dumps({"occupancy": occupancy_probe(dev)}), flush=True)
+        return
     if args.copy_probe_mb and args.read_probe:
         n = args.copy_probe_mb << 20
         rs = read_stream_reference(dev, n, runs=2, per_run=5)

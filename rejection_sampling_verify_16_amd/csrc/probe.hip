@@ -13,7 +13,9 @@
 //   probe_read_stream  a plain read of a buffer with 16-byte loads (the bandwidth reference the benchmark
 //                      quotes its kernels against);
 //   probe_dispatch_id  the dispatch's 64-bit id and queue address as a kernel sees them (the per-call tag of
-//                      cross-workgroup flags is built from them).
+//                      cross-workgroup flags is built from them);
+//   probe_occupancy    how many 256-thread workgroups the hardware holds at once for a kernel that reserves
+//                      given numbers of scalar or vector registers.
 // Every entry point takes device pointers, enqueues one kernel on `stream` and returns 0, or 1 for bad
 // arguments (nothing enqueued).
 #include <hip/hip_runtime.h>
@@ -70,6 +72,26 @@ __global__ __launch_bounds__(256) void k_read_stream(const uint4* src, size_t nv
   if ((threadIdx.x & 63) == 0 && acc == 0x9E3779B9u) sink[blockIdx.x] = acc;  // practically never stored
 }
 
+// Occupancy: each 256-thread workgroup stamps the wall clock (100 MHz) at its start, waits `spin` ticks and
+// stamps its end; the most workgroups alive at once is what the hardware holds per dispatch.  The variants
+// claim registers through empty inline-asm clobbers (no instruction is emitted): the compiler then reports
+// that many, and the launch reserves them.
+template <int REG>
+__global__ __launch_bounds__(256) void k_occupancy(unsigned long long* out, unsigned long long spin) {
+  if (REG == 1) asm volatile("" ::: "s73");  // 80 scalar registers in the compiler's total
+  if (REG == 2) asm volatile("" ::: "s75");  // 82
+  if (REG == 3) asm volatile("" ::: "s95");  // 102
+  if (REG == 4) asm volatile("" ::: "v60");  // 61 vector registers
+  if (REG == 5) asm volatile("" ::: "v68");  // 69
+  const unsigned long long t0 = wall_clock64();
+  while (wall_clock64() - t0 < spin) __builtin_amdgcn_s_sleep(2);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    out[2 * blockIdx.x] = t0;
+    out[2 * blockIdx.x + 1] = wall_clock64();
+  }
+}
+
 // The dispatch id (the LLVM intrinsic has no clang builtin of its own).
 extern "C" __device__ unsigned long long sv_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
 
@@ -103,6 +125,25 @@ extern "C" int probe_philox_uk(const uint32_t* ctr, uint32_t k0, uint32_t k1, ui
   (void)hipGetLastError();  // so that the check below is about this launch alone
   hipLaunchKernelGGL(k_philox_uk, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream, ctr, k0, k1, out,
                      n);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+// out: device uint64 [2 * blocks]; variant 0..5 (see k_occupancy); spin: wall-clock ticks each workgroup waits
+extern "C" int probe_occupancy(int32_t variant, unsigned long long* out, int32_t blocks, unsigned long long spin,
+                               void* stream) {
+  if (!out || blocks < 1 || spin > 100000ull) return 1;
+  (void)hipGetLastError();  // so that the check below is about this launch alone
+  const dim3 g((unsigned)blocks), t(256);
+  const hipStream_t st = (hipStream_t)stream;
+  switch (variant) {
+    case 0: hipLaunchKernelGGL(k_occupancy<0>, g, t, 0, st, out, spin); break;
+    case 1: hipLaunchKernelGGL(k_occupancy<1>, g, t, 0, st, out, spin); break;
+    case 2: hipLaunchKernelGGL(k_occupancy<2>, g, t, 0, st, out, spin); break;
+    case 3: hipLaunchKernelGGL(k_occupancy<3>, g, t, 0, st, out, spin); break;
+    case 4: hipLaunchKernelGGL(k_occupancy<4>, g, t, 0, st, out, spin); break;
+    case 5: hipLaunchKernelGGL(k_occupancy<5>, g, t, 0, st, out, spin); break;
+    default: return 1;
+  }
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
