@@ -11,7 +11,8 @@
 // counter does it (agent-scope atomics; partials travel through agent-scope atomic stores and loads,
 // coherent across the XCDs' L2s without cache-wide write-back or invalidation).
 //
-//   K1 stats   items (logit row, slice), all slices of a row on one XCD.  Streams every logit once with
+//   K1 stats   items (logit row, slice of 18432 bf16 logits, 24576 on calls of many slices, 9216 fp32), all
+//              slices of a row on one XCD.  Streams every logit once with
 //              16-byte loads and keeps only what the row needs: NaN-propagating max (lowest argmax for
 //              greedy rows); the sum of exp2((l - max) * log2(e) / T) for rows whose normaliser is the
 //              whole row; for bf16 rows with top-k <= 64, a record of the slice's candidate logits; for
@@ -631,7 +632,7 @@ __device__ inline uint32_t cand_bits_ge(const uint4& v, uint32_t fe) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// K1: row statistics (every logit read once), merged by the last slice of each row.
+// K1: row statistics (every logit read once) per slice, then one merge per row (k1_rows, its own kernel).
 // ---------------------------------------------------------------------------------------------
 struct K1Smem {
   RedSmem rs;
