@@ -98,6 +98,9 @@ CASES = {
     "topk3": lambda: W.make_tree(48, 32768, W.EAGLE_TREE_9, seed=3015, boost=9.0, top_k=3, name="topk3"),
     # greedy
     "greedy": lambda: W.make_tree(64, 65536, W.EAGLE_TREE_9, seed=3016, boost=5.0, temperature=0.0, name="greedy"),
+    # many trees: 9000 node rows, enough for the statistics kernel's wide slices; a ragged vocabulary tail
+    "many_trees_wide": lambda: W.make_tree(1000, 4104, W.EAGLE_TREE_9, seed=3017, boost=9.0, mixed_params=True,
+                                           name="many_trees_wide"),
 }
 
 
