@@ -1766,15 +1766,16 @@ __device__ inline void load_slice(const uint8_t* row, int x0, int nv, uint4 (&v)
 // a vector with no entry >= tt is skipped before any exp2.  Stream (tag, b, position j).  The winner's
 // (target) logit rides along.  ALPHA (with RESID): also adds min(p, q) of every entry to acc -- the
 // alpha partial sum of the position, from the same p and q.
-template <class E, int VPT, bool RESID, bool ALPHA = false>
+template <class E, int VPT, bool RESID, bool ALPHA = false, bool TRUNC = true>
 __device__ __forceinline__ void race_slice(const Params& p, const uint4 (&va)[VPT], const uint4 (&vb)[VPT], int x0, int nv, float c,
                            float mt, float lt, float tt, float md, float ld, float td, uint32_t tag, uint32_t sb,
                            uint32_t sj, float& best, int& bidx, float& bval, float* acc = nullptr) {
   constexpr int EPV = E::EPV;
   const int tid = threadIdx.x;
   // This thread's best so far.  Its entries come in increasing index order, so a strict compare keeps the
-  // lowest index among equal keys; the start value -0.5 lies between "no weight" (-1) and every real key
-  // (>= 0), and the caller's candidate is merged with the full tie rule at the end.
+  // lowest index among equal keys; entries without weight are never taken, the start value -0.5 lies below
+  // every real key (>= 0), and the caller's candidate is merged with the full tie rule at the end.  TRUNC
+  // false: an untruncated batch row (thresholds -inf), whose entries need no kept test.
   float lb = -0.5f, lv = 0.0f;
   int li = INT_MAX;
 #pragma unroll 1
@@ -1782,10 +1783,12 @@ __device__ __forceinline__ void race_slice(const Params& p, const uint4 (&va)[VP
     const int j = tid + u * NT;
     if (j >= nv) continue;
     const uint4 a = pick_vec<VPT>(va, u);
-    bool kept = false;
+    if (TRUNC) {  // untruncated rows keep every entry (thresholds -inf): no test
+      bool kept = false;
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) kept = kept | (E::get(a, e) >= tt);  // bitwise: no branch per entry
-    if (!kept) continue;
+      for (int e = 0; e < EPV; ++e) kept = kept | (E::get(a, e) >= tt);  // bitwise: no branch per entry
+      if (!kept) continue;
+    }
     const uint4 bv = RESID ? pick_vec<VPT>(vb, u) : a;
 #pragma unroll 1
     for (int g = 0; g < EPV; g += 4) {
@@ -1795,11 +1798,12 @@ __device__ __forceinline__ void race_slice(const Params& p, const uint4 (&va)[VP
         const float ft = E::get(a, g + e);
         if (RESID) {
           const float fd = E::get(bv, g + e);
-          const float pp = kept_p(ft, mt, c, lt, tt), qq = kept_p(fd, md, c, ld, td);
+          const float pp = TRUNC ? kept_p(ft, mt, c, lt, tt) : fexp2(fmaf(ft - mt, c, -lt));
+          const float qq = TRUNC ? kept_p(fd, md, c, ld, td) : fexp2(fmaf(fd - md, c, -ld));
           if (ALPHA) *acc += fminf(pp, qq);
           w[e] = pp - qq;
         } else {
-          w[e] = ft >= tt ? fexp2((ft - mt) * c) : 0.0f;
+          w[e] = (!TRUNC || ft >= tt) ? fexp2((ft - mt) * c) : 0.0f;
         }
       }
       // no positive weight in the group: no draw (the largest of the four, one compare)
@@ -1809,8 +1813,8 @@ __device__ __forceinline__ void race_slice(const Params& p, const uint4 (&va)[VP
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t word = e == 0 ? w4.x : e == 1 ? w4.y : e == 2 ? w4.z : w4.w;
-        const float key = race_key_or_none(w[e], word);
-        const bool take = key > lb;  // a later index never wins a tie
+        const float key = race_key(w[e], word);
+        const bool take = (w[e] > 0.0f) & (key > lb);  // no weight: no candidate; a later index never wins a tie
         lb = take ? key : lb;
         li = take ? x + e : li;
         lv = take ? E::get(a, g + e) : lv;
@@ -1837,7 +1841,7 @@ __device__ __forceinline__ void k5_position(const Params& p, K5Smem& sm, int b, 
   float acc = 0.0f;
   if (i == n) {
     // the drawing position: alpha and the residual race in one pass over p and q
-    race_slice<E, VPT, true, true>(p, va, vb, x0, nv, c, mt, lt, tt, md, ld, td, 1u, (uint32_t)b, (uint32_t)n, best,
+    race_slice<E, VPT, true, true, TRUNC>(p, va, vb, x0, nv, c, mt, lt, tt, md, ld, td, 1u, (uint32_t)b, (uint32_t)n, best,
                                    bidx, bval, &acc);
     acc = wave_sum(acc);
     if (lane == 0) sm.wacc[i][wave] = acc;
@@ -2157,8 +2161,12 @@ __device__ __forceinline__ void k5_item(const Params& p, K5Smem& sm, int item, i
       const uint32_t tag = smp ? 2u : 1u;
       const uint32_t sb = smp ? (uint32_t)(p.row_b ? p.row_b[b] : b) : (uint32_t)b;
       const uint32_t sj = smp ? (uint32_t)(p.row_pos ? p.row_pos[b] : 0) : (uint32_t)k;
-      race_slice<E, VPT, false>(p, vc, vc, x0, nv, q.c, sm.m[k], 0.0f, sm.fthr[k], 0.0f, 0.0f, 0.0f, tag, sb, sj, best,
-                                bidx, bval);
+      if (q.trunc)
+        race_slice<E, VPT, false>(p, vc, vc, x0, nv, q.c, sm.m[k], 0.0f, sm.fthr[k], 0.0f, 0.0f, 0.0f, tag, sb, sj, best,
+                                  bidx, bval);
+      else
+        race_slice<E, VPT, false, false, false>(p, vc, vc, x0, nv, q.c, sm.m[k], 0.0f, sm.fthr[k], 0.0f, 0.0f, 0.0f, tag,
+                                                sb, sj, best, bidx, bval);
     }
     SV_TRACE5_AT(p, item, 3);
     block_race(sm.rs, best, bidx, bval);  // its barriers also order the wacc writes before the reads below
